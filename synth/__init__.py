@@ -1,0 +1,248 @@
+"""Seeded synthetic inputs for the S3-DiT hot path (weights, latents, caption features,
+residual-stream inputs), shared by the oracle tests, the GPU parity tests and the bench.
+
+This module holds no arithmetic of the method: it only draws seeded random numbers and
+lays them out.  Weights are drawn from N(0, 0.02) in fp32 and then truncated to the nearest
+bf16-representable value toward zero (the low 16 bits of the fp32 pattern cleared), so the
+oracle (which reads them as fp32) and the GPU (which reads the same values as bf16 bits)
+see identical numbers.  Truncation is a choice of input distribution, not a rounding step
+of the method.
+
+Every tensor gets its own generator, seeded from ``SeedSequence([seed, tag, index])`` with
+a fixed tag per tensor kind, so adding or removing one tensor never shifts another.
+
+Workload shapes follow the pages: dim 3840, 30 heads of 128, a 34-block stack of
+2 noise-refiner + 2 context-refiner + 30 main blocks (Core AI model zoo, "Z-Image-Turbo
+port", table "Architecture -> export mapping", row DiT); caption width 2560 (FastVideo
+"Z-Image Port Status", summary of the pinned text encoder); caption padding to a multiple
+of 32 with a 45-token prompt and an empty negative (Core AI page, section "The three things
+that each cost a wrong image", item 3); 16-channel latents and a 2x2 patch (Core AI page,
+section "Three more things", patchify feature order); residual stream near 6.7e3 and w2 /
+to_out outputs near 3.1e5 (Core AI page, section "fp16 does not work. bf16 does.").  The
+SwiGLU hidden width 10240 and the 256-wide timestep embedding are not on the pages; they
+are chosen.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+
+# fixed tags, one per tensor kind
+_T_BLOCK = 1
+_T_EMBED = 2
+_T_X = 3
+_T_LAT = 4
+_T_CAP = 5
+_T_OUTLIER = 6
+
+
+@dataclass(frozen=True)
+class Dims:
+    dim: int = 3840
+    n_heads: int = 30
+    head_dim: int = 128
+    ffn_hidden: int = 10240
+    rope_axes: tuple = (32, 48, 48)
+    c_dim: int = 256
+    t_freq: int = 256
+    norm_eps: float = 1e-6
+    rope_theta: float = 10000.0
+    t_scale: float = 1000.0
+    latent_ch: int = 16
+    patch: int = 2
+    cap_dim: int = 2560
+    seq_multiple: int = 32
+    max_cap_len: int = 512
+    n_noise_ref: int = 2
+    n_ctx_ref: int = 2
+    n_main: int = 30
+
+    def replace(self, **kw) -> "Dims":
+        return dataclasses.replace(self, **kw)
+
+
+FULL = Dims()
+TINY = Dims(dim=384, n_heads=3, ffn_hidden=1024)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One named workload: shapes and seeds only."""
+    name: str
+    dims: Dims
+    batch: int
+    lat_h: int              # latent height (pixels / 8)
+    lat_w: int
+    cap_len: tuple          # caption token counts per branch (before padding)
+    t: float = 0.5
+    seed: int = 0
+    outlier_frac: float = 0.0
+    outlier_mag: float = 6.7e3
+    w2_outlier_channels: int = 0
+    w2_outlier_alpha: float = 1.0
+    guidance: float = 1.0
+    num_steps: int = 8
+    shift: float = 3.0
+    extra: dict = field(default_factory=dict)
+
+
+# The five workloads.  cfg1: tiny block/stack; cfg2: one full-width block at 256 px;
+# cfg3: one full-width block at 1024^2 on a cond/uncond pair; cfg4: one full-stack step at
+# 1024^2; cfg5: the 8-step negated-CFG loop at 1024^2 and 1536x1024.
+CFG1 = Workload("tiny block d384 at 128px (64 image tokens + caption 20 -> 32)",
+                TINY, batch=1, lat_h=16, lat_w=16, cap_len=(20,), t=0.5, seed=0)
+CFG2 = Workload("full-width block at 256px (256 image tokens + caption 45 -> 64)",
+                FULL, batch=1, lat_h=32, lat_w=32, cap_len=(45,), t=0.5, seed=2,
+                outlier_frac=0.001)
+# w2_outlier_alpha is fixed by tests/golden/calibrate_w2_alpha.py (oracle only) so that the
+# largest |w2 output| on this input is about 3e5.
+CFG3 = Workload("full-width block at 1024^2, cond/uncond pair (S = 4160 / 4128)",
+                FULL, batch=2, lat_h=128, lat_w=128, cap_len=(45, 10), t=0.5, seed=3,
+                outlier_frac=0.001, w2_outlier_channels=4, w2_outlier_alpha=41756.0)
+CFG4 = Workload("full 34-block stack, one sampler step at 1024^2",
+                FULL, batch=2, lat_h=128, lat_w=128, cap_len=(45, 10), t=0.5, seed=4)
+CFG5 = Workload("8-step negated-CFG FlowMatchEuler pass at 1024x1024",
+                FULL, batch=2, lat_h=128, lat_w=128, cap_len=(45, 10), seed=42,
+                guidance=1.0, num_steps=8, shift=3.0)
+CFG5_WIDE = Workload("8-step negated-CFG FlowMatchEuler pass at 1536x1024",
+                     FULL, batch=2, lat_h=128, lat_w=192, cap_len=(45, 10), seed=42,
+                     guidance=1.0, num_steps=8, shift=3.0)
+
+
+def rng(seed: int, tag: int, index: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(seed), int(tag), int(index)]))
+
+
+def bf16_truncate(a: np.ndarray) -> np.ndarray:
+    """fp32 array -> fp32 array whose values are bf16-representable (low 16 bits cleared)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Bit pattern (uint16) of a bf16-representable fp32 array; exact, no rounding."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    if np.any(u & np.uint32(0xFFFF)):
+        raise ValueError("array is not bf16-representable")
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _normal(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    x = g.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def _weight(g, shape):
+    return bf16_truncate(_normal(g, shape, WEIGHT_STD))
+
+
+def block_weights(dims: Dims, seed: int, index: int = 0, adaln: bool = True,
+                  w2_outlier_channels: int = 0, w2_outlier_alpha: float = 1.0) -> dict:
+    """Weights of one transformer block, [out, in] row-major, as fp32 arrays.
+
+    Matrices are bf16-representable; norm gains are 1 + 0.02 N(0,1) in fp32 (so a wrong
+    gain index is visible); adaLN bias is N(0, 0.02) in fp32.  With adaln=False the block
+    has no modulation weights (context-refiner blocks).
+    """
+    d, H = dims.dim, dims.ffn_hidden
+    base = 16 * index
+    w = {
+        "w_qkv": _weight(rng(seed, _T_BLOCK, base + 0), (3 * d, d)),
+        "w_out": _weight(rng(seed, _T_BLOCK, base + 1), (d, d)),
+        "w1": _weight(rng(seed, _T_BLOCK, base + 2), (H, d)),
+        "w3": _weight(rng(seed, _T_BLOCK, base + 3), (H, d)),
+        "w2": _weight(rng(seed, _T_BLOCK, base + 4), (d, H)),
+        "norm1": (1.0 + _normal(rng(seed, _T_BLOCK, base + 5), (d,), WEIGHT_STD)).astype(np.float32),
+        "norm2": (1.0 + _normal(rng(seed, _T_BLOCK, base + 6), (d,), WEIGHT_STD)).astype(np.float32),
+    }
+    if adaln:
+        w["w_ada"] = _weight(rng(seed, _T_BLOCK, base + 7), (6 * d, dims.c_dim))
+        w["b_ada"] = _normal(rng(seed, _T_BLOCK, base + 8), (6 * d,), WEIGHT_STD)
+    else:
+        w["w_ada"] = None
+        w["b_ada"] = None
+    if w2_outlier_channels:
+        # a few output channels of w2 scaled up, so the FFN output reaches the ~3e5 range
+        g = rng(seed, _T_OUTLIER, index)
+        ch = np.sort(g.choice(d, size=w2_outlier_channels, replace=False))
+        w2 = w["w2"]
+        w2[ch, :] = bf16_truncate(w2[ch, :] * np.float32(w2_outlier_alpha))
+        w["w2_outlier_rows"] = ch
+    return w
+
+
+def embed_weights(dims: Dims, seed: int) -> dict:
+    """x-embed, cap-embed, learned caption pad, timestep MLP and final-layer weights."""
+    d, p, C = dims.dim, dims.patch, dims.latent_ch
+    f = p * p * C
+    cd, tf = dims.c_dim, dims.t_freq
+    k = 0
+
+    def nxt():
+        nonlocal k
+        k += 1
+        return rng(seed, _T_EMBED, k)
+
+    return {
+        "x_emb_w": _weight(nxt(), (d, f)),
+        "x_emb_b": _normal(nxt(), (d,), WEIGHT_STD),
+        "cap_emb_w": _weight(nxt(), (d, dims.cap_dim)),
+        "cap_emb_b": _normal(nxt(), (d,), WEIGHT_STD),
+        "cap_pad": _normal(nxt(), (d,), 1.0),
+        "t_w1": _normal(nxt(), (cd, tf), WEIGHT_STD),
+        "t_b1": _normal(nxt(), (cd,), WEIGHT_STD),
+        "t_w2": _normal(nxt(), (cd, cd), WEIGHT_STD),
+        "t_b2": _normal(nxt(), (cd,), WEIGHT_STD),
+        "final_norm": (1.0 + _normal(nxt(), (d,), WEIGHT_STD)).astype(np.float32),
+        "final_ada_w": _weight(nxt(), (2 * d, cd)),
+        "final_ada_b": _normal(nxt(), (2 * d,), WEIGHT_STD),
+        "final_w": _weight(nxt(), (f, d)),
+        "final_b": _normal(nxt(), (f,), WEIGHT_STD),
+    }
+
+
+def model_weights(dims: Dims, seed: int) -> dict:
+    """All weights of a stack: embeds plus noise-refiner, context-refiner and main blocks."""
+    w = embed_weights(dims, seed)
+    idx = 0
+    nr, cr, mb = [], [], []
+    for _ in range(dims.n_noise_ref):
+        nr.append(block_weights(dims, seed, idx, adaln=True)); idx += 1
+    for _ in range(dims.n_ctx_ref):
+        cr.append(block_weights(dims, seed, idx, adaln=False)); idx += 1
+    for _ in range(dims.n_main):
+        mb.append(block_weights(dims, seed, idx, adaln=True)); idx += 1
+    w["noise_ref"], w["ctx_ref"], w["main"] = nr, cr, mb
+    return w
+
+
+def residual_input(shape, seed: int, outlier_frac: float = 0.0, outlier_mag: float = 6.7e3,
+                   index: int = 0) -> np.ndarray:
+    """Residual-stream input: N(0,1) fp32 with a seeded fraction of entries set to +-mag."""
+    g = rng(seed, _T_X, index)
+    x = _normal(g, shape)
+    if outlier_frac > 0:
+        n = x.size
+        k = int(round(outlier_frac * n))
+        pos = g.choice(n, size=k, replace=False)
+        sign = np.where(g.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+        x.reshape(-1)[pos] = sign * np.float32(outlier_mag)
+    return x
+
+
+def latents(shape, seed: int, index: int = 0) -> np.ndarray:
+    """fp32 N(0,1) latents, shape [..., C, h, w]."""
+    return _normal(rng(seed, _T_LAT, index), shape)
+
+
+def caption_features(batch: int, max_len: int, cap_dim: int, seed: int) -> np.ndarray:
+    """fp32 N(0,1) caption features [batch, max_len, cap_dim] (stand-in for the encoder's
+    penultimate hidden state, which needs trained weights)."""
+    return _normal(rng(seed, _T_CAP, 0), (batch, max_len, cap_dim))
