@@ -1,0 +1,341 @@
+"""ctypes binding of libzdit.so (the gfx950 S3-DiT library).
+
+Argument marshalling only: torch tensors supply device memory (``data_ptr()``) and streams
+(``torch.cuda.current_stream().cuda_stream``); every step of the computation runs in the
+library's HIP kernels.  The names mirror the C ABI in include/zdit.h.  If the library has
+not been built, loading raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libzdit.so")
+
+ZDIT_OK, ZDIT_EINVAL, ZDIT_EUNSUPPORTED, ZDIT_EWORKSPACE, ZDIT_EHIP = 0, -1, -2, -3, -4
+ZDIT_BF16, ZDIT_FP32_DEBUG = 0, 1
+ZDIT_SEQ_IMAGE, ZDIT_SEQ_CAPTION, ZDIT_SEQ_JOINT = 0, 1, 2
+ZDIT_EPI_STORE, ZDIT_EPI_BIAS, ZDIT_EPI_RESID, ZDIT_EPI_SWIGLU = 0, 1, 2, 3
+MAX_BATCH = 16
+
+# every exported symbol of include/zdit.h
+EXPORTS = [
+    "zdit_last_error", "zdit_abi_version", "zdit_block_workspace", "zdit_block_fwd",
+    "zdit_stack_workspace", "zdit_stack_fwd", "zdit_sigmas", "zdit_n_cap", "zdit_euler_step",
+    "zdit_sample_workspace", "zdit_sample", "zdit_rope_tables", "zdit_op_gemm",
+    "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn",
+    "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
+]
+
+
+class zdit_dims(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("ffn_hidden", C.c_int32), ("rope_axes", C.c_int32 * 3), ("c_dim", C.c_int32),
+                ("precision", C.c_int32), ("norm_eps", C.c_float)]
+
+
+class zdit_block_w(C.Structure):
+    _fields_ = [("w_qkv", C.c_void_p), ("w_out", C.c_void_p), ("w1", C.c_void_p),
+                ("w3", C.c_void_p), ("w2", C.c_void_p), ("norm1", C.c_void_p),
+                ("norm2", C.c_void_p), ("w_ada", C.c_void_p), ("b_ada", C.c_void_p)]
+
+
+class zdit_model_cfg(C.Structure):
+    _fields_ = [("d", zdit_dims), ("n_noise_ref", C.c_int32), ("n_ctx_ref", C.c_int32),
+                ("n_main", C.c_int32), ("latent_ch", C.c_int32), ("patch", C.c_int32),
+                ("cap_dim", C.c_int32), ("t_freq", C.c_int32), ("seq_multiple", C.c_int32),
+                ("max_cap_len", C.c_int32), ("rope_theta", C.c_float), ("t_scale", C.c_float)]
+
+
+class zdit_model_w(C.Structure):
+    _fields_ = [("x_emb_w", C.c_void_p), ("x_emb_b", C.c_void_p), ("cap_emb_w", C.c_void_p),
+                ("cap_emb_b", C.c_void_p), ("cap_pad", C.c_void_p), ("t_w1", C.c_void_p),
+                ("t_b1", C.c_void_p), ("t_w2", C.c_void_p), ("t_b2", C.c_void_p),
+                ("noise_ref", C.POINTER(zdit_block_w)), ("ctx_ref", C.POINTER(zdit_block_w)),
+                ("main", C.POINTER(zdit_block_w)), ("final_norm", C.c_void_p),
+                ("final_ada_w", C.c_void_p), ("final_ada_b", C.c_void_p),
+                ("final_w", C.c_void_p), ("final_b", C.c_void_p)]
+
+
+class ZditError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"zdit error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m diffusion_transformer_text_s3_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+        pi32 = C.POINTER(C.c_int32)
+        pf32 = C.POINTER(C.c_float)
+        pd, pw = C.POINTER(zdit_dims), C.POINTER(zdit_block_w)
+        pc, pm = C.POINTER(zdit_model_cfg), C.POINTER(zdit_model_w)
+        sig = {
+            "zdit_last_error": (C.c_char_p, []),
+            "zdit_abi_version": (i32, []),
+            "zdit_block_workspace": (sz, [pd, i32, i32]),
+            "zdit_block_fwd": (i32, [pd, pw, i32, i32, pi32, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_stack_workspace": (sz, [pc, i32, i32, i32, i32]),
+            "zdit_stack_fwd": (i32, [pc, pm, i32, i32, i32, vp, i64, vp, i32, pi32, pf32, vp, vp, sz, vp]),
+            "zdit_sigmas": (i32, [i32, f32, pf32]),
+            "zdit_n_cap": (i32, [i32, i32, pi32]),
+            "zdit_euler_step": (i32, [vp, vp, vp, i64, f32, f32, f32, vp, vp]),
+            "zdit_sample_workspace": (sz, [pc, i32, i32, i32, f32]),
+            "zdit_sample": (i32, [pc, pm, i32, i32, vp, vp, i32, pi32, f32, i32, f32, vp, vp, sz, vp]),
+            "zdit_rope_tables": (i32, [i32, pi32, f32, i32, i32, i32, i32, pi32, vp, vp, vp]),
+            "zdit_op_gemm": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+            "zdit_op_rmsnorm_mod": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
+            "zdit_op_rope": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, vp]),
+            "zdit_op_attn_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_attn": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
+            "zdit_op_patchify": (i32, [i32, i32, i32, i32, vp, i64, vp, vp]),
+            "zdit_op_unpatchify": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+            "zdit_op_cap_pad": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp]),
+            "zdit_op_temb": (i32, [i32, pf32, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
+            "zdit_op_adaln": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().zdit_last_error().decode()
+
+
+def check(code: int):
+    if code != ZDIT_OK:
+        raise ZditError(code, last_error())
+    return code
+
+
+# ----------------------------------------------------------------------------- marshalling
+def ptr(t):
+    """Device (or host) address of a torch tensor, or None."""
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def i32_array(vals):
+    vals = list(vals)
+    return (C.c_int32 * max(1, len(vals)))(*vals)
+
+
+def f32_array(vals):
+    vals = list(vals)
+    return (C.c_float * max(1, len(vals)))(*vals)
+
+
+def stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def make_dims(d, precision=ZDIT_BF16) -> zdit_dims:
+    """zdit_dims from any object with dim / n_heads / head_dim / ffn_hidden / rope_axes /
+    c_dim / norm_eps attributes."""
+    out = zdit_dims()
+    out.dim, out.n_heads, out.head_dim, out.ffn_hidden = d.dim, d.n_heads, d.head_dim, d.ffn_hidden
+    out.rope_axes[:] = list(d.rope_axes)
+    out.c_dim, out.precision, out.norm_eps = d.c_dim, precision, d.norm_eps
+    return out
+
+
+def make_cfg(d, precision=ZDIT_BF16) -> zdit_model_cfg:
+    c = zdit_model_cfg()
+    c.d = make_dims(d, precision)
+    c.n_noise_ref, c.n_ctx_ref, c.n_main = d.n_noise_ref, d.n_ctx_ref, d.n_main
+    c.latent_ch, c.patch, c.cap_dim, c.t_freq = d.latent_ch, d.patch, d.cap_dim, d.t_freq
+    c.seq_multiple, c.max_cap_len = d.seq_multiple, d.max_cap_len
+    c.rope_theta, c.t_scale = d.rope_theta, d.t_scale
+    return c
+
+
+class DeviceBlock:
+    """Device copies of one block's weights (torch tensors) and its zdit_block_w view."""
+
+    MATS = ("w_qkv", "w_out", "w1", "w3", "w2")
+
+    def __init__(self, tensors: dict):
+        self.t = tensors
+        self.w = zdit_block_w()
+        for k in self.MATS + ("norm1", "norm2", "w_ada", "b_ada"):
+            v = tensors.get(k)
+            setattr(self.w, k, None if v is None else v.data_ptr())
+
+
+def _to_dev(a, precision, device, matrix):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    t = torch.from_numpy(a)
+    if matrix and precision == ZDIT_BF16:
+        # the values are bf16-representable: the conversion is exact
+        t = t.to(torch.bfloat16)
+    return t.to(device)
+
+
+def upload_block(wdict: dict, precision=ZDIT_BF16, device="cuda") -> DeviceBlock:
+    """Device tensors for a block weight dict (fp32 numpy arrays)."""
+    out = {}
+    for k in DeviceBlock.MATS + ("w_ada",):
+        if wdict.get(k) is not None:
+            out[k] = _to_dev(wdict[k], precision, device, True)
+    for k in ("norm1", "norm2", "b_ada"):
+        if wdict.get(k) is not None:
+            out[k] = _to_dev(wdict[k], precision, device, False)
+    return DeviceBlock(out)
+
+
+class DeviceModel:
+    """Device copies of all stack weights and the zdit_model_w view (keeps them alive)."""
+
+    MATS = ("x_emb_w", "cap_emb_w", "final_ada_w", "final_w")
+    VECS = ("x_emb_b", "cap_emb_b", "cap_pad", "t_w1", "t_b1", "t_w2", "t_b2", "final_norm",
+            "final_ada_b", "final_b")
+
+    def __init__(self, tensors: dict, noise_ref, ctx_ref, main):
+        self.t = tensors
+        self.blocks = (list(noise_ref), list(ctx_ref), list(main))
+        self._arrs = []
+        self.w = zdit_model_w()
+        for k in self.MATS + self.VECS:
+            setattr(self.w, k, tensors[k].data_ptr())
+        for name, blocks in zip(("noise_ref", "ctx_ref", "main"), self.blocks):
+            arr = (zdit_block_w * max(1, len(blocks)))(*[b.w for b in blocks])
+            self._arrs.append(arr)
+            setattr(self.w, name, C.cast(arr, C.POINTER(zdit_block_w)))
+
+
+def upload_model(W: dict, precision=ZDIT_BF16, device="cuda") -> DeviceModel:
+    t = {}
+    for k in DeviceModel.MATS:
+        t[k] = _to_dev(W[k], precision, device, True)
+    for k in DeviceModel.VECS:
+        t[k] = _to_dev(W[k], precision, device, False)
+    nr = [upload_block(b, precision, device) for b in W["noise_ref"]]
+    cr = [upload_block(b, precision, device) for b in W["ctx_ref"]]
+    mb = [upload_block(b, precision, device) for b in W["main"]]
+    return DeviceModel(t, nr, cr, mb)
+
+
+# ----------------------------------------------------------------------------- calls
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def zdit_block_workspace(dims: zdit_dims, batch: int, s_max: int) -> int:
+    return lib().zdit_block_workspace(C.byref(dims), batch, s_max)
+
+
+def zdit_block_fwd(dims, w: DeviceBlock, batch, s_max, seq_len, x, c, cos, sin, ws, stream=None):
+    return check(lib().zdit_block_fwd(C.byref(dims), C.byref(w.w), batch, s_max, i32_array(seq_len),
+                                      ptr(x), ptr(c), ptr(cos), ptr(sin), ptr(ws), ws.numel(),
+                                      stream_handle(stream)))
+
+
+def zdit_stack_workspace(cfg, batch, lat_h, lat_w, max_cap_len) -> int:
+    return lib().zdit_stack_workspace(C.byref(cfg), batch, lat_h, lat_w, max_cap_len)
+
+
+def zdit_stack_fwd(cfg, m: DeviceModel, batch, lat_h, lat_w, latents, latent_batch_stride, cap_feats,
+                   max_cap_len, cap_len, t, velocity, ws, stream=None):
+    return check(lib().zdit_stack_fwd(C.byref(cfg), C.byref(m.w), batch, lat_h, lat_w, ptr(latents),
+                                      latent_batch_stride, ptr(cap_feats), max_cap_len, i32_array(cap_len),
+                                      f32_array(t), ptr(velocity), ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_sigmas(num_steps: int, shift: float):
+    out = (C.c_float * (num_steps + 1))()
+    check(lib().zdit_sigmas(num_steps, shift, out))
+    return list(out)
+
+
+def zdit_n_cap(cap_len: int, multiple: int = 32) -> int:
+    out = C.c_int32()
+    check(lib().zdit_n_cap(cap_len, multiple, C.byref(out)))
+    return out.value
+
+
+def zdit_euler_step(x, v_cond, v_uncond, n, guidance, sigma, sigma_next, decode_out=None, stream=None):
+    return check(lib().zdit_euler_step(ptr(x), ptr(v_cond), ptr(v_uncond), n, guidance, sigma, sigma_next,
+                                       ptr(decode_out), stream_handle(stream)))
+
+
+def zdit_sample_workspace(cfg, lat_h, lat_w, max_cap_len, guidance) -> int:
+    return lib().zdit_sample_workspace(C.byref(cfg), lat_h, lat_w, max_cap_len, guidance)
+
+
+def zdit_sample(cfg, m: DeviceModel, lat_h, lat_w, x, cap_feats, max_cap_len, cap_len, guidance, num_steps,
+                shift, decode_out, ws, stream=None):
+    return check(lib().zdit_sample(C.byref(cfg), C.byref(m.w), lat_h, lat_w, ptr(x), ptr(cap_feats), max_cap_len,
+                                   i32_array(cap_len), guidance, num_steps, shift, ptr(decode_out), ptr(ws),
+                                   ws.numel(), stream_handle(stream)))
+
+
+def zdit_rope_tables(kind, rope_axes, theta, batch, s_max, grid_h, grid_w, n_cap, cos_out, sin_out, stream=None):
+    return check(lib().zdit_rope_tables(kind, i32_array(rope_axes), theta, batch, s_max, grid_h, grid_w,
+                                        i32_array(n_cap if n_cap is not None else [0]), ptr(cos_out),
+                                        ptr(sin_out), stream_handle(stream)))
+
+
+def zdit_op_gemm(precision, epilogue, M, N, K, A, B, B2, vec, Cout, stream=None):
+    return check(lib().zdit_op_gemm(precision, epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
+                                    stream_handle(stream)))
+
+
+def zdit_op_rmsnorm_mod(precision, rows, dim, x, gain, shift, scale, eps, out, stream=None):
+    return check(lib().zdit_op_rmsnorm_mod(precision, rows, dim, ptr(x), ptr(gain), ptr(shift), ptr(scale), eps,
+                                           ptr(out), stream_handle(stream)))
+
+
+def zdit_op_rope(precision, batch, s_max, n_heads, seq_len, qkv, cos, sin, stream=None):
+    return check(lib().zdit_op_rope(precision, batch, s_max, n_heads, i32_array(seq_len), ptr(qkv), ptr(cos),
+                                    ptr(sin), stream_handle(stream)))
+
+
+def zdit_op_attn_workspace(precision, batch, s_max, n_heads) -> int:
+    return lib().zdit_op_attn_workspace(precision, batch, s_max, n_heads)
+
+
+def zdit_op_attn(precision, batch, s_max, n_heads, seq_len, qkv, out, ws, stream=None):
+    return check(lib().zdit_op_attn(precision, batch, s_max, n_heads, i32_array(seq_len), ptr(qkv), ptr(out),
+                                    ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_patchify(batch, Cch, h, w, lat, lat_batch_stride, tokens, stream=None):
+    return check(lib().zdit_op_patchify(batch, Cch, h, w, ptr(lat), lat_batch_stride, ptr(tokens),
+                                        stream_handle(stream)))
+
+
+def zdit_op_unpatchify(batch, Cch, h, w, tokens, lat, stream=None):
+    return check(lib().zdit_op_unpatchify(batch, Cch, h, w, ptr(tokens), ptr(lat), stream_handle(stream)))
+
+
+def zdit_op_cap_pad(batch, s_max, dim, row0, cap_len, cap_pad, x, stream=None):
+    return check(lib().zdit_op_cap_pad(batch, s_max, dim, row0, i32_array(cap_len), ptr(cap_pad), ptr(x),
+                                       stream_handle(stream)))
+
+
+def zdit_op_temb(batch, t, t_freq, c_dim, t_scale, w1, b1, w2, b2, c_out, stream=None):
+    return check(lib().zdit_op_temb(batch, f32_array(t), t_freq, c_dim, t_scale, ptr(w1), ptr(b1), ptr(w2),
+                                    ptr(b2), ptr(c_out), stream_handle(stream)))
+
+
+def zdit_op_adaln(precision, batch, c_dim, n_out, c, w, b, out, stream=None):
+    return check(lib().zdit_op_adaln(precision, batch, c_dim, n_out, ptr(c), ptr(w), ptr(b), ptr(out),
+                                     stream_handle(stream)))

@@ -1,0 +1,112 @@
+// Internal types and kernel launchers of the gfx950 S3-DiT library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zdit {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxBatch = 16;
+constexpr int kHeadDim = 128;
+
+// Maps a compact row index m (0..rows-1, `rows_per_batch` rows per branch) to a row of a
+// branch-strided buffer: address = base + b * batch_stride + r * ld, written only when
+// r < valid[b].
+struct RowMap {
+  int rows_per_batch;
+  int64_t batch_stride;
+  int64_t ld;
+  int valid[kMaxBatch];
+};
+
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* B2;        // second weight (SwiGLU up projection)
+  void* C;
+  const float* vec;      // bias [N] (EPI_BIAS) or gate (EPI_RESID; NULL = 1)
+  int64_t vec_bstride;   // gate branch stride in floats
+  int M, N, K;
+  int64_t lda, ldb;
+  RowMap out;
+};
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(int epi, const GemmArgs& g, hipStream_t s);
+
+struct AttnArgs {
+  const void* qkv;   // [B, s_max, 3*D]
+  void* vt;          // bf16 path: [B, nh, 128, s_pad] transposed values (workspace)
+  void* out;         // [B, s_max, D]
+  int batch, s_max, s_pad, n_heads;
+  int seq_len[kMaxBatch];
+};
+size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads);
+hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s);
+
+// Row r of branch b is x + b * x_bstride + r * dim; out is compact [batch * rows, dim].
+// shift / scale: fp32 [dim] vectors of branch 0, branch b at + b * mod_bstride; both NULL
+// for no modulation.  Rows with r >= valid[b] are written as 0.
+struct NormArgs {
+  const float* x;
+  int64_t x_bstride;
+  int rows_per_batch;
+  int batch;
+  int dim;
+  const float* gain;
+  const float* shift;
+  const float* scale;
+  int64_t mod_bstride;
+  float eps;
+  void* out;
+  int valid[kMaxBatch];
+};
+hipError_t launch_rmsnorm_mod(int precision, const NormArgs& a, hipStream_t s);
+
+struct RopeArgs {
+  void* qkv;
+  const float* cos;
+  const float* sin;
+  int64_t tab_bstride;   // floats between branches of the tables (0 = shared)
+  int batch, s_max, n_heads;
+  int seq_len[kMaxBatch];
+};
+hipError_t launch_rope(int precision, const RopeArgs& a, hipStream_t s);
+
+struct RopeTabArgs {
+  float* cos;
+  float* sin;
+  int kind, batch, s_max, grid_h, grid_w;
+  int axes[3];
+  float theta;
+  int n_cap[kMaxBatch];
+};
+hipError_t launch_rope_tables(const RopeTabArgs& a, hipStream_t s);
+
+hipError_t launch_patchify(int precision, int batch, int C, int h, int w, const float* lat,
+                           int64_t lat_bstride, void* tokens, hipStream_t s);
+hipError_t launch_unpatchify(int batch, int C, int h, int w, const float* tokens, float* lat,
+                             hipStream_t s);
+hipError_t launch_cap_pad(int batch, int s_max, int dim, int row0, const int* cap_len,
+                          int multiple, const float* pad, float* x, hipStream_t s);
+hipError_t launch_convert(int precision, const float* in, void* out, int64_t n, hipStream_t s);
+hipError_t launch_euler(float* x, const float* vc, const float* vu, int64_t n, float g,
+                        float sigma, float sigma_next, float* dec, hipStream_t s);
+hipError_t launch_temb(int batch, const float* t, int t_freq, int c_dim, float t_scale,
+                       const float* w1, const float* b1, const float* w2, const float* b2,
+                       float* c, hipStream_t s);
+hipError_t launch_adaln(int precision, int batch, int c_dim, int n_out, const float* c,
+                        const void* w, const float* b, float* out, hipStream_t s);
+hipError_t launch_copy_rows(const float* src, int64_t src_bstride, float* dst,
+                            int64_t dst_bstride, int batch, int64_t n, hipStream_t s);
+
+}  // namespace zdit

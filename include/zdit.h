@@ -1,0 +1,298 @@
+/*
+ * zdit.h - C ABI of the MI355X (gfx950) S3-DiT hot path: the Z-Image-Turbo single-stream
+ * diffusion transformer block, its 2 + 2 + 30 block stack and the 8-step negated-CFG
+ * FlowMatchEuler sampler.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [CoreAI]  Core AI model zoo, "Z-Image-Turbo port - a 6B diffusion DiT on Core AI, and
+ *             why it is Mac-only".
+ *   [Status]  FastVideo, tests/local_tests/zimage "Z-Image Port Status".
+ *   [Jobs]    1Cat-vLLM "Native creative jobs", section "Recipes and precision".
+ *
+ * Conventions for every call:
+ *   - Device pointers are HIP device addresses; host pointers are ordinary memory.  The
+ *     caller owns every buffer (weights, activations, workspace).  Pointers are borrowed for
+ *     the call and must stay valid until the enqueued work completes.  The library allocates
+ *     no device memory and keeps no pointer after returning.
+ *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
+ *     Nothing synchronises; no host<->device copy is made.
+ *   - Arguments are validated before anything is enqueued.  On error nothing runs, outputs
+ *     are untouched, the return value is negative and zdit_last_error() says why.  Faults
+ *     during execution surface at the caller's next synchronisation, as in any HIP library.
+ *   - Matrices are row-major.  Linear weights are [out, in] (the `in` index contiguous).
+ *     In ZDIT_BF16 precision, weight matrices are bf16 and activations between kernels are
+ *     bf16 (GEMM operands) or fp32 (residual stream, norms, modulation, softmax).  In
+ *     ZDIT_FP32_DEBUG precision every weight and activation is fp32.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are the dense ones implied
+ *     by the shapes given.
+ */
+#ifndef ZDIT_H
+#define ZDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t zdit_status;
+enum {
+  ZDIT_OK = 0,
+  ZDIT_EINVAL = -1,        /* bad argument (null/misaligned pointer, bad size, bad length) */
+  ZDIT_EUNSUPPORTED = -2,  /* dimensions the kernels do not implement */
+  ZDIT_EWORKSPACE = -3,    /* workspace smaller than the matching *_workspace() query */
+  ZDIT_EHIP = -4           /* a HIP launch failed */
+};
+
+enum { ZDIT_BF16 = 0, ZDIT_FP32_DEBUG = 1 };
+
+/* Token-sequence layouts for RoPE tables. */
+enum { ZDIT_SEQ_IMAGE = 0, ZDIT_SEQ_CAPTION = 1, ZDIT_SEQ_JOINT = 2 };
+
+#define ZDIT_MAX_BATCH 16
+#define ZDIT_ABI_VERSION 1
+
+/* Text of the last error on the calling thread; valid until the next zdit_* call on it. */
+const char* zdit_last_error(void);
+int32_t zdit_abi_version(void);
+
+/* Block dimensions.  The kernels implement head_dim 128, rope axes summing to head_dim
+ * (each even), dim = n_heads * head_dim with dim % 128 == 0, ffn_hidden % 128 == 0,
+ * c_dim % 64 == 0 and c_dim <= 1024.  norm_eps is the RMSNorm epsilon. */
+typedef struct {
+  int32_t dim, n_heads, head_dim, ffn_hidden;
+  int32_t rope_axes[3];
+  int32_t c_dim;
+  int32_t precision; /* ZDIT_BF16 or ZDIT_FP32_DEBUG */
+  float norm_eps;
+} zdit_dims;
+
+/* One block's weights (device).  w_qkv [3*dim, dim]: rows 0..dim-1 produce q, dim..2dim-1
+ * k, 2dim..3dim-1 v; heads are contiguous head_dim-wide slices.  w_out [dim, dim];
+ * w1, w3 [ffn_hidden, dim]; w2 [dim, ffn_hidden]; norm1, norm2 fp32 [dim].  w_ada
+ * [6*dim, c_dim] and b_ada fp32 [6*dim] give (shift1, scale1, gate1, shift2, scale2,
+ * gate2); both NULL for a block without adaLN (shift = scale = 0, gate = 1). */
+typedef struct {
+  const void *w_qkv, *w_out, *w1, *w3, *w2;
+  const float *norm1, *norm2;
+  const void* w_ada;
+  const float* b_ada;
+} zdit_block_w;
+
+/* ---------------------------------------------------------------------------------------
+ * S3-DiT block forward ([CoreAI] table "Architecture -> export mapping", row DiT: adaLN,
+ * 3-axis RoPE in the real interleaved cos/sin form, joint attention over one sequence):
+ *   (shift1, scale1, gate1, shift2, scale2, gate2) = W_ada SiLU(c) + b_ada
+ *   h  = RMSNorm(x; norm1) (1 + scale1) + shift1
+ *   q, k, v = split(h W_qkv^T); q, k rotated by RoPE(cos, sin)
+ *   x += gate1 * (softmax(q k^T / sqrt(head_dim)) v) W_out^T      (keys j < seq_len[b])
+ *   h2 = RMSNorm(x; norm2) (1 + scale2) + shift2
+ *   x += gate2 * ((SiLU(h2 W1^T) * (h2 W3^T)) W2^T)
+ * Rows j >= seq_len[b] of x are padding: masked as keys and left untouched.
+ *
+ *   batch        1..ZDIT_MAX_BATCH rows (branches) of x
+ *   s_max        rows per branch in x (>= every seq_len)
+ *   seq_len      host [batch], each in 1..s_max: valid rows of branch b
+ *   x            device fp32 [batch, s_max, dim], in/out (the residual stream)
+ *   c            device fp32 [batch, c_dim] conditioning vector; ignored when w_ada NULL
+ *   rope_cos/sin device fp32 [batch, s_max, head_dim/2] (see zdit_rope_tables)
+ *   ws           device workspace of at least zdit_block_workspace() bytes, 256-aligned
+ * ------------------------------------------------------------------------------------- */
+size_t zdit_block_workspace(const zdit_dims* dims, int32_t batch, int32_t s_max);
+zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t batch,
+                           int32_t s_max, const int32_t* seq_len, float* x, const float* c,
+                           const float* rope_cos, const float* rope_sin, void* ws,
+                           size_t ws_bytes, void* hip_stream);
+
+/* Whole-model configuration.  n_noise_ref adaLN blocks on image tokens, n_ctx_ref blocks
+ * without adaLN on caption tokens, n_main adaLN blocks on the joint sequence ([CoreAI]
+ * "Architecture -> export mapping", row DiT: 2 + 2 + 30).  latent_ch 16, patch 2 (the
+ * kernels implement exactly these), cap_dim the caption feature width, t_freq the
+ * timestep-embedding width (== c_dim), seq_multiple the caption padding multiple (32),
+ * max_cap_len the caption length limit (512), rope_theta the RoPE base, t_scale the
+ * factor applied to model time before the sinusoid (1000). */
+typedef struct {
+  zdit_dims d;
+  int32_t n_noise_ref, n_ctx_ref, n_main;
+  int32_t latent_ch, patch, cap_dim, t_freq, seq_multiple, max_cap_len;
+  float rope_theta, t_scale;
+} zdit_model_cfg;
+
+/* Whole-model weights (device pointers; the three block arrays are HOST arrays of
+ * zdit_block_w).  x_emb_w [dim, patch*patch*latent_ch], cap_emb_w [dim, cap_dim] (bf16 or
+ * fp32 by precision), biases fp32 [dim]; cap_pad fp32 [dim] (the learned caption pad);
+ * t_w1 fp32 [c_dim, t_freq], t_b1 [c_dim], t_w2 fp32 [c_dim, c_dim], t_b2 [c_dim];
+ * final_norm fp32 [dim]; final_ada_w [2*dim, c_dim] (shift then scale), final_ada_b fp32
+ * [2*dim]; final_w [patch*patch*latent_ch, dim], final_b fp32 [patch*patch*latent_ch]. */
+typedef struct {
+  const void* x_emb_w;
+  const float* x_emb_b;
+  const void* cap_emb_w;
+  const float* cap_emb_b;
+  const float* cap_pad;
+  const float *t_w1, *t_b1, *t_w2, *t_b2;
+  const zdit_block_w *noise_ref, *ctx_ref, *main;
+  const float* final_norm;
+  const void* final_ada_w;
+  const float* final_ada_b;
+  const void* final_w;
+  const float* final_b;
+} zdit_model_w;
+
+/* ---------------------------------------------------------------------------------------
+ * DiT stack forward for `batch` branches ([CoreAI] "Architecture -> export mapping": x-embed
+ * + cap-embed, noise refiners, context refiners, main blocks, final layer; host patchify,
+ * RoPE, pad-mask and unpatchify done here on the device).  Each branch b:
+ *   tokens  = patchify(latent_b) (feature f = (dy*2 + dx)*16 + ch, [CoreAI] "Three more
+ *             things"); x_img = tokens W_x^T + b_x
+ *   caption = cap_feats_b[0..L_b) W_cap^T + b_cap, then rows L_b..n_cap_b-1 set to cap_pad,
+ *             n_cap_b = round_up(L_b, 32) ([CoreAI] "The three things that each cost a
+ *             wrong image", item 3: pads are attention context, not masked)
+ *   c       = W2 SiLU(W1 [cos(1000 t f_k), sin(1000 t f_k)] + b1) + b2
+ *   noise refiners on x_img, context refiners on the caption, main blocks on the
+ *   sequence (image tokens, then caption tokens), final layer, unpatchify.
+ *
+ *   latents       device fp32 [batch, latent_ch, lat_h, lat_w] with branch stride
+ *                 latent_batch_stride floats (0: one latent shared by every branch)
+ *   cap_feats     device fp32 [batch, max_cap_len, cap_dim]
+ *   cap_len       host [batch], each in 1..min(max_cap_len, cfg->max_cap_len)
+ *   t             host [batch] model time (1 - sigma for the sampler)
+ *   velocity      device fp32 [batch, latent_ch, lat_h, lat_w], written
+ *   lat_h, lat_w  even, >= 2
+ * ------------------------------------------------------------------------------------- */
+size_t zdit_stack_workspace(const zdit_model_cfg* cfg, int32_t batch, int32_t lat_h,
+                            int32_t lat_w, int32_t max_cap_len);
+zdit_status zdit_stack_fwd(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_t batch,
+                           int32_t lat_h, int32_t lat_w, const float* latents,
+                           int64_t latent_batch_stride, const float* cap_feats,
+                           int32_t max_cap_len, const int32_t* cap_len, const float* t,
+                           float* velocity, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Shifted FlowMatchEuler sigmas, host only: out[i] = shift (1 - i/n) / (shift (1 - i/n) +
+ * i/n) for i = 0..num_steps, computed in double and stored fp32; out[0] = 1 and
+ * out[num_steps] = 0 exactly ([CoreAI] "Three more things": closed form with t = i/(n-1)
+ * over n = num_steps + 1 points; [Status] scheduler_contract: endpoint-preserving
+ * num_steps + 1 schedule, sigma_min 0).  out: host [num_steps + 1]; num_steps 1..1000,
+ * shift > 0. */
+zdit_status zdit_sigmas(int32_t num_steps, float shift, float* out);
+
+/* Padded caption length round_up(cap_len, multiple) ([CoreAI] "The three things...", item
+ * 3).  cap_len 1..512, multiple 1..512.  Host only. */
+zdit_status zdit_n_cap(int32_t cap_len, int32_t multiple, int32_t* out);
+
+/* One negated-CFG Euler update, fp32, each product and sum rounded separately:
+ *   d = v_cond - v_uncond; e = guidance * d; u = v_cond + e; np = -u   ([CoreAI] "The three
+ *   things...", item 2: noise_pred = -(pos + g (pos - neg)))
+ *   x = x + (sigma_next - sigma) * np
+ *   decode_out = x / 0.3611 + 0.1159 when decode_out != NULL ([Status] decode_contract;
+ *   x itself stays raw, so the unscale is applied exactly once)
+ * v_uncond NULL means a single branch (np = -v_cond) and requires guidance == 0.
+ * x, v_cond, v_uncond, decode_out: device fp32 [n]; n >= 0 (0 is a no-op). */
+zdit_status zdit_euler_step(float* x, const float* v_cond, const float* v_uncond, int64_t n,
+                            float guidance, float sigma, float sigma_next, float* decode_out,
+                            void* hip_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The full sampler: num_steps negated-CFG FlowMatchEuler updates ([Status]
+ * scheduler_contract: no DiT call at the final zero sigma; [CoreAI] "Architecture -> export
+ * mapping", row Sampler: FlowMatchEuler, 8 steps, guidance 1.0, host loop).  Step i runs
+ * the stack on the cond branch (and the uncond branch when guidance != 0) at model time
+ * 1 - sigma_i on the shared latent x, then zdit_euler_step from sigma_i to sigma_{i+1}.
+ *   x            device fp32 [latent_ch, lat_h, lat_w]: the initial noise in, the raw final
+ *                latent out
+ *   cap_feats    device fp32 [nb, max_cap_len, cap_dim], branch 0 cond, branch 1 uncond
+ *                (nb = 2 when guidance != 0, else 1)
+ *   cap_len      host [nb]
+ *   decode_out   NULL or device fp32 [latent_ch, lat_h, lat_w]: final latent unscaled once
+ * ------------------------------------------------------------------------------------- */
+size_t zdit_sample_workspace(const zdit_model_cfg* cfg, int32_t lat_h, int32_t lat_w,
+                             int32_t max_cap_len, float guidance);
+zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_t lat_h,
+                        int32_t lat_w, float* x, const float* cap_feats, int32_t max_cap_len,
+                        const int32_t* cap_len, float guidance, int32_t num_steps,
+                        float shift, float* decode_out, void* ws, size_t ws_bytes,
+                        void* hip_stream);
+
+/* RoPE cos/sin tables for one of the three sequence layouts, fp32 [batch, s_max,
+ * head_dim/2], computed on the device in double and rounded to fp32 ([CoreAI]
+ * "Architecture -> export mapping", row DiT: precomputed cos/sin; [Status] issue I006:
+ * RoPE buffers stay fp32).  Positions: image token (r, c) of a grid_h x grid_w grid ->
+ * (0, r, c) in row-major order; caption token j -> (1 + j, 0, 0); ZDIT_SEQ_JOINT is the
+ * image tokens followed by n_cap[b] caption tokens.  Column k enumerates rotation pairs:
+ * axis 0's rope_axes[0]/2 pairs, then axis 1's, then axis 2's; pair p of axis a turns by
+ * pos_a * theta^(-2p / rope_axes[a]).  Rows past a branch's length get cos 1, sin 0.
+ * n_cap: host [batch] (ignored for ZDIT_SEQ_IMAGE).  cos_out, sin_out: device. */
+zdit_status zdit_rope_tables(int32_t kind, const int32_t rope_axes[3], float theta,
+                             int32_t batch, int32_t s_max, int32_t grid_h, int32_t grid_w,
+                             const int32_t* n_cap, float* cos_out, float* sin_out,
+                             void* hip_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Single-kernel entry points, for tests and measurement.  They run exactly the kernels the
+ * block and stack use.
+ * ------------------------------------------------------------------------------------- */
+
+/* GEMM epilogues: C = A B^T with A [M, K], B [N, K] (K % 64 == 0 in ZDIT_BF16).
+ *   ZDIT_EPI_STORE   C [M, N] activation type (bf16 / fp32) = A B^T
+ *   ZDIT_EPI_BIAS    C [M, N] fp32 = A B^T + vec[n]
+ *   ZDIT_EPI_RESID   C [M, N] fp32 += vec[n] * (A B^T)   (vec NULL: gate 1)
+ *   ZDIT_EPI_SWIGLU  C [M, N] activation type = SiLU(A B^T) * (A B2^T), B and B2 [N, K] */
+enum { ZDIT_EPI_STORE = 0, ZDIT_EPI_BIAS = 1, ZDIT_EPI_RESID = 2, ZDIT_EPI_SWIGLU = 3 };
+zdit_status zdit_op_gemm(int32_t precision, int32_t epilogue, int32_t M, int32_t N, int32_t K,
+                         const void* A, const void* B, const void* B2, const float* vec,
+                         void* C, void* hip_stream);
+
+/* RMSNorm + modulation: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * gain * (1 + scale) +
+ * shift over `rows` rows of `dim`; x fp32, gain/shift/scale fp32 [dim] (shift/scale NULL:
+ * 0); out activation type. */
+zdit_status zdit_op_rmsnorm_mod(int32_t precision, int32_t rows, int32_t dim, const float* x,
+                                const float* gain, const float* shift, const float* scale,
+                                float eps, void* out, void* hip_stream);
+
+/* RoPE on the q and k parts of a fused qkv buffer [batch, s_max, 3 * n_heads * 128]
+ * (activation type), in place, with tables [batch, s_max, 64]; rows >= seq_len[b] are not
+ * touched.  Bit-exact contract: y0 = x0 c - x1 s, y1 = x0 s + x1 c in fp32, each product
+ * and sum rounded, then rounded to the activation type (bf16 ties-to-even). */
+zdit_status zdit_op_rope(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads,
+                         const int32_t* seq_len, void* qkv, const float* cos, const float* sin,
+                         void* hip_stream);
+
+/* Joint attention on a fused, already rotated qkv buffer [batch, s_max, 3 * n_heads * 128]
+ * -> out [batch, s_max, n_heads * 128] (activation type); keys j >= seq_len[b] masked; rows
+ * >= seq_len[b] of out are written as 0.  ws: zdit_op_attn_workspace() bytes. */
+size_t zdit_op_attn_workspace(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads);
+zdit_status zdit_op_attn(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads,
+                         const int32_t* seq_len, const void* qkv, void* out, void* ws,
+                         size_t ws_bytes, void* hip_stream);
+
+/* Patchify latents [batch, C, h, w] (branch stride lat_batch_stride floats) into fp32 tokens
+ * [batch, (h/2)(w/2), 4C], token r*(w/2)+c, feature (dy*2 + dx)*C + ch. */
+zdit_status zdit_op_patchify(int32_t batch, int32_t C, int32_t h, int32_t w, const float* lat,
+                             int64_t lat_batch_stride, float* tokens, void* hip_stream);
+/* Inverse: fp32 tokens [batch, (h/2)(w/2), 4C] -> latents [batch, C, h, w]. */
+zdit_status zdit_op_unpatchify(int32_t batch, int32_t C, int32_t h, int32_t w,
+                               const float* tokens, float* lat, void* hip_stream);
+
+/* Learned caption pad: for branch b, rows row0 + j of x [batch, s_max, dim] (fp32) with
+ * cap_len[b] <= j < round_up(cap_len[b], 32) are set to cap_pad [dim]; other rows untouched. */
+zdit_status zdit_op_cap_pad(int32_t batch, int32_t s_max, int32_t dim, int32_t row0,
+                            const int32_t* cap_len, const float* cap_pad, float* x,
+                            void* hip_stream);
+
+/* Timestep conditioning c [batch, c_dim] = W2 SiLU(W1 e + b1) + b2 with e = [cos(t_scale t
+ * f_k), sin(t_scale t f_k)], f_k = 10000^(-k / (t_freq/2)); t host [batch]; fp32 weights. */
+zdit_status zdit_op_temb(int32_t batch, const float* t, int32_t t_freq, int32_t c_dim,
+                         float t_scale, const float* w1, const float* b1, const float* w2,
+                         const float* b2, float* c_out, void* hip_stream);
+
+/* adaLN projection out [batch, n_out] fp32 = W SiLU(c) + b, W [n_out, c_dim] (bf16 or fp32
+ * by precision), b fp32 [n_out], c fp32 [batch, c_dim]. */
+zdit_status zdit_op_adaln(int32_t precision, int32_t batch, int32_t c_dim, int32_t n_out,
+                          const float* c, const void* w, const float* b, float* out,
+                          void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZDIT_H */

@@ -1,0 +1,161 @@
+"""The C-ABI library loads, exports every symbol include/zdit.h declares, and its host-only
+logic (sigmas, n_cap, workspace queries, argument validation) behaves; no device work."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from conftest import ROOT, golden
+from diffusion_transformer_text_s3_amd import binding as Z
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "zdit.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zdit_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = Z.lib()
+    declared = _header_functions()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(Z.EXPORTS) == declared
+    assert L.zdit_abi_version() == 1
+
+
+def test_sigmas_match_oracle_bit_exact():
+    for n in (1, 2, 4, 8, 20, 50, 1000):
+        for shift in (1.0, 3.0, 7.5):
+            got = np.array(Z.zdit_sigmas(n, shift), dtype=np.float32)
+            np.testing.assert_array_equal(got, O.sigmas(n, shift))
+    got = Z.zdit_sigmas(8, 3.0)
+    assert got[0] == 1.0 and got[-1] == 0.0
+
+
+def test_n_cap_matches_oracle_and_pages():
+    for L, want in golden("n_cap_cases.txt"):
+        assert Z.zdit_n_cap(int(L)) == int(want)
+    for L in range(1, 513):
+        assert Z.zdit_n_cap(L) == O.n_cap(L)
+
+
+@pytest.mark.parametrize("bad", [0, -3, 513])
+def test_n_cap_rejects(bad):
+    with pytest.raises(Z.ZditError) as e:
+        Z.zdit_n_cap(bad)
+    assert e.value.code == Z.ZDIT_EINVAL
+
+
+def test_sigmas_rejects():
+    for n, s in ((0, 3.0), (1001, 3.0), (8, 0.0), (8, -1.0), (8, float("nan"))):
+        with pytest.raises(Z.ZditError):
+            Z.zdit_sigmas(n, s)
+
+
+def test_block_workspace_and_dims_validation():
+    d = Z.make_dims(synth.FULL)
+    ws = Z.zdit_block_workspace(d, 2, 4160)
+    # h + qkv + vt + o, plus the modulation vectors
+    assert ws >= 2 * 4160 * 3840 * 2 * 5
+    bad = Z.make_dims(synth.FULL)
+    bad.head_dim = 64
+    assert Z.zdit_block_workspace(bad, 2, 4160) == 0
+    bad = Z.make_dims(synth.FULL)
+    bad.rope_axes[:] = [32, 48, 40]
+    assert Z.zdit_block_workspace(bad, 2, 4160) == 0
+    assert Z.zdit_block_workspace(d, 0, 10) == 0 and Z.zdit_block_workspace(d, 17, 10) == 0
+
+
+def _fake(addr=1 << 20):
+    return C.c_void_p(addr)
+
+
+def test_block_fwd_rejects_bad_arguments_before_launch():
+    L = Z.lib()
+    d = Z.make_dims(synth.TINY)
+    w = Z.zdit_block_w()
+    for k in ("w_qkv", "w_out", "w1", "w3", "w2", "norm1", "norm2"):
+        setattr(w, k, 1 << 20)
+    p = _fake()
+    # seq_len outside 1..s_max
+    for seq in ([0], [97]):
+        rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array(seq), p, None, p, p, p, 1 << 30, None)
+        assert rc == Z.ZDIT_EINVAL and "seq_len" in Z.last_error()
+    # misaligned x
+    rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), _fake((1 << 20) + 4), None, p, p, p,
+                          1 << 30, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
+    # workspace too small
+    rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), p, None, p, p, p, 1024, None)
+    assert rc == Z.ZDIT_EWORKSPACE
+    # adaLN weights without c
+    w.w_ada, w.b_ada = 1 << 20, 1 << 20
+    rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), p, None, p, p, p, 1 << 30, None)
+    assert rc == Z.ZDIT_EINVAL
+    # unsupported head dim
+    d.head_dim = 64
+    rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), p, p, p, p, p, 1 << 30, None)
+    assert rc == Z.ZDIT_EUNSUPPORTED
+
+
+def test_euler_step_rejects_missing_uncond_with_guidance():
+    L = Z.lib()
+    p = _fake()
+    rc = L.zdit_euler_step(p, p, None, 10, 1.0, 1.0, 0.5, None, None)
+    assert rc == Z.ZDIT_EINVAL and "v_uncond" in Z.last_error()
+    assert L.zdit_euler_step(p, p, None, -1, 0.0, 1.0, 0.5, None, None) == Z.ZDIT_EINVAL
+    # n == 0 is a no-op that launches nothing
+    assert L.zdit_euler_step(None, None, None, 0, 0.0, 1.0, 0.5, None, None) == Z.ZDIT_OK
+
+
+def test_stack_fwd_rejects_bad_caption_lengths():
+    L = Z.lib()
+    dims = synth.TINY
+    cfg = Z.make_cfg(dims)
+    blk = Z.zdit_block_w()
+    for k in ("w_qkv", "w_out", "w1", "w3", "w2", "norm1", "norm2", "w_ada", "b_ada"):
+        setattr(blk, k, 1 << 20)
+    arr = (Z.zdit_block_w * 40)(*([blk] * 40))
+    ctx = Z.zdit_block_w()
+    for k in ("w_qkv", "w_out", "w1", "w3", "w2", "norm1", "norm2"):
+        setattr(ctx, k, 1 << 20)
+    carr = (Z.zdit_block_w * 4)(*([ctx] * 4))
+    mw = Z.zdit_model_w()
+    for k, _ in Z.zdit_model_w._fields_:
+        if k not in ("noise_ref", "ctx_ref", "main"):
+            setattr(mw, k, 1 << 20)
+    mw.noise_ref = C.cast(arr, C.POINTER(Z.zdit_block_w))
+    mw.main = C.cast(arr, C.POINTER(Z.zdit_block_w))
+    mw.ctx_ref = C.cast(carr, C.POINTER(Z.zdit_block_w))
+    p = _fake()
+    for cl, why in (([0, 10], "cap_len"), ([45, 600], "cap_len"), ([45, 30], None)):
+        rc = L.zdit_stack_fwd(C.byref(cfg), C.byref(mw), 2, 16, 16, p, 0, p, 64, Z.i32_array(cl),
+                              Z.f32_array([0.5, 0.5]), p, p, 16, None)
+        if why:
+            assert rc == Z.ZDIT_EINVAL and why in Z.last_error()
+        else:
+            assert rc == Z.ZDIT_EWORKSPACE  # valid arguments, workspace too small: still no launch
+    # odd latent size
+    rc = L.zdit_stack_fwd(C.byref(cfg), C.byref(mw), 2, 15, 16, p, 0, p, 64, Z.i32_array([4, 4]),
+                          Z.f32_array([0.5, 0.5]), p, p, 1 << 40, None)
+    assert rc == Z.ZDIT_EINVAL
+    # a main block without adaLN weights
+    bad = (Z.zdit_block_w * 40)(*([ctx] * 40))
+    mw.main = C.cast(bad, C.POINTER(Z.zdit_block_w))
+    rc = L.zdit_stack_fwd(C.byref(cfg), C.byref(mw), 2, 16, 16, p, 0, p, 64, Z.i32_array([4, 4]),
+                          Z.f32_array([0.5, 0.5]), p, p, 1 << 40, None)
+    assert rc == Z.ZDIT_EINVAL and "adaLN" in Z.last_error()
+
+
+def test_gemm_op_rejects_unsupported_k():
+    L = Z.lib()
+    p = _fake()
+    assert L.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_STORE, 16, 16, 40, p, p, None, None, p, None) == Z.ZDIT_EUNSUPPORTED
+    assert L.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, 16, 16, 64, p, p, None, None, p, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_gemm(Z.ZDIT_BF16, 9, 16, 16, 64, p, p, None, None, p, None) == Z.ZDIT_EINVAL
