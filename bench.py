@@ -1,0 +1,273 @@
+"""Throughput of the S3-DiT hot path on one MI355X.
+
+A step is one full 8-step negated-CFG FlowMatchEuler pass at 1024x1024 (cond caption 45 ->
+n_cap 64, uncond 10 -> 32): 16 stack forwards of 2 + 2 + 30 blocks at dim 3840 plus the 8
+Euler updates and the decode unscale, through zdit_sample.  Inputs are resident in HBM before
+the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16 MFMA)
+PEAK_HBM_GBS = 8000.0
+METRIC = "S3-DiT block fwd TFLOP/s (% bf16 MFMA peak) + ms per 8-step CFG 1024² DiT pass"
+
+
+def block_flops(S, d, H):
+    """Algorithmic FLOPs of one block on S valid tokens: QKV, out, w1/w3, w2 GEMMs and
+    non-causal attention (QK^T and PV)."""
+    return 2 * S * d * (3 * d + d + 3 * H) + 4 * S * S * d
+
+
+def pass_flops(dims, nimg, cap_len, num_steps, n_cap):
+    """Algorithmic FLOPs of one sampler pass (every branch, every step)."""
+    d, H, F = dims.dim, dims.ffn_hidden, 4 * dims.latent_ch
+    per_step = 0
+    for L in cap_len:
+        nc = n_cap(L)
+        S = nimg + nc
+        f = 2 * nimg * F * d + 2 * L * dims.cap_dim * d + 2 * nimg * d * F
+        f += dims.n_noise_ref * block_flops(nimg, d, H)
+        f += dims.n_ctx_ref * block_flops(nc, d, H)
+        f += dims.n_main * block_flops(S, d, H)
+        per_step += f
+    return per_step * num_steps
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def random_model_on_device(dims, seed):
+    """Seeded N(0, 0.02) bf16 weights generated on the device (norm gains 1 + 0.02 N(0,1))."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    d, H, cd, F = dims.dim, dims.ffn_hidden, dims.c_dim, 4 * dims.latent_ch
+
+    def mat(r, c):
+        return (torch.randn((r, c), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+
+    def vec(n, std=0.02, base=0.0):
+        return torch.randn(n, generator=g, device="cuda") * std + base
+
+    def block(adaln):
+        t = {"w_qkv": mat(3 * d, d), "w_out": mat(d, d), "w1": mat(H, d), "w3": mat(H, d), "w2": mat(d, H),
+             "norm1": vec(d, base=1.0), "norm2": vec(d, base=1.0)}
+        if adaln:
+            t["w_ada"], t["b_ada"] = mat(6 * d, cd), vec(6 * d)
+        return Z.DeviceBlock(t)
+
+    t = {"x_emb_w": mat(d, F), "x_emb_b": vec(d), "cap_emb_w": mat(d, dims.cap_dim), "cap_emb_b": vec(d),
+         "cap_pad": vec(d, 1.0), "t_w1": vec(cd * cd).reshape(cd, cd), "t_b1": vec(cd),
+         "t_w2": vec(cd * cd).reshape(cd, cd), "t_b2": vec(cd), "final_norm": vec(d, base=1.0),
+         "final_ada_w": mat(2 * d, cd), "final_ada_b": vec(2 * d), "final_w": mat(F, d), "final_b": vec(F)}
+    nr = [block(True) for _ in range(dims.n_noise_ref)]
+    cr = [block(False) for _ in range(dims.n_ctx_ref)]
+    mb = [block(True) for _ in range(dims.n_main)]
+    return Z.DeviceModel(t, nr, cr, mb)
+
+
+def time_op(fn, reps, stream):
+    """Average duration (ms) of fn() over reps launches, HIP events on `stream`."""
+    import torch
+    fn()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def measure_block(dims, B, S, seed, stream):
+    """One main block at the 1024^2 pair shape through zdit_block_fwd."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    d, H = dims.dim, dims.ffn_hidden
+    mat = lambda r, c: (torch.randn((r, c), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    blk = Z.DeviceBlock({"w_qkv": mat(3 * d, d), "w_out": mat(d, d), "w1": mat(H, d), "w3": mat(H, d),
+                         "w2": mat(d, H), "norm1": torch.ones(d, device="cuda"), "norm2": torch.ones(d, device="cuda"),
+                         "w_ada": mat(6 * d, dims.c_dim), "b_ada": torch.zeros(6 * d, device="cuda")})
+    s_max = max(S)
+    x = torch.randn((B, s_max, d), generator=g, device="cuda")
+    c = torch.randn((B, dims.c_dim), generator=g, device="cuda")
+    cos = torch.ones((B, s_max, 64), device="cuda")
+    sin = torch.zeros((B, s_max, 64), device="cuda")
+    dd = Z.make_dims(dims)
+    ws = Z.workspace(Z.zdit_block_workspace(dd, B, s_max))
+    ms = time_op(lambda: Z.zdit_block_fwd(dd, blk, B, s_max, S, x, c, cos, sin, ws, stream), 10, stream)
+    fl = sum(block_flops(s, d, H) for s in S)
+    return ms, fl
+
+
+def measure_dominant_gemm(dims, M, stream):
+    """The SwiGLU w1/w3 GEMM of a main block at the 1024^2 pair shape (M = 2 x 4160)."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    d, H = dims.dim, dims.ffn_hidden
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    A = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
+    W1 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    W3 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    U = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ms = time_op(lambda: Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M, H, d, A, W1, W3, None, U, stream), 20, stream)
+    return ms, 2.0 * M * d * 2 * H
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "diffusion_transformer_text_s3_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or _src_hash(src) != rec["source_sha"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(dims):
+    """The oracle (as it stands) on a bounded sample: one main block on the 1024^2 cond/uncond
+    pair (S = 4160 and 4128), timed on this host's cores."""
+    import numpy as np
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    wl = synth.CFG3
+    w = synth.block_weights(dims, 1, 0)
+    ew = synth.embed_weights(dims, 1)
+    gh = wl.lat_h // 2
+    flops = 0.0
+    t0 = time.perf_counter()
+    for b, L in enumerate(wl.cap_len):
+        nc = O.n_cap(L)
+        S = gh * gh + nc
+        x = synth.residual_input((S, dims.dim), 1, index=b)
+        c = O.t_condition(np.array([0.5], np.float32), ew, dims)[0]
+        cos, sin = O.rope_tables(O.position_ids("joint", gh, gh, nc))
+        O.block(x, w, O.block_mod(c, w), cos, sin, dims)
+        flops += block_flops(S, dims.dim, dims.ffn_hidden)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one main block (fp32 NumPy oracle) on the 1024^2 cond/uncond pair, S = 4160 and 4128",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", choices=["1024", "1536"], default="1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=42)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    from diffusion_transformer_text_s3_amd import binding as Z
+
+    wl = synth.CFG5 if args.workload == "1024" else synth.CFG5_WIDE
+    dims = wl.dims
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    cfg = Z.make_cfg(dims)
+    model = random_model_on_device(dims, args.seed)
+    lat_h, lat_w = wl.lat_h, wl.lat_w
+    cap_len = list(wl.cap_len)
+    Lmax = max(cap_len)
+    x0 = torch.from_numpy(synth.latents((dims.latent_ch, lat_h, lat_w), wl.seed)).cuda()
+    cap = torch.from_numpy(synth.caption_features(2, Lmax, dims.cap_dim, wl.seed)).cuda()
+    x = x0.clone()
+    dec = torch.empty_like(x0)
+    ws = Z.workspace(Z.zdit_sample_workspace(cfg, lat_h, lat_w, Lmax, wl.guidance))
+
+    def step():
+        x.copy_(x0)
+        Z.zdit_sample(cfg, model, lat_h, lat_w, x, cap, Lmax, cap_len, wl.guidance, wl.num_steps, wl.shift, dec, ws,
+                      stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    out = x.float().cpu().numpy()
+    finite = bool(np.isfinite(out).all())
+
+    n_cap = lambda L: -(-L // dims.seq_multiple) * dims.seq_multiple
+    nimg = (lat_h // 2) * (lat_w // 2)
+    flops = pass_flops(dims, nimg, cap_len, wl.num_steps, n_cap)
+    tflops = flops / dt / 1e12
+
+    # one main block at the 1024^2 pair shape
+    S_pair = [64 * 64 + n_cap(L) for L in (45, 10)]
+    blk_ms, blk_fl = measure_block(dims, 2, S_pair, args.seed + 1, stream)
+    # dominant kernel: the SwiGLU w1/w3 GEMM at the main-block pair shape
+    M = 2 * max(S_pair)
+    g_ms, g_fl = measure_dominant_gemm(dims, M, stream)
+    achieved = g_fl / (g_ms * 1e-3) / 1e12
+    roof = {"kernel": "gemm_bf16_kernel<EPI_SWIGLU> (w1/w3 + SwiGLU), M=8320 N=10240 K=3840",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(g_ms, 4),
+            "traffic": traffic_from_profiles("gemm_swiglu")}
+
+    rec = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) latents and caption features, "
+        "random-init N(0,0.02) bf16 weights)",
+        "config": {"workload": wl.name, "lat": [lat_h, lat_w], "cap_len": cap_len, "guidance": wl.guidance,
+                   "num_steps": wl.num_steps, "blocks": [dims.n_noise_ref, dims.n_ctx_ref, dims.n_main],
+                   "dim": dims.dim, "heads": dims.n_heads, "ffn_hidden": dims.ffn_hidden,
+                   "algorithmic_tflop_per_step": round(flops / 1e12, 2)},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "block_fwd": {"shape": "main block, 1024^2 cond/uncond pair, S = 4160 / 4128", "ms": round(blk_ms, 3),
+                      "tflops": round(blk_fl / (blk_ms * 1e-3) / 1e12, 2),
+                      "pct_bf16_peak": round(100 * blk_fl / (blk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roof,
+        "output_finite": finite,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(dims)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,3 +53,20 @@ def ulp_diff_bf16(a, b):
         mag = u & 0x7FFF
         return np.where(u >> 15, -mag, mag)
     return np.abs(line(a) - line(b))
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 values at |v| (normal range)."""
+    v = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(v)) - 7)
+
+
+def assert_bf16_result(got, ref64, acc_err):
+    """got = bf16(fp32 value within acc_err of ref64): |got - ref64| <= half a bf16 ulp of the
+    fp32 value plus acc_err."""
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    acc_err = np.asarray(acc_err, dtype=np.float64)
+    allow = 0.5 * bf16_ulp(np.abs(ref64) + acc_err) + acc_err
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref64)
+    bad = err > allow * (1 + 1e-9)
+    assert not bad.any(), f"{bad.sum()} elements outside bound; worst excess {(err - allow).max():.3e}"

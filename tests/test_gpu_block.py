@@ -111,19 +111,26 @@ def _tiny_pair(s_extra=0):
 
 
 def test_block_padding_rows_invisible_and_untouched():
+    """The same valid rows with 32 or 96 extra padding rows per branch, the padding full of
+    NaN: valid outputs are bit-identical and the padding rows stay as they were."""
     note("block padding invariance")
     base = _tiny_pair()
     blk = Z.upload_block(base["w"])
     ref = run_gpu(base, blk=blk)
+    B, s0, d = base["x"].shape
     for extra in (32, 96):
-        case = _tiny_pair(extra)
-        x = case["x"].copy()
-        for b in range(2):
-            x[b, case["S"][b]:] = np.nan
-        case["x"] = x
+        s1 = s0 + extra
+        x = np.full((B, s1, d), np.nan, np.float32)
+        cos = np.ones((B, s1, 64), np.float32)
+        sin = np.zeros((B, s1, 64), np.float32)
+        for b in range(B):
+            n = base["S"][b]
+            x[b, :n] = base["x"][b, :n]
+            cos[b, :n], sin[b, :n] = base["cos"][b, :n], base["sin"][b, :n]
+        case = dict(base, s_max=s1, x=x, cos=cos, sin=sin)
         got = run_gpu(case, blk=blk)
-        for b in range(2):
-            n = case["S"][b]
+        for b in range(B):
+            n = base["S"][b]
             np.testing.assert_array_equal(got[b, :n], ref[b, :n])
             assert np.all(np.isnan(got[b, n:]))
 
