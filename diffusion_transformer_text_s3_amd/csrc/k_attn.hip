@@ -18,7 +18,6 @@ namespace zdit {
 
 namespace {
 
-constexpr int QT = 128;  // queries per workgroup
 constexpr int KT = 64;   // keys per LDS block
 constexpr int KROW = 17; // 16-byte chunks per K row in LDS (16 + 1 pad)
 constexpr int VROW = 9;  // 16-byte chunks per V^T row in LDS (8 + 1 pad)
@@ -52,10 +51,18 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ uint4 Ks[KT * KROW];
-  __shared__ uint4 Vs[kHeadDim * VROW];
-  const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * QT;
+// 8 wavefronts x 32 queries = 256 queries per workgroup (two wavefronts per SIMD, so one's
+// softmax overlaps the other's MFMAs).  K and V^T key blocks are double-buffered in LDS and
+// prefetched through registers one block ahead.  Per key block t: softmax of the scores of
+// block t, O^T += V^T P^T, then the QK^T MFMAs of block t+1 (built with ZDIT_ATTN_PIPELINE
+// the QK^T of block t+1 is issued before the softmax instead; measured slower on gfx950).
+constexpr int NWAVE = 8;
+constexpr int QTILE = 32 * NWAVE;
+
+__global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ uint4 Ks[2][KT * KROW];
+  __shared__ uint4 Vs[2][kHeadDim * VROW];
+  const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * QTILE;
   const int D = a.n_heads * kHeadDim;
   const int S = a.seq_len[b];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,8 +71,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const bf16* qkv = (const bf16*)a.qkv;
   bf16* out = (bf16*)a.out;
 
-  if (q0 >= S) {  // whole tile is padding: write zeros
-    for (int i = tid; i < QT * 16; i += 256) {
+  if (q0 >= S) {  // the whole tile is padding: write zeros
+    for (int i = tid; i < QTILE * 16; i += 512) {
       const int r = q0 + (i >> 4), c = i & 15;
       if (r < a.s_max) *(uint4*)(out + ((int64_t)b * a.s_max + r) * D + h * kHeadDim + c * 8) = make_uint4(0, 0, 0, 0);
     }
@@ -79,6 +86,52 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
   }
 
+  const bf16* kbase = qkv + (int64_t)b * a.s_max * 3 * D + D + h * kHeadDim;
+  const bf16* vbase = (const bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
+  // prefetch assignment: K chunk c = tid + 512 i -> key c / 16, 16-byte chunk c % 16;
+  // V^T chunk c -> dim c / 8, chunk c % 8
+  uint4 rk[2], rv[2];
+  auto gload_k = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i, key = t * KT + (c >> 4);
+      rk[i] = key < S ? *(const uint4*)(kbase + (int64_t)key * 3 * D + (c & 15) * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto gload_v = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i;
+      rv[i] = *(const uint4*)(vbase + (int64_t)(c >> 3) * a.s_pad + t * KT + (c & 7) * 8);
+    }
+  };
+  auto sstore_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i;
+      Ks[buf][(c >> 4) * KROW + (c & 15)] = rk[i];
+    }
+  };
+  auto sstore_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i;
+      Vs[buf][(c >> 3) * VROW + (c & 7)] = rv[i];
+    }
+  };
+  auto qk = [&](int buf, f32x16 (&st)[2]) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[t2][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, Ks[buf][(t2 * 32 + fr) * KROW + 2 * s + fh]);
+        st[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t2], 0, 0, 0);
+      }
+    }
+  };
+
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -87,82 +140,85 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const int nkt = (S + KT - 1) / KT;
-  const bf16* vt = (const bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
-  const bf16* Vb = (const bf16*)Vs;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c >> 4, dc = c & 15;
-      const int kk = k0 + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kk < S) v = *(const uint4*)(qkv + ((int64_t)b * a.s_max + kk) * 3 * D + D + h * kHeadDim + dc * 8);
-      Ks[key * KROW + dc] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int d = c >> 3, kc = c & 7;
-      Vs[d * VROW + kc] = *(const uint4*)(vt + (int64_t)d * a.s_pad + k0 + kc * 8);
-    }
-    __syncthreads();
+  // One key block: softmax of block t (held in `cur`), O^T += V^T P^T, QK^T of block t+1
+  // into `nxt`.  Two copies alternate the roles of the score registers, so no copy is
+  // needed between iterations.
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const bool more = t + 1 < nkt;
+    if (more) gload_v(t + 1);
+#ifdef ZDIT_ATTN_PIPELINE
+    if (more) qk((t + 1) & 1, nxt);
+#endif
 
-    f32x16 st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[t][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, Ks[(t * 32 + fr) * KROW + 2 * s + fh]);
-        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t], 0, 0, 0);
-      }
-    }
     float mx = -INFINITY;
+    if (t == nkt - 1) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + t * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-        const float v = (key < S) ? st[t][r] * sc : -INFINITY;
-        st[t][r] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * KT + t2 * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+          if (key >= S) cur[t2][r] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[t2][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const float m_new = fmaxf(m_run, mx * sc);
+    if (__any(m_new > m_run)) {  // rescale only when some running max moved (else the factor is 1)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      m_run = m_new;
+    }
     bf16x8 pb[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(st[t][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[t2][r], sc, -m_run));
         l_run += p;
-        pb[t][r >> 3][r & 7] = (bf16)p;
+        pb[t2][r >> 3][r & 7] = (bf16)p;
       }
+    // the K prefetch is issued once this block's scores are dead (keeps the register peak low)
+    if (t + 2 < nkt) gload_k(t + 2);
+    const bf16* Vb = (const bf16*)Vs[t & 1];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const bf16* vrow = Vb + (dt * 32 + fr) * (VROW * 8);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int base = t * 32 + 16 * j + 4 * fh;
+          const int base = t2 * 32 + 16 * j + 4 * fh;
           const bf16x4 lo = *(const bf16x4*)(vrow + base);
           const bf16x4 hi = *(const bf16x4*)(vrow + base + 8);
           const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][j], o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t2][j], o[dt], 0, 0, 0);
         }
     }
+#ifndef ZDIT_ATTN_PIPELINE
+    if (more) qk((t + 1) & 1, nxt);
+#endif
+    if (t + 2 < nkt) sstore_k(t & 1);
+    if (more) sstore_v((t + 1) & 1);
     __syncthreads();
+  };
+
+  gload_k(0); sstore_k(0);
+  gload_v(0); sstore_v(0);
+  if (nkt > 1) { gload_k(1); sstore_k(1); }
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  qk(0, sA);
+  for (int t = 0; t < nkt; t += 2) {
+    step(t, sA, sB);
+    if (t + 1 < nkt) step(t + 1, sB, sA);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
@@ -223,8 +279,8 @@ size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads) {
 hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s) {
   if (precision == 0) {
     hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_heads, a.batch), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((a.s_max + QT - 1) / QT, a.n_heads, a.batch),
-                       dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((a.s_max + QTILE - 1) / QTILE, a.n_heads, a.batch),
+                       dim3(512), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.s_max, a.n_heads, a.batch), dim3(64), 0, s, a);
   }

@@ -27,10 +27,15 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int NT = 256;  // threads
 // buffer resource word 3 for raw (untyped, offset-addressed) buffer loads
 constexpr int kBufFlags = 0x00020000;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+// Chunk kc of row r sits at slot kc ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1): any 8 aligned
+// consecutive rows, and the rows of either parity among 16 consecutive rows, see distinct
+// slots, so 16-byte fragment reads of 16 consecutive rows touch distinct banks.
+__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7) ^ ((row >> 3) & 1)); }
 
 // Physical workgroup id -> (tile row, tile col).
 __device__ __forceinline__ void tile_coords(int pid, int nwg, int tiles_m, int tiles_n, int& tm,
@@ -62,11 +67,54 @@ __device__ __forceinline__ RowAddr map_row(const RowMap& rm, int m) {
   return ra;
 }
 
+// LDS stage: A tile [256 rows][8 x 16-byte chunks] then B tile, 64 KB.  Chunk kc of row r
+// sits at slot kc ^ (r & 7).
+__device__ __forceinline__ void lds_dma_16(const __amdgpu_buffer_rsrc_t rs, const uint4* lds_base,
+                                           int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff,
+                                           soff, 0, 0);
+}
+
+// Fragments of k16 step s (0..3) of a stage for this wave's 4 A and 4 B MFMA tiles.
+__device__ __forceinline__ void load_frags(const uint4* sa, const uint4* sb, int arow, int brow, int kc,
+                                           bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    af[i] = __builtin_bit_cast(bf16x8, sa[swz(arow + i * 32, kc)]);
+    bf[i] = __builtin_bit_cast(bf16x8, sb[swz(brow + i * 32, kc)]);
+  }
+}
+
+__device__ __forceinline__ void mma16(const bf16x8 (&af)[4], const bf16x8 (&bf)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+}
+
+// scheduling hint for a run of 16 MFMAs with 8 LDS reads interleaved (2 MFMA : 1 read)
+__device__ __forceinline__ void sched_mma_ds() {
+#ifndef ZDIT_GEMM_NO_SCHED
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#endif
+}
+
 template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ uint4 smem[2][2][BM * BK / 8];
+  // two stages as separate objects, so reads of one stage are not ordered behind the
+  // in-flight direct-to-LDS loads of the other
+  __shared__ uint4 st0[2][BM * BK / 8];
+  __shared__ uint4 st1[2][BM * BK / 8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform: keep it in a scalar register (LDS bases and buffer offsets
+  // derived from it must be scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int nout_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -76,9 +124,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int m0 = tm * BM, n0 = tn * nout_tile;
 
   // Operands are read through buffer resources based at the tile's first row: rows past M
-  // (or N) fall outside the resource and load as zero.  Thread t covers rows (t / 8) + 32 i,
-  // i = 0..7, 16-byte chunk t % 8 of each 64-wide K slab.
-  const int lrow = tid >> 3, lkc = tid & 7;
+  // (or N) fall outside the resource and load as zero.
   const bf16* A0 = (const bf16*)g.A + (int64_t)m0 * g.lda;
   const __amdgpu_buffer_rsrc_t ra_rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, (int)min((int64_t)(g.M - m0) * g.lda * 2, (int64_t)0x7fffffff), kBufFlags);
@@ -88,13 +134,34 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   __amdgpu_buffer_rsrc_t rb2_rs = rb_rs;
   if constexpr (EPI == EPI_SWIGLU)
     rb2_rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)g.B2 + (int64_t)n0 * g.ldb), 0, brec, kBufFlags);
-  const int va = (lrow * (int)g.lda + lkc * 8) * 2;
-  const int vb = (lrow * (int)g.ldb + lkc * 8) * 2;
-  // uniform row offsets (bytes) of the 8 rows a thread loads
-  auto a_soff = [&](int i) { return 32 * i * (int)g.lda * 2; };
-  auto b_soff = [&](int i) {
-    if constexpr (EPI == EPI_SWIGLU) return ((i >> 2) * 64 + ((i & 3) >> 1) * 32) * (int)g.ldb * 2;
-    else return 32 * i * (int)g.ldb * 2;
+
+  // Direct-to-LDS: one wave instruction writes 1 KB = 8 rows (blk * 8 ..) of the tile, lane L
+  // landing at slot L % 8 of row L / 8; it therefore fetches chunk (L % 8) ^ g(row), where
+  // g(row) = (L / 8) ^ (blk & 1).  Two lane offsets, for even and odd blk.
+  const int lr = lane >> 3;
+  const int lkc0 = (lane & 7) ^ lr, lkc1 = lkc0 ^ 1;
+  const int va0 = (lr * (int)g.lda + lkc0 * 8) * 2, va1 = (lr * (int)g.lda + lkc1 * 8) * 2;
+  const int vb0 = (lr * (int)g.ldb + lkc0 * 8) * 2, vb1 = (lr * (int)g.ldb + lkc1 * 8) * 2;
+
+  auto issue = [&](int kt, uint4 (&stage)[2][BM * BK / 8]) {
+    const int kb = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int blk = wave * 8 + i;          // rows blk*8 .. blk*8+7 of the tile
+      lds_dma_16(ra_rs, &stage[0][blk * 64], (i & 1) ? va1 : va0, blk * 8 * (int)g.lda * 2 + kb);
+      int brow;
+      __amdgpu_buffer_rsrc_t rsb = rb_rs;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // tile row t = blk*8 + r: wave column t / 128, MFMA tile (t % 128) / 32 (even: W1,
+        // odd: W3), output column (t / 128) * 64 + (tile / 2) * 32 + t % 32
+        const int t = blk * 8, wc = t >> 7, mt = (t & 127) >> 5;
+        brow = wc * 64 + (mt >> 1) * 32 + (t & 31);
+        if (mt & 1) rsb = rb2_rs;
+      } else {
+        brow = blk * 8;
+      }
+      lds_dma_16(rsb, &stage[1][blk * 64], (i & 1) ? vb1 : vb0, brow * (int)g.ldb * 2 + kb);
+    }
   };
 
   f32x16 acc[4][4];
@@ -105,97 +172,106 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[8], rb[8];
   const int nk = g.K / BK;
-
-  auto load_slab = [&](int kt) {
-    const int kb = kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_rs, va, a_soff(i) + kb, 0));
-      const __amdgpu_buffer_rsrc_t rsb = (EPI == EPI_SWIGLU && (i & 1)) ? rb2_rs : rb_rs;
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, vb, b_soff(i) + kb, 0));
-    }
-  };
-
-  load_slab(0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    smem[0][0][swz(lrow + 32 * i, lkc)] = ra[i];
-    smem[0][1][swz(lrow + 32 * i, lkc)] = rb[i];
-  }
-  __syncthreads();
-
   const int fr = lane & 31, fh = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_slab(kt + 1);
-    const uint4* sa = smem[cur][0];
-    const uint4* sb = smem[cur][1];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kc = 2 * s + fh;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int row = wm * 128 + mt * 32 + fr;
-        af[mt] = __builtin_bit_cast(bf16x8, sa[swz(row, kc)]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int row = wn * 128 + nt * 32 + fr;
-        bfr[nt] = __builtin_bit_cast(bf16x8, sb[swz(row, kc)]);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        smem[cur ^ 1][0][swz(lrow + 32 * i, lkc)] = ra[i];
-        smem[cur ^ 1][1][swz(lrow + 32 * i, lkc)] = rb[i];
-      }
-    }
-    __syncthreads();
+
+  const uint4* s0a = st0[0];
+  const uint4* s0b = st0[1];
+  const uint4* s1a = st1[0];
+  const uint4* s1b = st1[1];
+  const int arow = wm * 128 + fr, brow = wn * 128 + fr;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+
+  // One 64-wide K slab from stage `cur` (its step-0 fragments already in fa0/fb0).  The
+  // barrier comes once the slab's last fragments are in registers: after it, the DMA of the
+  // slab two ahead goes into `cur`, and the next slab's step-0 fragments are read from `nxt`
+  // while the last 16 MFMAs of this slab run.
+#define ZDIT_SLAB(CA, CB, NA, NB, CUR_ST, HAS_NEXT, NEXT2)                                    \
+  {                                                                                           \
+    load_frags(CA, CB, arow, brow, 2 + fh, fa1, fb1);                                         \
+    mma16(fa0, fb0, acc);                                                                     \
+    sched_mma_ds();                                                                          \
+    load_frags(CA, CB, arow, brow, 4 + fh, fa0, fb0);                                         \
+    mma16(fa1, fb1, acc);                                                                     \
+    sched_mma_ds();                                                                          \
+    load_frags(CA, CB, arow, brow, 6 + fh, fa1, fb1);                                         \
+    mma16(fa0, fb0, acc);                                                                     \
+    sched_mma_ds();                                                                          \
+    if (HAS_NEXT) {                                                                           \
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);                                                    \
+      __syncthreads();                                                                        \
+      if (NEXT2) issue(kt + 2, CUR_ST);                                                       \
+      load_frags(NA, NB, arow, brow, fh, fa0, fb0);                                           \
+    }                                                                                         \
+    mma16(fa1, fb1, acc);                                                                     \
   }
+
+  issue(0, st0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  if (nk > 1) issue(1, st1);
+  load_frags(s0a, s0b, arow, brow, fh, fa0, fb0);
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    ZDIT_SLAB(s0a, s0b, s1a, s1b, st0, true, kt + 2 < nk)
+    ++kt;
+    ZDIT_SLAB(s1a, s1b, s0a, s0b, st1, kt + 1 < nk, kt + 2 < nk)
+    --kt;
+  }
+  if (kt < nk) ZDIT_SLAB(s0a, s0b, s1a, s1b, st0, false, false)
+#undef ZDIT_SLAB
 
   // ---- epilogue.  Accumulator (mt, nt) element r of this lane is C[row][col] with
   // row = 8 (r / 4) + 4 (lane / 32) + r % 4 and col = lane % 32 within the 32 x 32 tile.
+  // Row addressing is resolved once per row; loads of a tile's 16 values are issued together
+  // before any store, so their latencies overlap.
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
+    int64_t roff[16];
+    bool rok[16];
+    int rb[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = m0 + wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      if (m >= g.M) continue;
-      const RowAddr ro = map_row(g.out, m);
-      if (!ro.ok) continue;
-      if constexpr (EPI == EPI_SWIGLU) {
+      const int mm = min(m, g.M - 1);
+      const RowAddr ro = map_row(g.out, mm);
+      roff[r] = ro.off;
+      rok[r] = (m < g.M) && ro.ok;
+      rb[r] = mm / g.out.rows_per_batch;
+    }
+    if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-        for (int np = 0; np < 2; ++np) {
-          const int n = n0 + wn * 64 + np * 32 + fr;
-          if (n < g.N) {
-            const float u = silu(acc[mt][2 * np][r]) * acc[mt][2 * np + 1][r];
-            ((bf16*)g.C)[ro.off + n] = (bf16)u;
-          }
-        }
-      } else {
+      for (int np = 0; np < 2; ++np) {
+        const int n = n0 + wn * 64 + np * 32 + fr;
+        if (n >= g.N) continue;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int n = n0 + wn * 128 + nt * 32 + fr;
-          if (n >= g.N) continue;
-          const float v = acc[mt][nt][r];
-          if constexpr (EPI == EPI_STORE) {
-            ((bf16*)g.C)[ro.off + n] = (bf16)v;
-          } else if constexpr (EPI == EPI_BIAS) {
-            ((float*)g.C)[ro.off + n] = v + g.vec[n];
-          } else {  // EPI_RESID
-            const int b = m / g.out.rows_per_batch;
-            const float gate = g.vec ? g.vec[b * g.vec_bstride + n] : 1.0f;
-            float* p = (float*)g.C + ro.off + n;
-            *p = *p + gate * v;
+        for (int r = 0; r < 16; ++r)
+          if (rok[r]) ((bf16*)g.C)[roff[r] + n] = (bf16)(silu(acc[mt][2 * np][r]) * acc[mt][2 * np + 1][r]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 128 + nt * 32 + fr;
+        if (n >= g.N) continue;
+        if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rok[r]) ((bf16*)g.C)[roff[r] + n] = (bf16)acc[mt][nt][r];
+        } else if constexpr (EPI == EPI_BIAS) {
+          const float bias = g.vec[n];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rok[r]) ((float*)g.C)[roff[r] + n] = acc[mt][nt][r] + bias;
+        } else {  // EPI_RESID: x += gate * (A B^T)
+          float* C = (float*)g.C;
+          float cur[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cur[r] = rok[r] ? C[roff[r] + n] : 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (!rok[r]) continue;
+            const float gate = g.vec ? g.vec[rb[r] * g.vec_bstride + n] : 1.0f;
+            C[roff[r] + n] = cur[r] + gate * acc[mt][nt][r];
           }
         }
       }
