@@ -181,6 +181,31 @@ def cpu_baseline(dims):
             "seconds": round(dt, 2)}
 
 
+def kernel_only(which):
+    """Three launches of the SwiGLU GEMM at the main-block 1024^2 pair shape, or three plain
+    device copies of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written)."""
+    import torch
+    import synth
+    from diffusion_transformer_text_s3_amd import binding as Z
+    d, H, M = synth.FULL.dim, synth.FULL.ffn_hidden, 8320
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    if which == "copy":
+        src = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+    else:
+        A = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
+        W1 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        W3 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        U = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M, H, d, A, W1, W3, None, U)
+    torch.cuda.synchronize()
+    print(f"kernel-only {which}: 3 launches done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +214,9 @@ def main():
     ap.add_argument("--workload", choices=["1024", "1536"], default="1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--kernel-only", choices=["swiglu", "copy"], default=None,
+                    help="launch only the dominant GEMM at its main-block shape (or a plain device copy of "
+                         "170,393,600 bytes, the counter calibration) three times, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not part "
@@ -199,6 +227,10 @@ def main():
     import torch
     import synth
     from diffusion_transformer_text_s3_amd import binding as Z
+
+    if args.kernel_only:
+        kernel_only(args.kernel_only)
+        return
 
     wl = synth.CFG5 if args.workload == "1024" else synth.CFG5_WIDE
     dims = wl.dims
