@@ -24,7 +24,6 @@ namespace zdit {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NT = 256;  // threads
 // buffer resource word 3 for raw (untyped, offset-addressed) buffer loads
 constexpr int kBufFlags = 0x00020000;
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
@@ -75,37 +74,54 @@ __device__ __forceinline__ void lds_dma_16(const __amdgpu_buffer_rsrc_t rs, cons
                                            soff, 0, 0);
 }
 
-// Fragments of k16 step s (0..3) of a stage for this wave's 4 A and 4 B MFMA tiles.
+// Fragments of one k16 step (16-byte chunk kc) of a stage for this wave's MT A tiles and 4 B
+// tiles (each 32 rows).
+template <int MT>
 __device__ __forceinline__ void load_frags(const uint4* sa, const uint4* sb, int arow, int brow, int kc,
-                                           bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+                                           bf16x8 (&af)[MT], bf16x8 (&bf)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    af[i] = __builtin_bit_cast(bf16x8, sa[swz(arow + i * 32, kc)]);
-    bf[i] = __builtin_bit_cast(bf16x8, sb[swz(brow + i * 32, kc)]);
-  }
+  for (int i = 0; i < MT; ++i) af[i] = __builtin_bit_cast(bf16x8, sa[swz(arow + i * 32, kc)]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bf[i] = __builtin_bit_cast(bf16x8, sb[swz(brow + i * 32, kc)]);
 }
 
-__device__ __forceinline__ void mma16(const bf16x8 (&af)[4], const bf16x8 (&bf)[4], f32x16 (&acc)[4][4]) {
+template <int MT>
+__device__ __forceinline__ void mma_step(const bf16x8 (&af)[MT], const bf16x8 (&bf)[4], f32x16 (&acc)[MT][4]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
 }
 
-// scheduling hint for a run of 16 MFMAs with 8 LDS reads interleaved (2 MFMA : 1 read)
+// scheduling hint for one step's 4*MT MFMAs with the next step's MT + 4 LDS reads interleaved
+template <int MT>
 __device__ __forceinline__ void sched_mma_ds() {
 #ifndef ZDIT_GEMM_NO_SCHED
+  if constexpr (MT == 4) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 #endif
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
+// WAVES = 4: each wavefront owns 128 x 128 of the tile (4 x 4 MFMA tiles, one wave per SIMD).
+// WAVES = 8: each owns 64 x 128 (2 x 4 MFMA tiles, two waves per SIMD, so one wave's LDS and
+// barrier waits are covered by the other's MFMAs).
+template <int EPI, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int MT = 16 / WAVES;          // 32-row MFMA tiles per wave along M
+  constexpr int BLK = 32 / WAVES;         // 8-row DMA blocks per wave per operand
   // two stages as separate objects, so reads of one stage are not ordered behind the
   // in-flight direct-to-LDS loads of the other
   __shared__ uint4 st0[2][BM * BK / 8];
@@ -115,7 +131,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   // the wave index is uniform: keep it in a scalar register (LDS bases and buffer offsets
   // derived from it must be scalar)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;  // wm: MT*32-row band, wn: 128-column half
   const int nout_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + nout_tile - 1) / nout_tile;
@@ -146,8 +162,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   auto issue = [&](int kt, uint4 (&stage)[2][BM * BK / 8]) {
     const int kb = kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk = wave * 8 + i;          // rows blk*8 .. blk*8+7 of the tile
+    for (int i = 0; i < BLK; ++i) {
+      const int blk = wave * BLK + i;        // rows blk*8 .. blk*8+7 of the tile
       lds_dma_16(ra_rs, &stage[0][blk * 64], (i & 1) ? va1 : va0, blk * 8 * (int)g.lda * 2 + kb);
       int brow;
       __amdgpu_buffer_rsrc_t rsb = rb_rs;
@@ -164,9 +180,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -179,8 +195,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   const uint4* s0b = st0[1];
   const uint4* s1a = st1[0];
   const uint4* s1b = st1[1];
-  const int arow = wm * 128 + fr, brow = wn * 128 + fr;
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  const int arow = wm * (32 * MT) + fr, brow = wn * 128 + fr;
+  bf16x8 fa0[MT], fb0[4], fa1[MT], fb1[4];
 
   // One 64-wide K slab from stage `cur` (its step-0 fragments already in fa0/fb0).  The
   // barrier comes once the slab's last fragments are in registers: after it, the DMA of the
@@ -188,29 +204,29 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   // while the last 16 MFMAs of this slab run.
 #define ZDIT_SLAB(CA, CB, NA, NB, CUR_ST, HAS_NEXT, NEXT2)                                    \
   {                                                                                           \
-    load_frags(CA, CB, arow, brow, 2 + fh, fa1, fb1);                                         \
-    mma16(fa0, fb0, acc);                                                                     \
-    sched_mma_ds();                                                                          \
-    load_frags(CA, CB, arow, brow, 4 + fh, fa0, fb0);                                         \
-    mma16(fa1, fb1, acc);                                                                     \
-    sched_mma_ds();                                                                          \
-    load_frags(CA, CB, arow, brow, 6 + fh, fa1, fb1);                                         \
-    mma16(fa0, fb0, acc);                                                                     \
-    sched_mma_ds();                                                                          \
+    load_frags<MT>(CA, CB, arow, brow, 2 + fh, fa1, fb1);                                     \
+    mma_step<MT>(fa0, fb0, acc);                                                              \
+    sched_mma_ds<MT>();                                                                       \
+    load_frags<MT>(CA, CB, arow, brow, 4 + fh, fa0, fb0);                                     \
+    mma_step<MT>(fa1, fb1, acc);                                                              \
+    sched_mma_ds<MT>();                                                                       \
+    load_frags<MT>(CA, CB, arow, brow, 6 + fh, fa1, fb1);                                     \
+    mma_step<MT>(fa0, fb0, acc);                                                              \
+    sched_mma_ds<MT>();                                                                       \
     if (HAS_NEXT) {                                                                           \
       __builtin_amdgcn_s_waitcnt(kVmcnt0);                                                    \
       __syncthreads();                                                                        \
       if (NEXT2) issue(kt + 2, CUR_ST);                                                       \
-      load_frags(NA, NB, arow, brow, fh, fa0, fb0);                                           \
+      load_frags<MT>(NA, NB, arow, brow, fh, fa0, fb0);                                       \
     }                                                                                         \
-    mma16(fa1, fb1, acc);                                                                     \
+    mma_step<MT>(fa1, fb1, acc);                                                              \
   }
 
   issue(0, st0);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   if (nk > 1) issue(1, st1);
-  load_frags(s0a, s0b, arow, brow, fh, fa0, fb0);
+  load_frags<MT>(s0a, s0b, arow, brow, fh, fa0, fb0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
     ZDIT_SLAB(s0a, s0b, s1a, s1b, st0, true, kt + 2 < nk)
@@ -226,13 +242,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmArgs g) {
   // Row addressing is resolved once per row; loads of a tile's 16 values are issued together
   // before any store, so their latencies overlap.
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     int64_t roff[16];
     bool rok[16];
     int rb[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + mt * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+      const int m = m0 + wm * (32 * MT) + mt * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
       const int mm = min(m, g.M - 1);
       const RowAddr ro = map_row(g.out, mm);
       roff[r] = ro.off;
@@ -352,12 +368,18 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   const int nout_tile = (epi == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + nout_tile - 1) / nout_tile);
-  dim3 grid(tiles), block(NT);
+  dim3 grid(tiles);
+#ifdef ZDIT_GEMM_4WAVE
+  constexpr int W = 4;
+#else
+  constexpr int W = 8;
+#endif
+  dim3 block(64 * W);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE>, grid, block, 0, s, g); break;
-    case EPI_BIAS: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_BIAS>, grid, block, 0, s, g); break;
-    case EPI_RESID: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_RESID>, grid, block, 0, s, g); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, s, g); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, W>), grid, block, 0, s, g); break;
+    case EPI_BIAS: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_BIAS, W>), grid, block, 0, s, g); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_RESID, W>), grid, block, 0, s, g); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, W>), grid, block, 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
