@@ -10,8 +10,11 @@
 // and the rescale of the output accumulator is a per-lane scalar.  The output is formed
 // transposed too, O^T += V^T P^T, where the bf16 P^T operand is taken straight from the
 // score registers: in a 32x32 MFMA result, lane half h holds keys {8g + 4h + 0..3}, so for
-// each group of 16 keys both operands use the key order {4h..4h+3, 8+4h..8+4h+3}.
+// each group of 16 keys both operands use the key order {4h..4h+3, 8+4h..8+4h+3}; V^T is
+// stored with each 16-key group in that order, so a lane reads its 8 keys in one 16-byte load.
 // Online softmax in fp32 with exp2 and the 1/sqrt(128) scale folded into log2(e).
+#include <type_traits>
+
 #include "common.h"
 
 namespace zdit {
@@ -40,13 +43,17 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
   __syncthreads();
   const bf16* tb = (const bf16*)t;
   bf16* vt = (bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
+  // Within every 16-key group the keys are stored in the order the 32x32 MFMA result hands
+  // them to a lane half: chunk 2g holds keys {0-3, 8-11} of group g, chunk 2g+1 holds keys
+  // {4-7, 12-15}, so the attention kernel reads a lane's 8 keys as one 16-byte chunk.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = threadIdx.x + 256 * i;
     const int d = c >> 3, sc = c & 7;
+    const int kbase = (sc >> 1) * 16 + (sc & 1) * 4;
     bf16x8 o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = tb[(sc * 8 + e) * (KROW * 8) + d];
+    for (int e = 0; e < 8; ++e) o[e] = tb[(kbase + (e & 3) + 8 * (e >> 2)) * (KROW * 8) + d];
     *(bf16x8*)(vt + (int64_t)d * a.s_pad + s0 + sc * 8) = o;
   }
 }
@@ -56,13 +63,32 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
 // prefetched through registers one block ahead.  Per key block t: softmax of the scores of
 // block t, O^T += V^T P^T, then the QK^T MFMAs of block t+1 (built with ZDIT_ATTN_PIPELINE
 // the QK^T of block t+1 is issued before the softmax instead; measured slower on gfx950).
-constexpr int NWAVE = 8;
+#ifndef ZDIT_ATTN_WAVES
+#define ZDIT_ATTN_WAVES 8
+#endif
+constexpr int NWAVE = ZDIT_ATTN_WAVES;
 constexpr int QTILE = 32 * NWAVE;
+constexpr int ATT_NT = 64 * NWAVE;           // threads per workgroup
+constexpr int KCH = KT * 16 / ATT_NT;        // 16-byte K chunks per thread per key block
+constexpr int VCH = kHeadDim * 8 / ATT_NT;   // 16-byte V^T chunks per thread per key block
 
-__global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
+// Workgroups are dispatched round-robin over the 8 XCDs.  The 1-D grid is renumbered so that
+// consecutive logical ids (the query tiles of one (branch, head), which share its K and V)
+// run on the same XCD and hit its L2.
+__device__ __forceinline__ int xcd_logical_id(int pid, int nwg) {
+  const int xcd = pid & 7, idx = pid >> 3;
+  const int full = nwg >> 3, rem = nwg & 7;
+  return (xcd < rem) ? xcd * (full + 1) + idx : rem * (full + 1) + (xcd - rem) * full + idx;
+}
+
+// two wavefronts per SIMD in either shape (8-wave workgroups: one per CU; 4-wave: two per CU)
+__global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a) {
   __shared__ uint4 Ks[2][KT * KROW];
   __shared__ uint4 Vs[2][kHeadDim * VROW];
-  const int b = blockIdx.z, h = blockIdx.y, q0 = blockIdx.x * QTILE;
+  const int nqt = (a.s_max + QTILE - 1) / QTILE;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int qt = lid % nqt, bh = lid / nqt;
+  const int h = bh % a.n_heads, b = bh / a.n_heads, q0 = qt * QTILE;
   const int D = a.n_heads * kHeadDim;
   const int S = a.seq_len[b];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -72,7 +98,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   bf16* out = (bf16*)a.out;
 
   if (q0 >= S) {  // the whole tile is padding: write zeros
-    for (int i = tid; i < QTILE * 16; i += 512) {
+    for (int i = tid; i < QTILE * 16; i += ATT_NT) {
       const int r = q0 + (i >> 4), c = i & 15;
       if (r < a.s_max) *(uint4*)(out + ((int64_t)b * a.s_max + r) * D + h * kHeadDim + c * 8) = make_uint4(0, 0, 0, 0);
     }
@@ -88,34 +114,34 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 
   const bf16* kbase = qkv + (int64_t)b * a.s_max * 3 * D + D + h * kHeadDim;
   const bf16* vbase = (const bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
-  // prefetch assignment: K chunk c = tid + 512 i -> key c / 16, 16-byte chunk c % 16;
+  // prefetch assignment: K chunk c = tid + ATT_NT i -> key c / 16, 16-byte chunk c % 16;
   // V^T chunk c -> dim c / 8, chunk c % 8
-  uint4 rk[2], rv[2];
+  uint4 rk[KCH], rv[VCH];
   auto gload_k = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 512 * i, key = t * KT + (c >> 4);
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + ATT_NT * i, key = t * KT + (c >> 4);
       rk[i] = key < S ? *(const uint4*)(kbase + (int64_t)key * 3 * D + (c & 15) * 8) : make_uint4(0, 0, 0, 0);
     }
   };
   auto gload_v = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 512 * i;
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + ATT_NT * i;
       rv[i] = *(const uint4*)(vbase + (int64_t)(c >> 3) * a.s_pad + t * KT + (c & 7) * 8);
     }
   };
   auto sstore_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 512 * i;
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + ATT_NT * i;
       Ks[buf][(c >> 4) * KROW + (c & 15)] = rk[i];
     }
   };
   auto sstore_v = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 512 * i;
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + ATT_NT * i;
       Vs[buf][(c >> 3) * VROW + (c & 7)] = rv[i];
     }
   };
@@ -143,8 +169,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 
   // One key block: softmax of block t (held in `cur`), O^T += V^T P^T, QK^T of block t+1
   // into `nxt`.  Two copies alternate the roles of the score registers, so no copy is
-  // needed between iterations.
-  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  // needed between iterations.  Only the final block can hold keys >= S (masked).
+  auto step = [&](auto masked, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const bool more = t + 1 < nkt;
     if (more) gload_v(t + 1);
 #ifdef ZDIT_ATTN_PIPELINE
@@ -152,7 +178,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
 #endif
 
     float mx = -INFINITY;
-    if (t == nkt - 1) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -167,7 +193,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[t2][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx * sc);
-    if (__any(m_new > m_run)) {  // rescale only when some running max moved (else the factor is 1)
+    // Lazy rescale: the reference max moves only when some lane's max rose by more than 8
+    // (log2 units), so p = exp2(s - m_run) stays below 2^8; O and l share the reference, so
+    // the result O / l is the same softmax.
+    if (__any(m_new > m_run + 8.0f)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -187,18 +216,15 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
       }
     // the K prefetch is issued once this block's scores are dead (keeps the register peak low)
     if (t + 2 < nkt) gload_k(t + 2);
-    const bf16* Vb = (const bf16*)Vs[t & 1];
+    const uint4* Vb = Vs[t & 1];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const bf16* vrow = Vb + (dt * 32 + fr) * (VROW * 8);
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int base = t2 * 32 + 16 * j + 4 * fh;
-          const bf16x4 lo = *(const bf16x4*)(vrow + base);
-          const bf16x4 hi = *(const bf16x4*)(vrow + base + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          // 16-byte chunk (t2 * 4 + j * 2 + fh) of the V^T row holds this lane half's 8 keys
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, Vb[(dt * 32 + fr) * VROW + t2 * 4 + j * 2 + fh]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t2][j], o[dt], 0, 0, 0);
         }
     }
@@ -216,9 +242,18 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   f32x16 sA[2], sB[2];
   qk(0, sA);
-  for (int t = 0; t < nkt; t += 2) {
-    step(t, sA, sB);
-    if (t + 1 < nkt) step(t + 1, sB, sA);
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  int t = 0;
+  for (; t + 2 < nkt; t += 2) {
+    step(Plain{}, t, sA, sB);
+    step(Plain{}, t + 1, sB, sA);
+  }
+  if (nkt - t == 2) {
+    step(Plain{}, t, sA, sB);
+    step(Masked{}, t + 1, sB, sA);
+  } else {
+    step(Masked{}, t, sA, sB);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
@@ -279,8 +314,8 @@ size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads) {
 hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s) {
   if (precision == 0) {
     hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_heads, a.batch), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((a.s_max + QTILE - 1) / QTILE, a.n_heads, a.batch),
-                       dim3(512), 0, s, a);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(((a.s_max + QTILE - 1) / QTILE) * a.n_heads * a.batch),
+                       dim3(ATT_NT), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(a.s_max, a.n_heads, a.batch), dim3(64), 0, s, a);
   }
