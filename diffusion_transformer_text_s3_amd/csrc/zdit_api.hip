@@ -274,10 +274,19 @@ zdit_status check_stack_args(const zdit_model_cfg* cfg, const zdit_model_w* w, i
   return ZDIT_OK;
 }
 
+// Caption cache: the caption rows after the context refiners depend only on the caption
+// features (no timestep, no latent), so a caller running several steps on the same captions
+// can pass cap_out on the first call ([B][max n_cap][dim] fp32, filled) and cap_in on the
+// later ones (copied in place of cap-embed, learned pad and context refiners).
+struct CapCache {
+  const float* in = nullptr;
+  float* out = nullptr;
+};
+
 zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int B, int lat_h, int lat_w,
                           const float* latents, int64_t lat_bstride, const float* cap_feats,
                           int max_cap_len, const int* cap_len, const float* t, float* velocity,
-                          char* ws, hipStream_t st) {
+                          char* ws, hipStream_t st, CapCache cache = CapCache{}) {
   const zdit_dims& d = cfg.d;
   const int P = d.precision, D = d.dim, F = cfg.patch * cfg.patch * cfg.latent_ch;
   const StackPlan p = plan_stack(cfg, B, lat_h, lat_w, max_cap_len, cap_len);
@@ -291,24 +300,20 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   // conditioning
   HIP_TRY(launch_temb(B, t, cfg.t_freq, d.c_dim, cfg.t_scale, w.t_w1, w.t_b1, w.t_w2, w.t_b2, c, st));
 
-  // image tokens -> rows [0, nimg) of every branch
-  HIP_TRY(launch_patchify(P, B, cfg.latent_ch, lat_h, lat_w, latents, lat_bstride, ws + p.tok, st));
+  // Image tokens -> rows [0, nimg) of every branch.  When every branch sees the same latent
+  // (branch stride 0) at the same model time, the image rows through the noise refiners are
+  // identical per branch (no kernel mixes branches, and each output's arithmetic does not
+  // depend on the batch), so they are computed for branch 0 and copied.
+  bool same_img = B > 1 && lat_bstride == 0;
+  for (int b = 1; b < B && same_img; ++b) same_img = (t[b] == t[0]);
+  const int Bi = same_img ? 1 : B;
+  HIP_TRY(launch_patchify(P, Bi, cfg.latent_ch, lat_h, lat_w, latents, lat_bstride, ws + p.tok, st));
   GemmArgs g{};
   g.A = ws + p.tok; g.B = w.x_emb_w; g.C = x; g.vec = w.x_emb_b;
-  g.M = B * p.nimg; g.N = D; g.K = F; g.lda = F; g.ldb = F;
+  g.M = Bi * p.nimg; g.N = D; g.K = F; g.lda = F; g.ldb = F;
   g.out.rows_per_batch = p.nimg; g.out.batch_stride = xb; g.out.ld = D;
   for (int b = 0; b < kMaxBatch; ++b) g.out.valid[b] = p.nimg;
   HIP_TRY(gemm(P, EPI_BIAS, g, st));
-
-  // caption tokens -> rows [nimg, nimg + L_b), learned pad up to n_cap_b
-  HIP_TRY(launch_convert(P, cap_feats, ws + p.capa, (int64_t)B * max_cap_len * cfg.cap_dim, st));
-  g = GemmArgs{};
-  g.A = ws + p.capa; g.B = w.cap_emb_w; g.C = x + (int64_t)p.nimg * D; g.vec = w.cap_emb_b;
-  g.M = B * max_cap_len; g.N = D; g.K = cfg.cap_dim; g.lda = cfg.cap_dim; g.ldb = cfg.cap_dim;
-  g.out.rows_per_batch = max_cap_len; g.out.batch_stride = xb; g.out.ld = D;
-  for (int b = 0; b < kMaxBatch; ++b) g.out.valid[b] = b < B ? cap_len[b] : 0;
-  HIP_TRY(gemm(P, EPI_BIAS, g, st));
-  HIP_TRY(launch_cap_pad(B, p.s_max, D, p.nimg, cap_len, cfg.seq_multiple, w.cap_pad, x, st));
 
   // RoPE tables, shared by every branch (positions of valid rows do not depend on the branch)
   RopeTabArgs rt;
@@ -326,19 +331,39 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   HIP_TRY(launch_rope_tables(rt, st));
 
   int len[kMaxBatch];
-  // noise refiners: image rows only
+  // noise refiners: image rows only (branch 0 only when the image rows are shared)
   for (int b = 0; b < B; ++b) len[b] = p.nimg;
   for (int i = 0; i < cfg.n_noise_ref; ++i) {
     const zdit_block_w& bw = w.noise_ref[i];
-    HIP_TRY(launch_adaln(P, B, d.c_dim, 6 * D, c, bw.w_ada, bw.b_ada, mod, st));
-    if (zdit_status s = block_forward(d, bw, B, p.nimg, len, x, xb, mod, ti_c, ti_s, 0, bws, st)) return s;
+    HIP_TRY(launch_adaln(P, Bi, d.c_dim, 6 * D, c, bw.w_ada, bw.b_ada, mod, st));
+    if (zdit_status s = block_forward(d, bw, Bi, p.nimg, len, x, xb, mod, ti_c, ti_s, 0, bws, st)) return s;
   }
-  // context refiners: caption rows only, no adaLN
-  for (int b = 0; b < B; ++b) len[b] = p.nc[b];
-  for (int i = 0; i < cfg.n_ctx_ref; ++i) {
-    if (zdit_status s = block_forward(d, w.ctx_ref[i], B, p.max_nc, len, x + (int64_t)p.nimg * D, xb,
-                                      nullptr, tc_c, tc_s, 0, bws, st)) return s;
+  if (same_img)
+    HIP_TRY(launch_copy_rows(x, 0, x + xb, xb, B - 1, (int64_t)p.nimg * D, st));
+
+  // caption tokens -> rows [nimg, nimg + n_cap_b): cap-embed, learned pad, context refiners
+  float* xcap = x + (int64_t)p.nimg * D;
+  const int64_t cache_bstride = (int64_t)p.max_nc * D;
+  if (cache.in) {
+    HIP_TRY(launch_copy_rows(cache.in, cache_bstride, xcap, xb, B, cache_bstride, st));
+  } else {
+    HIP_TRY(launch_convert(P, cap_feats, ws + p.capa, (int64_t)B * max_cap_len * cfg.cap_dim, st));
+    g = GemmArgs{};
+    g.A = ws + p.capa; g.B = w.cap_emb_w; g.C = xcap; g.vec = w.cap_emb_b;
+    g.M = B * max_cap_len; g.N = D; g.K = cfg.cap_dim; g.lda = cfg.cap_dim; g.ldb = cfg.cap_dim;
+    g.out.rows_per_batch = max_cap_len; g.out.batch_stride = xb; g.out.ld = D;
+    for (int b = 0; b < kMaxBatch; ++b) g.out.valid[b] = b < B ? cap_len[b] : 0;
+    HIP_TRY(gemm(P, EPI_BIAS, g, st));
+    HIP_TRY(launch_cap_pad(B, p.s_max, D, p.nimg, cap_len, cfg.seq_multiple, w.cap_pad, x, st));
+    // context refiners: caption rows only, no adaLN
+    for (int b = 0; b < B; ++b) len[b] = p.nc[b];
+    for (int i = 0; i < cfg.n_ctx_ref; ++i) {
+      if (zdit_status s = block_forward(d, w.ctx_ref[i], B, p.max_nc, len, xcap, xb, nullptr, tc_c, tc_s, 0, bws, st))
+        return s;
+    }
+    if (cache.out) HIP_TRY(launch_copy_rows(xcap, xb, cache.out, cache_bstride, B, cache_bstride, st));
   }
+
   // main blocks on the joint sequence
   for (int b = 0; b < B; ++b) len[b] = p.S[b];
   for (int i = 0; i < cfg.n_main; ++i) {
@@ -458,12 +483,20 @@ zdit_status zdit_euler_step(float* x, const float* v_cond, const float* v_uncond
   return ok();
 }
 
+// Caption rows after the context refiners, kept across sampler steps: [nb][n_cap max][dim]
+// fp32 (n_cap of any valid length is at most max_cap_len rounded up to the multiple).
+static size_t sample_cap_cache_bytes(const zdit_model_cfg* cfg, int nb, int max_cap_len) {
+  const int m = cfg->seq_multiple;
+  const size_t nc = (size_t)((max_cap_len + m - 1) / m) * m;
+  return al256((size_t)nb * nc * cfg->d.dim * 4);
+}
+
 size_t zdit_sample_workspace(const zdit_model_cfg* cfg, int32_t lat_h, int32_t lat_w, int32_t max_cap_len,
                              float guidance) {
   const int nb = guidance != 0.f ? 2 : 1;
   const size_t st = zdit_stack_workspace(cfg, nb, lat_h, lat_w, max_cap_len);
   if (!st) return 0;
-  return st + al256((size_t)nb * cfg->latent_ch * lat_h * lat_w * 4);
+  return st + al256((size_t)nb * cfg->latent_ch * lat_h * lat_w * 4) + sample_cap_cache_bytes(cfg, nb, max_cap_len);
 }
 
 zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_t lat_h, int32_t lat_w, float* x,
@@ -483,14 +516,18 @@ zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_
   hipStream_t st = (hipStream_t)hip_stream;
   const int64_t n = (int64_t)cfg->latent_ch * lat_h * lat_w;
   float* vel = (float*)ws;
-  char* sws = (char*)ws + al256((size_t)nb * n * 4);
+  float* cap_cache = (float*)((char*)ws + al256((size_t)nb * n * 4));
+  char* sws = (char*)cap_cache + sample_cap_cache_bytes(cfg, nb, max_cap_len);
   std::vector<float> sg(num_steps + 1);
   for (int i = 0; i <= num_steps; ++i) sg[i] = (float)sigma_at(i, num_steps, (double)shift);
   for (int i = 0; i < num_steps; ++i) {
     const float ti = 1.0f - sg[i];
     const float tv[2] = {ti, ti};
+    // the caption rows do not depend on the step: context refiners run in step 0 only
+    CapCache cc;
+    if (i == 0) cc.out = cap_cache; else cc.in = cap_cache;
     if (zdit_status s = stack_forward(*cfg, *w, nb, lat_h, lat_w, x, 0, cap_feats, max_cap_len, cap_len, tv, vel,
-                                      sws, st)) return s;
+                                      sws, st, cc)) return s;
     HIP_TRY(launch_euler(x, vel, nb == 2 ? vel + n : nullptr, n, guidance, sg[i], sg[i + 1],
                          i == num_steps - 1 ? decode_out : nullptr, st));
   }

@@ -160,6 +160,9 @@ typedef struct {
  *   t             host [batch] model time (1 - sigma for the sampler)
  *   velocity      device fp32 [batch, latent_ch, lat_h, lat_w], written
  *   lat_h, lat_w  even, >= 2
+ * With latent_batch_stride 0 and the same t for every branch, the image tokens through the
+ * noise refiners are the same in every branch: they are computed once and copied (the result
+ * is bit-identical to computing each branch).
  * ------------------------------------------------------------------------------------- */
 size_t zdit_stack_workspace(const zdit_model_cfg* cfg, int32_t batch, int32_t lat_h,
                             int32_t lat_w, int32_t max_cap_len);
@@ -205,6 +208,9 @@ zdit_status zdit_euler_step(float* x, const float* v_cond, const float* v_uncond
  *                (nb = 2 when guidance != 0, else 1)
  *   cap_len      host [nb]
  *   decode_out   NULL or device fp32 [latent_ch, lat_h, lat_w]: final latent unscaled once
+ * The caption rows after the context refiners depend on neither the latent nor t: they are
+ * computed in the first step, kept in the workspace and reused in every later step (the
+ * result is bit-identical to running the full stack each step).
  * ------------------------------------------------------------------------------------- */
 size_t zdit_sample_workspace(const zdit_model_cfg* cfg, int32_t lat_h, int32_t lat_w,
                              int32_t max_cap_len, float guidance);

@@ -25,15 +25,21 @@ def stack_case(dims, lat_h, lat_w, cap_len, seed, t=0.5):
     return dict(dims=dims, W=W, lat=lat, cap=cap, cap_len=list(cap_len), Lmax=Lmax, t=t, lat_h=lat_h, lat_w=lat_w)
 
 
-def gpu_stack(case, prec=BF, model=None, batch=None):
+def gpu_stack(case, prec=BF, model=None, batch=None, t=None, per_branch_latents=False):
+    """per_branch_latents: pass B copies of the latent with a nonzero branch stride instead of
+    one shared latent (stride 0); t: per-branch model times (default case["t"] for all)."""
     dims = case["dims"]
     B = batch or len(case["cap_len"])
     cfg = Z.make_cfg(dims, prec)
     model = model or Z.upload_model(case["W"], prec)
     vel = torch.empty((B, dims.latent_ch, case["lat_h"], case["lat_w"]), device="cuda")
     ws = Z.workspace(Z.zdit_stack_workspace(cfg, B, case["lat_h"], case["lat_w"], case["Lmax"]))
-    Z.zdit_stack_fwd(cfg, model, B, case["lat_h"], case["lat_w"], dev(case["lat"]), 0, dev(case["cap"][:B]),
-                     case["Lmax"], case["cap_len"][:B], [case["t"]] * B, vel, ws)
+    lat, stride = dev(case["lat"]), 0
+    if per_branch_latents:
+        lat = dev(np.stack([case["lat"]] * B))
+        stride = case["lat"].size
+    Z.zdit_stack_fwd(cfg, model, B, case["lat_h"], case["lat_w"], lat, stride, dev(case["cap"][:B]),
+                     case["Lmax"], case["cap_len"][:B], t or [case["t"]] * B, vel, ws)
     return host(vel), model
 
 
@@ -66,6 +72,32 @@ def test_stack_branch_alone_equals_branch_in_pair():
     pair, model = gpu_stack(case)
     alone, _ = gpu_stack(case, model=model, batch=1)
     np.testing.assert_array_equal(alone[0], pair[0])
+
+
+def test_stack_shared_latent_equals_per_branch_copies():
+    """One shared latent at one model time lets the image path through the noise refiners run
+    once for every branch; the result is bit-identical to giving each branch its own copy of
+    the latent (which computes every branch), and to the oracle per branch."""
+    note("stack shared latent vs per-branch copies")
+    case = stack_case(synth.TINY.replace(n_main=3), 16, 16, (45, 10, 33), seed=76)
+    shared, model = gpu_stack(case)
+    copies, _ = gpu_stack(case, model=model, per_branch_latents=True)
+    np.testing.assert_array_equal(shared, copies)
+    for b in range(3):
+        assert rel_l2(shared[b], oracle_stack(case, b)) <= 1e-2
+
+
+def test_stack_shared_latent_different_times():
+    """A shared latent at different model times per branch: each branch matches the oracle at
+    its own time and equals that branch run alone."""
+    note("stack shared latent, two model times")
+    case = stack_case(synth.TINY.replace(n_main=2), 16, 16, (20, 20), seed=77)
+    got, model = gpu_stack(case, t=[0.25, 0.75])
+    for b, tb in enumerate((0.25, 0.75)):
+        ref = O.stack(case["lat"], case["cap"][b], 20, tb, case["W"], case["dims"])
+        assert rel_l2(got[b], ref) <= 1e-2
+    alone, _ = gpu_stack(dict(case, cap=case["cap"][1:]), model=model, batch=1, t=[0.75])
+    np.testing.assert_array_equal(alone[0], got[1])
 
 
 def test_stack_full_width_reduced_depth_256px():
@@ -121,3 +153,30 @@ def test_sample_tiny_full_depth(guidance):
     assert e <= 1e-2
     # the decode output is the GPU's own final latent unscaled exactly once
     np.testing.assert_array_equal(host(dec), O.unscale(host(x)))
+
+
+def test_sample_equals_stack_and_euler_calls():
+    """zdit_sample keeps the caption rows after the context refiners from its first step and
+    reuses them in later steps; the final latent is bit-identical to calling zdit_stack_fwd
+    (which runs the context refiners every time) and zdit_euler_step once per step."""
+    note("sample vs per-step stack + euler calls")
+    dims = synth.TINY.replace(n_main=4)
+    case = stack_case(dims, 16, 16, (45, 10), seed=78)
+    cfg = Z.make_cfg(dims)
+    model = Z.upload_model(case["W"])
+    steps, g = 4, 1.0
+    x = dev(case["lat"])
+    dec = torch.empty_like(x)
+    ws = Z.workspace(Z.zdit_sample_workspace(cfg, 16, 16, case["Lmax"], g))
+    Z.zdit_sample(cfg, model, 16, 16, x, dev(case["cap"]), case["Lmax"], case["cap_len"], g, steps, 3.0, dec, ws)
+    sg = Z.zdit_sigmas(steps, 3.0)
+    y = dev(case["lat"])
+    vel = torch.empty((2,) + tuple(y.shape), device="cuda")
+    sws = Z.workspace(Z.zdit_stack_workspace(cfg, 2, 16, 16, case["Lmax"]))
+    n = y.numel()
+    for i in range(steps):
+        ti = float(np.float32(1.0) - np.float32(sg[i]))
+        Z.zdit_stack_fwd(cfg, model, 2, 16, 16, y, 0, dev(case["cap"]), case["Lmax"], case["cap_len"], [ti, ti],
+                         vel, sws)
+        Z.zdit_euler_step(y, vel[0], vel[1], n, g, sg[i], sg[i + 1])
+    np.testing.assert_array_equal(host(x), host(y))
