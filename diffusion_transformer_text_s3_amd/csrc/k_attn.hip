@@ -2,16 +2,17 @@
 // ragged per branch: keys j >= seq_len[b] are masked (batch-alignment padding), every key
 // below it (image tokens, caption tokens and learned caption pads) is context.
 //
-// bf16 path on gfx950.  A 256-thread workgroup owns 128 queries of one (branch, head); each
+// bf16 path on gfx950.  A 512-thread workgroup owns 256 queries of one (branch, head); each
 // wavefront owns 32 of them and keeps their 128-dim rows in registers as MFMA B operands.
-// Key blocks of 64 are staged in LDS: K as [key][dim] and V as [dim][key] (V is transposed
-// once per layer by vtrans_kernel).  Scores are formed transposed, S^T = K Q^T, so each lane
-// holds 32 scores of a single query: the running max needs one cross-lane step (lane ^ 32)
-// and the rescale of the output accumulator is a per-lane scalar.  The output is formed
-// transposed too, O^T += V^T P^T, where the bf16 P^T operand is taken straight from the
-// score registers: in a 32x32 MFMA result, lane half h holds keys {8g + 4h + 0..3}, so for
-// each group of 16 keys both operands use the key order {4h..4h+3, 8+4h..8+4h+3}; V^T is
-// stored with each 16-key group in that order, so a lane reads its 8 keys in one 16-byte load.
+// Key blocks of 64 are staged in LDS by direct-to-LDS buffer loads: K as [key][dim] and V as
+// [dim][key] (V is transposed once per layer by vtrans_kernel).  Scores are formed
+// transposed, S^T = K Q^T, so each lane holds 32 scores of a single query: the running max
+// needs one cross-lane step (lane ^ 32) and the rescale of the output accumulator is a
+// per-lane scalar.  The output is formed transposed too, O^T += V^T P^T, where the bf16 P^T
+// operand is taken straight from the score registers: in a 32x32 MFMA result, lane half h
+// holds keys {8g + 4h + 0..3}, so for each group of 16 keys both operands use the key order
+// {4h..4h+3, 8+4h..8+4h+3}; V^T is stored with each 16-key group in that order, so a lane
+// reads its 8 keys in one 16-byte load.
 // Online softmax in fp32 with exp2 and the 1/sqrt(128) scale folded into log2(e).
 #include <type_traits>
 
@@ -22,8 +23,7 @@ namespace zdit {
 namespace {
 
 constexpr int KT = 64;   // keys per LDS block
-constexpr int KROW = 17; // 16-byte chunks per K row in LDS (16 + 1 pad)
-constexpr int VROW = 9;  // 16-byte chunks per V^T row in LDS (8 + 1 pad)
+constexpr int KROW = 17; // 16-byte chunks per row of the V transpose staging tile (16 + 1 pad)
 
 __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
   __shared__ uint4 t[64 * KROW];
@@ -59,18 +59,16 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
 }
 
 // 8 wavefronts x 32 queries = 256 queries per workgroup (two wavefronts per SIMD, so one's
-// softmax overlaps the other's MFMAs).  K and V^T key blocks are double-buffered in LDS and
-// prefetched through registers one block ahead.  Per key block t: softmax of the scores of
-// block t, O^T += V^T P^T, then the QK^T MFMAs of block t+1 (built with ZDIT_ATTN_PIPELINE
-// the QK^T of block t+1 is issued before the softmax instead; measured slower on gfx950).
-#ifndef ZDIT_ATTN_WAVES
-#define ZDIT_ATTN_WAVES 8
-#endif
-constexpr int NWAVE = ZDIT_ATTN_WAVES;
+// softmax can overlap the other's MFMAs).  K and V^T key blocks are double-buffered in LDS and
+// fetched with direct-to-LDS buffer loads one block ahead (no staging registers).  Per key
+// block t: softmax of the scores of block t, O^T += V^T P^T, then the QK^T MFMAs of block t+1.
+constexpr int NWAVE = 8;
 constexpr int QTILE = 32 * NWAVE;
-constexpr int ATT_NT = 64 * NWAVE;           // threads per workgroup
-constexpr int KCH = KT * 16 / ATT_NT;        // 16-byte K chunks per thread per key block
-constexpr int VCH = kHeadDim * 8 / ATT_NT;   // 16-byte V^T chunks per thread per key block
+constexpr int ATT_NT = 64 * NWAVE;  // threads per workgroup
+// buffer resource word 3 for raw (untyped, offset-addressed) buffer loads
+constexpr int kAttBufFlags = 0x00020000;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kAttVmcnt0 = 0x0F70;
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  The 1-D grid is renumbered so that
 // consecutive logical ids (the query tiles of one (branch, head), which share its K and V)
@@ -81,17 +79,34 @@ __device__ __forceinline__ int xcd_logical_id(int pid, int nwg) {
   return (xcd < rem) ? xcd * (full + 1) + idx : rem * (full + 1) + (xcd - rem) * full + idx;
 }
 
-// two wavefronts per SIMD in either shape (8-wave workgroups: one per CU; 4-wave: two per CU)
+// One lane's 16 bytes of a direct-to-LDS load: lane L writes LDS at lds_base + 16 L.  voff is
+// bounds-checked against the resource (out of range loads zero); soff is not.
+__device__ __forceinline__ void att_dma_16(const __amdgpu_buffer_rsrc_t rs, const uint4* lds_base, int voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff,
+                                           soff, 0, 0);
+}
+
+// LDS layouts (16-byte chunks).  K block: row = key (16 chunks = 128 dims), chunk c of key k
+// at slot c ^ (k & 15).  V^T block: row = dim (8 chunks = 64 keys), chunk c of dim d at slot
+// c ^ (d & 7) ^ ((d >> 3) & 1).  Either way the 16 lanes that one 16-byte LDS read serves in
+// a cycle (16 consecutive rows, one logical chunk) hit 16 distinct bank groups.
+__device__ __forceinline__ int k_slot(int key, int c) { return key * 16 + (c ^ (key & 15)); }
+__device__ __forceinline__ int v_slot(int d, int c) { return d * 8 + (c ^ (d & 7) ^ ((d >> 3) & 1)); }
+
 __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ uint4 Ks[2][KT * KROW];
-  __shared__ uint4 Vs[2][kHeadDim * VROW];
+  // four separate objects, so reads of one buffer are not ordered behind the in-flight
+  // direct-to-LDS writes of another
+  __shared__ uint4 K0[KT * 16], K1[KT * 16];
+  __shared__ uint4 V0[kHeadDim * 8], V1[kHeadDim * 8];
   const int nqt = (a.s_max + QTILE - 1) / QTILE;
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int qt = lid % nqt, bh = lid / nqt;
   const int h = bh % a.n_heads, b = bh / a.n_heads, q0 = qt * QTILE;
   const int D = a.n_heads * kHeadDim;
   const int S = a.seq_len[b];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, fh = lane >> 5;
   const int q = q0 + wave * 32 + fr;
   const bf16* qkv = (const bf16*)a.qkv;
@@ -112,47 +127,44 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
   }
 
+  // K rows of this (branch, head): key k at k * 3D elements from kbase.  The resource ends
+  // after key S - 1's 128 dims, so keys >= S load as zero.
+  const int krow = 3 * D * 2;  // bytes between consecutive keys
   const bf16* kbase = qkv + (int64_t)b * a.s_max * 3 * D + D + h * kHeadDim;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (S - 1) * krow + kHeadDim * 2, kAttBufFlags);
   const bf16* vbase = (const bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
-  // prefetch assignment: K chunk c = tid + ATT_NT i -> key c / 16, 16-byte chunk c % 16;
-  // V^T chunk c -> dim c / 8, chunk c % 8
-  uint4 rk[KCH], rv[VCH];
-  auto gload_k = [&](int t) {
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kHeadDim * a.s_pad * 2, kAttBufFlags);
+  // Each key block is 16 KB of K and 16 KB of V^T: 16 wave loads of 1 KB each, two per wave.
+  // K load j covers keys 4j .. 4j+3 (lane L: key 4j + L / 16, slot L % 16); V^T load j covers
+  // dims 8j .. 8j+7 (lane L: dim 8j + L / 8, slot L % 8).  Lanes fetch the chunk that belongs
+  // in their slot.
+  int kvo[2], vvo[2];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + ATT_NT * i, key = t * KT + (c >> 4);
-      rk[i] = key < S ? *(const uint4*)(kbase + (int64_t)key * 3 * D + (c & 15) * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto gload_v = [&](int t) {
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave * 2 + i;
+    const int key = 4 * j + (lane >> 4), ks = lane & 15;
+    kvo[i] = key * krow + (ks ^ (key & 15)) * 16;
+    const int d = 8 * j + (lane >> 3), vs = lane & 7;
+    vvo[i] = d * a.s_pad * 2 + (vs ^ (d & 7) ^ ((d >> 3) & 1)) * 16;
+  }
+  auto dma_k = [&](int t, uint4* dst) {
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + ATT_NT * i;
-      rv[i] = *(const uint4*)(vbase + (int64_t)(c >> 3) * a.s_pad + t * KT + (c & 7) * 8);
-    }
+    for (int i = 0; i < 2; ++i) att_dma_16(krs, dst + (wave * 2 + i) * 64, kvo[i] + t * KT * krow, 0);
   };
-  auto sstore_k = [&](int buf) {
+  auto dma_v = [&](int t, uint4* dst) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + ATT_NT * i;
-      Ks[buf][(c >> 4) * KROW + (c & 15)] = rk[i];
-    }
+    for (int i = 0; i < 2; ++i) att_dma_16(vrs, dst + (wave * 2 + i) * 64, vvo[i], t * KT * 2);
   };
-  auto sstore_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + ATT_NT * i;
-      Vs[buf][(c >> 3) * VROW + (c & 7)] = rv[i];
-    }
-  };
-  auto qk = [&](int buf, f32x16 (&st)[2]) {
+  auto qk = [&](const uint4* Kb, f32x16 (&st)[2]) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[t2][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, Ks[buf][(t2 * 32 + fr) * KROW + 2 * s + fh]);
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, Kb[k_slot(t2 * 32 + fr, 2 * s + fh)]);
         st[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t2], 0, 0, 0);
       }
     }
@@ -167,15 +179,16 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
   const float sc = 1.4426950408889634f / sqrtf((float)kHeadDim);
   const int nkt = (S + KT - 1) / KT;
 
-  // One key block: softmax of block t (held in `cur`), O^T += V^T P^T, QK^T of block t+1
-  // into `nxt`.  Two copies alternate the roles of the score registers, so no copy is
-  // needed between iterations.  Only the final block can hold keys >= S (masked).
-  auto step = [&](auto masked, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  // One key block t, its K in Kc / V^T in Vc: loads of V^T block t+1 (into Vn) and K block
+  // t+2 (into Kc, free since the scores of block t exist) start first; softmax of block t
+  // (scores in `cur`), O^T += V^T P^T, QK^T of block t+1 (K in Kn) into `nxt`; then every
+  // wave waits for its loads and the workgroup meets at a barrier.  Only the final block can
+  // hold keys >= S (masked).
+  auto step = [&](auto masked, int t, uint4* Kc, uint4* Vc, uint4* Kn, uint4* Vn, f32x16 (&cur)[2],
+                  f32x16 (&nxt)[2]) {
     const bool more = t + 1 < nkt;
-    if (more) gload_v(t + 1);
-#ifdef ZDIT_ATTN_PIPELINE
-    if (more) qk((t + 1) & 1, nxt);
-#endif
+    if (more) dma_v(t + 1, Vn);
+    if (t + 2 < nkt) dma_k(t + 2, Kc);
 
     float mx = -INFINITY;
     if constexpr (decltype(masked)::value) {
@@ -214,46 +227,43 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
         l_run += p;
         pb[t2][r >> 3][r & 7] = (bf16)p;
       }
-    // the K prefetch is issued once this block's scores are dead (keeps the register peak low)
-    if (t + 2 < nkt) gload_k(t + 2);
-    const uint4* Vb = Vs[t & 1];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          // 16-byte chunk (t2 * 4 + j * 2 + fh) of the V^T row holds this lane half's 8 keys
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, Vb[(dt * 32 + fr) * VROW + t2 * 4 + j * 2 + fh]);
+          // logical chunk (t2 * 4 + j * 2 + fh) of the V^T row holds this lane half's 8 keys
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, Vc[v_slot(dt * 32 + fr, t2 * 4 + j * 2 + fh)]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t2][j], o[dt], 0, 0, 0);
         }
     }
-#ifndef ZDIT_ATTN_PIPELINE
-    if (more) qk((t + 1) & 1, nxt);
-#endif
-    if (t + 2 < nkt) sstore_k(t & 1);
-    if (more) sstore_v((t + 1) & 1);
+    if (more) qk(Kn, nxt);
+    __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
     __syncthreads();
   };
 
-  gload_k(0); sstore_k(0);
-  gload_v(0); sstore_v(0);
-  if (nkt > 1) { gload_k(1); sstore_k(1); }
+  dma_k(0, K0);
+  dma_v(0, V0);
+  if (nkt > 1) dma_k(1, K1);
+  __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
   __syncthreads();
   f32x16 sA[2], sB[2];
-  qk(0, sA);
+  qk(K0, sA);
+  // step 0 loads key block 2 into K0: every wave's reads of K0 must be done
+  __syncthreads();
   using Plain = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
   int t = 0;
   for (; t + 2 < nkt; t += 2) {
-    step(Plain{}, t, sA, sB);
-    step(Plain{}, t + 1, sB, sA);
+    step(Plain{}, t, K0, V0, K1, V1, sA, sB);
+    step(Plain{}, t + 1, K1, V1, K0, V0, sB, sA);
   }
   if (nkt - t == 2) {
-    step(Plain{}, t, sA, sB);
-    step(Masked{}, t + 1, sB, sA);
+    step(Plain{}, t, K0, V0, K1, V1, sA, sB);
+    step(Masked{}, t + 1, K1, V1, K0, V0, sB, sA);
   } else {
-    step(Masked{}, t, sA, sB);
+    step(Masked{}, t, K0, V0, K1, V1, sA, sB);
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);

@@ -153,7 +153,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   // Direct-to-LDS: one wave instruction writes 1 KB = 8 rows (blk * 8 ..) of the tile, lane L
   // landing at slot L % 8 of row L / 8; it therefore fetches chunk (L % 8) ^ g(row), where
-  // g(row) = (L / 8) ^ (blk & 1).  Two lane offsets, for even and odd blk.
+  // g(row) = (L / 8) ^ (blk & 1).  The row offset goes into the per-lane (bounds-checked)
+  // offset, so rows past the resource read as zero; only the K offset is scalar (the scalar
+  // offset is not bounds-checked, and K offsets always stay inside a row).
   const int lr = lane >> 3;
   const int lkc0 = (lane & 7) ^ lr, lkc1 = lkc0 ^ 1;
   const int va0 = (lr * (int)g.lda + lkc0 * 8) * 2, va1 = (lr * (int)g.lda + lkc1 * 8) * 2;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < BLK; ++i) {
       const int blk = wave * BLK + i;        // rows blk*8 .. blk*8+7 of the tile
-      lds_dma_16(ra_rs, &stage[0][blk * 64], (i & 1) ? va1 : va0, blk * 8 * (int)g.lda * 2 + kb);
+      lds_dma_16(ra_rs, &stage[0][blk * 64], ((i & 1) ? va1 : va0) + blk * 8 * (int)g.lda * 2, kb);
       int brow;
       __amdgpu_buffer_rsrc_t rsb = rb_rs;
       if constexpr (EPI == EPI_SWIGLU) {
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
       } else {
         brow = blk * 8;
       }
-      lds_dma_16(rsb, &stage[1][blk * 64], (i & 1) ? vb1 : vb0, brow * (int)g.ldb * 2 + kb);
+      lds_dma_16(rsb, &stage[1][blk * 64], ((i & 1) ? vb1 : vb0) + brow * (int)g.ldb * 2, kb);
     }
   };
 

@@ -3,6 +3,7 @@
 // first launch; on error nothing is enqueued.
 #include <math.h>
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -255,6 +256,10 @@ zdit_status check_model_w(const zdit_model_cfg& cfg, const zdit_model_w* w) {
   return ZDIT_OK;
 }
 
+// The attention kernel addresses one branch's qkv rows ([s_max, 3 dim] bf16) with 32-bit byte
+// offsets.
+bool seq_fits(int64_t s_max, int dim) { return s_max * 6 * dim <= INT32_MAX; }
+
 zdit_status check_stack_args(const zdit_model_cfg* cfg, const zdit_model_w* w, int batch, int lat_h,
                              int lat_w, const float* latents, const float* cap_feats, int max_cap_len,
                              const int* cap_len, const float* t, const float* velocity) {
@@ -264,6 +269,9 @@ zdit_status check_stack_args(const zdit_model_cfg* cfg, const zdit_model_w* w, i
   if (lat_h < 2 || lat_w < 2 || lat_h % 2 || lat_w % 2) return fail(ZDIT_EINVAL, "lat_h %d / lat_w %d must be even and >= 2", lat_h, lat_w);
   if ((int64_t)(lat_h / 2) * (lat_w / 2) > (1 << 20)) return fail(ZDIT_EUNSUPPORTED, "too many image tokens");
   if (max_cap_len < 1) return fail(ZDIT_EINVAL, "max_cap_len %d", max_cap_len);
+  const int64_t s_bound = (int64_t)(lat_h / 2) * (lat_w / 2) +
+                          round_up(std::min(max_cap_len, cfg->max_cap_len), cfg->seq_multiple);
+  if (!seq_fits(s_bound, cfg->d.dim)) return fail(ZDIT_EUNSUPPORTED, "sequence of %lld tokens too long", (long long)s_bound);
   if (!latents || !cap_feats || !velocity || !cap_len || !t) return fail(ZDIT_EINVAL, "NULL pointer argument");
   if (!aligned16(latents) || !aligned16(cap_feats) || !aligned16(velocity)) return fail(ZDIT_EINVAL, "device pointer not 16-byte aligned");
   const int lim = std::min(max_cap_len, cfg->max_cap_len);
@@ -412,6 +420,7 @@ zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t
   if (zdit_status s = check_block_w(w, false)) return s;
   if (batch < 1 || batch > ZDIT_MAX_BATCH) return fail(ZDIT_EINVAL, "batch %d (1..%d)", batch, ZDIT_MAX_BATCH);
   if (s_max < 1 || (int64_t)batch * s_max > (1 << 24)) return fail(ZDIT_EINVAL, "s_max %d", s_max);
+  if (!seq_fits(s_max, dims->dim)) return fail(ZDIT_EUNSUPPORTED, "s_max %d too long for dim %d", s_max, dims->dim);
   if (!seq_len) return fail(ZDIT_EINVAL, "seq_len is NULL");
   for (int b = 0; b < batch; ++b)
     if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d outside 1..%d", b, seq_len[b], s_max);
@@ -614,6 +623,7 @@ zdit_status zdit_op_attn(int32_t precision, int32_t batch, int32_t s_max, int32_
                          const void* qkv, void* out, void* ws, size_t ws_bytes, void* hip_stream) {
   if (precision != ZDIT_BF16 && precision != ZDIT_FP32_DEBUG) return fail(ZDIT_EINVAL, "precision %d", precision);
   if (batch < 1 || batch > ZDIT_MAX_BATCH || s_max < 1 || n_heads < 1) return fail(ZDIT_EINVAL, "batch/s_max/n_heads");
+  if (n_heads > 32 || !seq_fits(s_max, n_heads * kHeadDim)) return fail(ZDIT_EUNSUPPORTED, "s_max %d / n_heads %d too large", s_max, n_heads);
   if (!seq_len || !qkv || !out) return fail(ZDIT_EINVAL, "NULL pointer argument");
   for (int b = 0; b < batch; ++b)
     if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d", b, seq_len[b]);

@@ -92,7 +92,7 @@ typedef struct {
  * Rows j >= seq_len[b] of x are padding: masked as keys and left untouched.
  *
  *   batch        1..ZDIT_MAX_BATCH rows (branches) of x
- *   s_max        rows per branch in x (>= every seq_len)
+ *   s_max        rows per branch in x (>= every seq_len; s_max * 6 * dim <= 2^31 - 1)
  *   seq_len      host [batch], each in 1..s_max: valid rows of branch b
  *   x            device fp32 [batch, s_max, dim], in/out (the residual stream)
  *   c            device fp32 [batch, c_dim] conditioning vector; ignored when w_ada NULL
@@ -266,7 +266,8 @@ zdit_status zdit_op_rope(int32_t precision, int32_t batch, int32_t s_max, int32_
 
 /* Joint attention on a fused, already rotated qkv buffer [batch, s_max, 3 * n_heads * 128]
  * -> out [batch, s_max, n_heads * 128] (activation type); keys j >= seq_len[b] masked; rows
- * >= seq_len[b] of out are written as 0.  ws: zdit_op_attn_workspace() bytes. */
+ * >= seq_len[b] of out are written as 0.  ws: zdit_op_attn_workspace() bytes.  n_heads
+ * 1..32, s_max * 6 * n_heads * 128 <= 2^31 - 1 (else ZDIT_EUNSUPPORTED). */
 size_t zdit_op_attn_workspace(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads);
 zdit_status zdit_op_attn(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads,
                          const int32_t* seq_len, const void* qkv, void* out, void* ws,
