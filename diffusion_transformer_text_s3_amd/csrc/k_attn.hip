@@ -87,6 +87,17 @@ __device__ __forceinline__ void att_dma_16(const __amdgpu_buffer_rsrc_t rs, cons
                                            soff, 0, 0);
 }
 
+// f(v[lane], v[lane ^ 32]) for a symmetric f, on the VALU: v_permlane32_swap of (v, v) gives
+// {v[lane & 31], v[32 + (lane & 31)]}.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // LDS layouts (16-byte chunks).  K block: row = key (16 chunks = 128 dims), chunk c of key k
 // at slot c ^ (k & 15).  V^T block: row = dim (8 chunks = 64 keys), chunk c of dim d at slot
 // c ^ (d & 7) ^ ((d >> 3) & 1).  Either way the 16 lanes that one 16-byte LDS read serves in
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[t2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx * sc);
     // Lazy rescale: the reference max moves only when some lane's max rose by more than 8
     // (log2 units), so p = exp2(s - m_run) stays below 2^8; O and l share the reference, so
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
     step(Masked{}, t, K0, V0, K1, V1, sA, sB);
   }
 
-  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float l = xor32_sum(l_run);
   const float inv = 1.0f / l;
   if (q < a.s_max) {
     bf16* op = out + ((int64_t)b * a.s_max + q) * D + h * kHeadDim;
