@@ -180,3 +180,23 @@ def test_sample_equals_stack_and_euler_calls():
                          vel, sws)
         Z.zdit_euler_step(y, vel[0], vel[1], n, g, sg[i], sg[i + 1])
     np.testing.assert_array_equal(host(x), host(y))
+
+
+def test_sample_base_recipe_50_steps_cfg4():
+    """The Base recipe on the same path: 50 FlowMatchEuler updates with negated CFG at g = 4
+    (shift 3), cond/uncond pair, against the oracle's sampler (100 DiT calls)."""
+    note("sample 50 steps g=4")
+    dims = synth.TINY.replace(n_main=4)
+    case = stack_case(dims, 16, 16, (45, 10), seed=79)
+    cfg = Z.make_cfg(dims)
+    model = Z.upload_model(case["W"])
+    x = dev(case["lat"])
+    dec = torch.empty_like(x)
+    ws = Z.workspace(Z.zdit_sample_workspace(cfg, 16, 16, case["Lmax"], 4.0))
+    Z.zdit_sample(cfg, model, 16, 16, x, dev(case["cap"]), case["Lmax"], case["cap_len"], 4.0, 50, 3.0, dec, ws)
+    rx, _, calls = _oracle_sample(case, 4.0, num_steps=50)
+    assert len(calls) == 100
+    e = rel_l2(host(x), rx)
+    print(f"sample 50 steps g=4: final latent rel-L2 {e:.2e}", flush=True)
+    assert e <= 1e-2
+    np.testing.assert_array_equal(host(dec), O.unscale(host(x)))
