@@ -1,13 +1,19 @@
 // Dense contractions of the S3-DiT block on gfx950: C = A B^T with A [M, K] and B [N, K]
 // both K-contiguous (activations [tokens, features] and weights [out, in]).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  One 256-thread workgroup owns a
-// 256 x 256 tile of C; its four wavefronts each own 128 x 128 (4 x 4 MFMA tiles, 256 fp32
-// accumulators per lane).  K advances in steps of 64 through two LDS buffers (2 x 64 KB):
-// the next K-slab is fetched from global into registers while the current one feeds the
-// MFMAs, then written to the other buffer.  LDS rows are 128 B (64 bf16); the eight 16-byte
-// chunks of row r are stored at chunk ^ (r & 7), so both the 16-byte stores of a row and
-// the 16-byte fragment reads of eight consecutive rows hit distinct banks.
+// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  One 512-thread workgroup owns a
+// 256 x 256 tile of C; each of its eight wavefronts owns 64 x 128 of it (2 x 4 MFMA tiles,
+// 128 fp32 accumulators per lane).  K advances in 32-wide slabs through a ring of four LDS
+// stages of 32 KB filled by direct-to-LDS buffer loads, issued three slabs ahead.
+//
+// The eight wavefronts form two groups of four, one wave of each group per SIMD (waves w and
+// w + 4 share a SIMD), run half a period apart ("ping-pong"): while one group issues the
+// sixteen MFMAs of a slab (with its share of the global loads spread between them), the other
+// reads the fragments of its next slab from LDS.  A workgroup barrier separates the phases, so
+// each SIMD's matrix pipe is fed by one wave while the other waits on LDS.
+//
+// LDS rows are 64 B (32 bf16 = four 16-byte chunks); chunk c of row r sits at slot
+// c ^ ((r >> 2) & 3), so the 16-byte fragment reads of 16 consecutive rows cover all 64 banks.
 //
 // Workgroups are numbered so that the ones dispatched to the same XCD (round-robin over 8)
 // get consecutive tiles, and tiles are walked in groups of 8 row-panels, so each XCD's L2
@@ -23,18 +29,27 @@ namespace zdit {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int STAGE_CHUNKS = 2 * BM * (BK / 8);  // A rows then B rows, 16-byte chunks (32 KB)
+constexpr int DMA_PER_WAVE = 4;                  // 1 KB direct-to-LDS loads per wave per slab
 // buffer resource word 3 for raw (untyped, offset-addressed) buffer loads
 constexpr int kBufFlags = 0x00020000;
-// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
-constexpr int kVmcnt0 = 0x0F70;
+// s_waitcnt immediates: vmcnt in bits 3:0 (low) and 15:14 (high), expcnt in 6:4, lgkmcnt in
+// 11:8; a field at its maximum does not wait
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kVmcnt0 = waitcnt_vm(0);
+// all but the loads of the last NST - 2 slabs a wave issued
+constexpr int kVmcntRing = waitcnt_vm((NST - 2) * DMA_PER_WAVE);
+// group 1 at the end of its memory phase of slab k has issued up to slab k + NST - 2
+constexpr int kVmcntG1 = waitcnt_vm((NST - 3) * DMA_PER_WAVE);
+constexpr int kLgkmcnt0 = 0xC07F;                     // lgkmcnt(0)
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// v * sigmoid(v) with the hardware reciprocal (about 1 ulp): the product is rounded to bf16
+__device__ __forceinline__ float silu_fast(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
-// Chunk kc of row r sits at slot kc ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1): any 8 aligned
-// consecutive rows, and the rows of either parity among 16 consecutive rows, see distinct
-// slots, so 16-byte fragment reads of 16 consecutive rows touch distinct banks.
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7) ^ ((row >> 3) & 1)); }
+// Slot (16-byte units from the operand's first row) of logical chunk c of row r.
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 // Physical workgroup id -> (tile row, tile col).
 __device__ __forceinline__ void tile_coords(int pid, int nwg, int tiles_m, int tiles_n, int& tm,
@@ -66,72 +81,194 @@ __device__ __forceinline__ RowAddr map_row(const RowMap& rm, int m) {
   return ra;
 }
 
-// LDS stage: A tile [256 rows][8 x 16-byte chunks] then B tile, 64 KB.  Chunk kc of row r
-// sits at slot kc ^ (r & 7).
+// m / rpb for 0 <= m < 2^24 through a float reciprocal (rinv = 1 / rpb, rounded), corrected
+// to the exact quotient: the float estimate is off by at most one.
+__device__ __forceinline__ int div_rows(int m, int rpb, float rinv) {
+  int b = (int)((float)m * rinv);
+  const int r = m - b * rpb;
+  b += (r >= rpb) - (r < 0);
+  return b;
+}
+
 __device__ __forceinline__ void lds_dma_16(const __amdgpu_buffer_rsrc_t rs, const uint4* lds_base,
                                            int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff,
                                            soff, 0, 0);
 }
 
-// Fragments of one k16 step (16-byte chunk kc) of a stage for this wave's MT A tiles and 4 B
-// tiles (each 32 rows).
-template <int MT>
-__device__ __forceinline__ void load_frags(const uint4* sa, const uint4* sb, int arow, int brow, int kc,
-                                           bf16x8 (&af)[MT], bf16x8 (&bf)[4]) {
-#pragma unroll
-  for (int i = 0; i < MT; ++i) af[i] = __builtin_bit_cast(bf16x8, sa[swz(arow + i * 32, kc)]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) bf[i] = __builtin_bit_cast(bf16x8, sb[swz(brow + i * 32, kc)]);
+__device__ __forceinline__ void barrier_fenced() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MT>
-__device__ __forceinline__ void mma_step(const bf16x8 (&af)[MT], const bf16x8 (&bf)[4], f32x16 (&acc)[MT][4]) {
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
-}
+// Per-wave state of the main loop.
+struct Frags {
+  bf16x8 a[2][2];  // [k16 step][32-row A tile]
+  bf16x8 b[2][4];  // [k16 step][32-row B tile]
+};
 
-// scheduling hint for one step's 4*MT MFMAs with the next step's MT + 4 LDS reads interleaved
-template <int MT>
-__device__ __forceinline__ void sched_mma_ds() {
-#ifndef ZDIT_GEMM_NO_SCHED
-  if constexpr (MT == 4) {
+__device__ __forceinline__ void read_frags(const uint4* st, int arow, int brow, int fh, Frags& f) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  } else {
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int i = 0; i < 2; ++i) f.a[s][i] = __builtin_bit_cast(bf16x8, st[swz(arow + 32 * i, 2 * s + fh)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[s][j] = __builtin_bit_cast(bf16x8, st[BM * 4 + swz(brow + 32 * j, 2 * s + fh)]);
   }
-#endif
 }
 
-// WAVES = 4: each wavefront owns 128 x 128 of the tile (4 x 4 MFMA tiles, one wave per SIMD).
-// WAVES = 8: each owns 64 x 128 (2 x 4 MFMA tiles, two waves per SIMD, so one wave's LDS and
-// barrier waits are covered by the other's MFMAs).
-template <int EPI, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int MT = 16 / WAVES;          // 32-row MFMA tiles per wave along M
-  constexpr int BLK = 32 / WAVES;         // 8-row DMA blocks per wave per operand
-  // two stages as separate objects, so reads of one stage are not ordered behind the
-  // in-flight direct-to-LDS loads of the other
-  __shared__ uint4 st0[2][BM * BK / 8];
-  __shared__ uint4 st1[2][BM * BK / 8];
+__device__ __forceinline__ void mma_slab(const Frags& f, f32x16 (&acc)[2][4]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+}
+
+// Epilogue of one wave: its MT x 4 accumulator tiles cover rows m_wave .. m_wave + 32 MT - 1 and
+// 128 columns from ncol_wave (SwiGLU: 64 output columns, W1 / W3 tiles paired).  stg is this
+// wave's private staging space in LDS (at least 9216 bytes).
+template <int EPI, int MT>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 (&acc)[MT][4], int m_wave, int ncol_wave,
+                                         char* stg, int lane) {
+  const int fr = lane & 31, fh = lane >> 5;
+  // Accumulator (mt, nt) element r of this lane is C[row][col] with
+  // row = 8 (r / 4) + 4 (lane / 32) + r % 4 and col = lane % 32 within the 32 x 32 tile.  Each
+  // wave stages 32 x 64 sub-tiles of its results in its own 16 KB of LDS (row-major, rows
+  // padded so that both the staging writes and the 16-byte read-back are free of bank
+  // conflicts) and writes them out as 16-byte row chunks: fp32 4 values, bf16 8 values per
+  // lane, one row address per chunk.
+  constexpr bool kF32 = (EPI == EPI_BIAS || EPI == EPI_RESID);
+  constexpr int ES = kF32 ? 4 : 2;             // bytes per staged element
+  constexpr int VW = 16 / ES;                  // elements per 16-byte chunk
+  constexpr int CPR = 64 / VW;                 // chunks per 64-wide row
+  constexpr int STRIDE = 64 * ES + 16 * (ES / 2);  // fp32: 288 B, bf16: 144 B
+  constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;  // 64-column sub-tiles per 32-row band
+  const int rpb = g.out.rows_per_batch;
+  const float rinv = 1.0f / (float)rpb;
+  // 16-byte row chunks need 16-byte aligned rows
+  const bool vec_ok = ((g.out.ld | g.out.batch_stride) % VW == 0) && (((uintptr_t)g.C & 15) == 0) &&
+                      (EPI != EPI_RESID || g.vec == nullptr || (g.vec_bstride % VW == 0 && ((uintptr_t)g.vec & 15) == 0)) &&
+                      (EPI != EPI_BIAS || ((uintptr_t)g.vec & 15) == 0);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int p = 0; p < NSUB; ++p) {
+      // stage: half h covers columns h*32 .. h*32+31 of the sub-tile
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
+          char* dst = stg + row * STRIDE + (h * 32 + fr) * ES;
+          if constexpr (EPI == EPI_SWIGLU) {
+            *(bf16*)dst = (bf16)(silu_fast(acc[mt][2 * h][r]) * acc[mt][2 * h + 1][r]);
+          } else if constexpr (EPI == EPI_STORE) {
+            *(bf16*)dst = (bf16)acc[mt][2 * p + h][r];
+          } else {
+            *(float*)dst = acc[mt][2 * p + h][r];
+          }
+        }
+      }
+      const int ncol0 = ncol_wave + p * 64;
+      constexpr int NIT = 32 * CPR / 64;
+      // addresses of this lane's chunks; all global loads are issued before any is used
+      int64_t off[NIT];
+      int nn[NIT], bq[NIT];
+      bool ok[NIT], full[NIT];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
+        const int m = m_wave + mt * 32 + row;
+        nn[it] = ncol0 + ch * VW;
+        const int mm = min(m, g.M - 1);
+        bq[it] = div_rows(mm, rpb, rinv);
+        const int rr = mm - bq[it] * rpb;
+        ok[it] = m < g.M && nn[it] < g.N && rr < g.out.valid[bq[it]];
+        off[it] = bq[it] * g.out.batch_stride + (int64_t)rr * g.out.ld + nn[it];
+        full[it] = vec_ok && nn[it] + VW <= g.N;
+      }
+      if constexpr (EPI == EPI_RESID) {
+        // two batches of four chunks: loads of a batch are all in flight before the first use
+#pragma unroll
+        for (int h0 = 0; h0 < NIT; h0 += 4) {
+          float4 x[4], gv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int it = h0 + q;
+            x[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            gv[q] = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (ok[it] && full[it]) {
+              x[q] = *(const float4*)((const float*)g.C + off[it]);
+              if (g.vec) gv[q] = *(const float4*)(g.vec + bq[it] * g.vec_bstride + nn[it]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int it = h0 + q;
+            if (!ok[it]) continue;
+            const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
+            const uint4 v = *(const uint4*)(stg + row * STRIDE + ch * 16);
+            const float* vf = (const float*)&v;
+            float* C = (float*)g.C + off[it];
+            if (full[it]) {
+              *(float4*)C = make_float4(x[q].x + gv[q].x * vf[0], x[q].y + gv[q].y * vf[1],
+                                        x[q].z + gv[q].z * vf[2], x[q].w + gv[q].w * vf[3]);
+            } else {
+              const float* gt = g.vec ? g.vec + bq[it] * g.vec_bstride + nn[it] : nullptr;
+              for (int e = 0; e < VW && nn[it] + e < g.N; ++e) C[e] = C[e] + (gt ? gt[e] : 1.0f) * vf[e];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          if (!ok[it]) continue;
+          const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
+          const uint4 v = *(const uint4*)(stg + row * STRIDE + ch * 16);
+          const int n = nn[it];
+          if constexpr (EPI == EPI_BIAS) {
+            const float* vf = (const float*)&v;
+            float* C = (float*)g.C + off[it];
+            if (full[it]) {
+              const float4 bi = *(const float4*)(g.vec + n);
+              *(float4*)C = make_float4(vf[0] + bi.x, vf[1] + bi.y, vf[2] + bi.z, vf[3] + bi.w);
+            } else {
+              for (int e = 0; e < VW && n + e < g.N; ++e) C[e] = vf[e] + g.vec[n + e];
+            }
+          } else {
+            bf16* C = (bf16*)g.C + off[it];
+            if (full[it]) {
+              *(uint4*)C = v;
+            } else {
+              const bf16* vb = (const bf16*)&v;
+              for (int e = 0; e < VW && n + e < g.N; ++e) C[e] = vb[e];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
+  // one object per stage, so LDS reads of one stage are not ordered behind the in-flight
+  // direct-to-LDS loads of another
+  __shared__ uint4 st0[STAGE_CHUNKS];
+  __shared__ uint4 st1[STAGE_CHUNKS];
+  __shared__ uint4 st2[STAGE_CHUNKS];
+  __shared__ uint4 st3[STAGE_CHUNKS];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  // the wave index is uniform: keep it in a scalar register (LDS bases and buffer offsets
-  // derived from it must be scalar)
+  // wave-uniform values live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // wm: MT*32-row band, wn: 128-column half
+  const int grp = wave >> 2, sw = wave & 3;   // group; the group's wave on SIMD sw
+  const int wm = grp * 2 + (sw >> 1), wn = sw & 1;  // 64-row band, 128-column half
   const int nout_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + nout_tile - 1) / nout_tile;
@@ -151,150 +288,101 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gemm_bf16_kernel(GemmArgs g) {
   if constexpr (EPI == EPI_SWIGLU)
     rb2_rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)g.B2 + (int64_t)n0 * g.ldb), 0, brec, kBufFlags);
 
-  // Direct-to-LDS: one wave instruction writes 1 KB = 8 rows (blk * 8 ..) of the tile, lane L
-  // landing at slot L % 8 of row L / 8; it therefore fetches chunk (L % 8) ^ g(row), where
-  // g(row) = (L / 8) ^ (blk & 1).  The row offset goes into the per-lane (bounds-checked)
-  // offset, so rows past the resource read as zero; only the K offset is scalar (the scalar
-  // offset is not bounds-checked, and K offsets always stay inside a row).
-  const int lr = lane >> 3;
-  const int lkc0 = (lane & 7) ^ lr, lkc1 = lkc0 ^ 1;
-  const int va0 = (lr * (int)g.lda + lkc0 * 8) * 2, va1 = (lr * (int)g.lda + lkc1 * 8) * 2;
-  const int vb0 = (lr * (int)g.ldb + lkc0 * 8) * 2, vb1 = (lr * (int)g.ldb + lkc1 * 8) * 2;
-
-  auto issue = [&](int kt, uint4 (&stage)[2][BM * BK / 8]) {
-    const int kb = kt * BK * 2;
+  // Direct-to-LDS loads: group 0 fetches the A rows of a slab, group 1 the B rows, each wave
+  // four 16-row blocks (1 KB each).  One instruction writes lane L at slot L of the block (row
+  // L / 4, slot L % 4), so lane L fetches logical chunk (L % 4) ^ ((L / 16) % 4) of its row.
+  // The row offset is in the per-lane (bounds-checked) offset; the K offset is scalar.
+  const int nk = g.K / BK;
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int64_t ld = grp == 0 ? g.lda : g.ldb;
+  int voff[DMA_PER_WAVE];
+  __amdgpu_buffer_rsrc_t drs[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < BLK; ++i) {
-      const int blk = wave * BLK + i;        // rows blk*8 .. blk*8+7 of the tile
-      lds_dma_16(ra_rs, &stage[0][blk * 64], ((i & 1) ? va1 : va0) + blk * 8 * (int)g.lda * 2, kb);
-      int brow;
-      __amdgpu_buffer_rsrc_t rsb = rb_rs;
-      if constexpr (EPI == EPI_SWIGLU) {
-        // tile row t = blk*8 + r: wave column t / 128, MFMA tile (t % 128) / 32 (even: W1,
-        // odd: W3), output column (t / 128) * 64 + (tile / 2) * 32 + t % 32
-        const int t = blk * 8, wc = t >> 7, mt = (t & 127) >> 5;
-        brow = wc * 64 + (mt >> 1) * 32 + (t & 31);
-        if (mt & 1) rsb = rb2_rs;
-      } else {
-        brow = blk * 8;
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int blk = sw * DMA_PER_WAVE + i;  // tile rows blk*16 .. blk*16+15
+    int row = blk * 16;
+    drs[i] = grp == 0 ? ra_rs : rb_rs;
+    if constexpr (EPI == EPI_SWIGLU) {
+      if (grp == 1) {
+        // tile row t: wave column t / 128, MFMA tile (t % 128) / 32 (even: W1, odd: W3),
+        // output column (t / 128) * 64 + (tile / 2) * 32 + t % 32
+        const int t = blk * 16, wc = t >> 7, mt = (t & 127) >> 5;
+        row = wc * 64 + (mt >> 1) * 32 + (t & 31);
+        if (mt & 1) drs[i] = rb2_rs;
       }
-      lds_dma_16(rsb, &stage[1][blk * 64], ((i & 1) ? vb1 : vb0) + brow * (int)g.ldb * 2, kb);
     }
+    voff[i] = (int)((row + (lane >> 2)) * ld * 2) + lchunk * 16;
+  }
+  const int dma_dst = (grp * BM + sw * DMA_PER_WAVE * 16) * 4;  // first chunk of this wave's blocks
+
+  auto issue = [&](int kt, uint4* stage) {
+    const int kb = min(kt, nk - 1) * BK * 2;  // past the end: reload the last slab into a dead stage
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma_16(drs[i], stage + dma_dst + i * 64, voff[i], kb);
   };
 
-  f32x16 acc[MT][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = g.K / BK;
   const int fr = lane & 31, fh = lane >> 5;
+  const int arow = wm * 64 + fr, brow = wn * 128 + fr;
+  Frags f;
 
-  const uint4* s0a = st0[0];
-  const uint4* s0b = st0[1];
-  const uint4* s1a = st1[0];
-  const uint4* s1b = st1[1];
-  const int arow = wm * (32 * MT) + fr, brow = wn * 128 + fr;
-  bf16x8 fa0[MT], fb0[4], fa1[MT], fb1[4];
-
-  // One 64-wide K slab from stage `cur` (its step-0 fragments already in fa0/fb0).  The
-  // barrier comes once the slab's last fragments are in registers: after it, the DMA of the
-  // slab two ahead goes into `cur`, and the next slab's step-0 fragments are read from `nxt`
-  // while the last 16 MFMAs of this slab run.
-#define ZDIT_SLAB(CA, CB, NA, NB, CUR_ST, HAS_NEXT, NEXT2)                                    \
-  {                                                                                           \
-    load_frags<MT>(CA, CB, arow, brow, 2 + fh, fa1, fb1);                                     \
-    mma_step<MT>(fa0, fb0, acc);                                                              \
-    sched_mma_ds<MT>();                                                                       \
-    load_frags<MT>(CA, CB, arow, brow, 4 + fh, fa0, fb0);                                     \
-    mma_step<MT>(fa1, fb1, acc);                                                              \
-    sched_mma_ds<MT>();                                                                       \
-    load_frags<MT>(CA, CB, arow, brow, 6 + fh, fa1, fb1);                                     \
-    mma_step<MT>(fa0, fb0, acc);                                                              \
-    sched_mma_ds<MT>();                                                                       \
-    if (HAS_NEXT) {                                                                           \
-      __builtin_amdgcn_s_waitcnt(kVmcnt0);                                                    \
-      __syncthreads();                                                                        \
-      if (NEXT2) issue(kt + 2, CUR_ST);                                                       \
-      load_frags<MT>(NA, NB, arow, brow, fh, fa0, fb0);                                       \
-    }                                                                                         \
-    mma_step<MT>(fa1, fb1, acc);                                                              \
-  }
-
+  // Prologue: slabs 0..NST-2 in flight, slab 0 landed and visible.
   issue(0, st0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-  if (nk > 1) issue(1, st1);
-  load_frags<MT>(s0a, s0b, arow, brow, fh, fa0, fb0);
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    ZDIT_SLAB(s0a, s0b, s1a, s1b, st0, true, kt + 2 < nk)
-    ++kt;
-    ZDIT_SLAB(s1a, s1b, s0a, s0b, st1, kt + 1 < nk, kt + 2 < nk)
-    --kt;
-  }
-  if (kt < nk) ZDIT_SLAB(s0a, s0b, s1a, s1b, st0, false, false)
-#undef ZDIT_SLAB
+  issue(1, st1);
+  issue(2, st2);
+  __builtin_amdgcn_s_waitcnt(kVmcntRing);
+  barrier_fenced();
+  if (grp == 1) barrier_fenced();  // group 1 runs one phase behind
 
-  // ---- epilogue.  Accumulator (mt, nt) element r of this lane is C[row][col] with
-  // row = 8 (r / 4) + 4 (lane / 32) + r % 4 and col = lane % 32 within the 32 x 32 tile.
-  // Row addressing is resolved once per row; loads of a tile's 16 values are issued together
-  // before any store, so their latencies overlap.
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int64_t roff[16];
-    bool rok[16];
-    int rb[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * (32 * MT) + mt * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      const int mm = min(m, g.M - 1);
-      const RowAddr ro = map_row(g.out, mm);
-      roff[r] = ro.off;
-      rok[r] = (m < g.M) && ro.ok;
-      rb[r] = mm / g.out.rows_per_batch;
-    }
-    if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-      for (int np = 0; np < 2; ++np) {
-        const int n = n0 + wn * 64 + np * 32 + fr;
-        if (n >= g.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (rok[r]) ((bf16*)g.C)[roff[r] + n] = (bf16)(silu(acc[mt][2 * np][r]) * acc[mt][2 * np + 1][r]);
-      }
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 128 + nt * 32 + fr;
-        if (n >= g.N) continue;
-        if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (rok[r]) ((bf16*)g.C)[roff[r] + n] = (bf16)acc[mt][nt][r];
-        } else if constexpr (EPI == EPI_BIAS) {
-          const float bias = g.vec[n];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (rok[r]) ((float*)g.C)[roff[r] + n] = acc[mt][nt][r] + bias;
-        } else {  // EPI_RESID: x += gate * (A B^T)
-          float* C = (float*)g.C;
-          float cur[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) cur[r] = rok[r] ? C[roff[r] + n] : 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (!rok[r]) continue;
-            const float gate = g.vec ? g.vec[rb[r] * g.vec_bstride + n] : 1.0f;
-            C[roff[r] + n] = cur[r] + gate * acc[mt][nt][r];
-          }
-        }
-      }
-    }
+  // One slab: memory phase (read this slab's fragments), barrier, compute phase (the MFMAs,
+  // with this wave's loads of slab kt+NST-1 into the stage freed by slab kt-1 spread between
+  // them), barrier.  Group 0's loads of slab kt+1 are complete after its compute phase of slab
+  // kt, group 1's after its memory phase of slab kt; both before the barrier that precedes
+  // group 0's reads of slab kt+1.
+#define ZDIT_SLAB(CUR, FREE, KT)                                   \
+  {                                                                \
+    read_frags(CUR, arow, brow, fh, f);                            \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                         \
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(kVmcntG1);            \
+    barrier_fenced();                                              \
+    mma_slab(f, acc);                                              \
+    issue((KT) + NST - 1, FREE);                                   \
+    for (int q = 0; q < DMA_PER_WAVE; ++q) {                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           \
+    }                                                              \
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(kVmcntRing);          \
+    if (grp == 0 || (KT) + 1 < nk) barrier_fenced();               \
   }
+
+  // Whole turns of the ring, then the remaining slabs.  (The loop body is branch-free, so the
+  // compiler sees every stage's last load exactly.)
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    ZDIT_SLAB(st0, st3, kt)
+    ZDIT_SLAB(st1, st0, kt + 1)
+    ZDIT_SLAB(st2, st1, kt + 2)
+    ZDIT_SLAB(st3, st2, kt + 3)
+  }
+  if (kt < nk) ZDIT_SLAB(st0, st3, kt)
+  if (kt + 1 < nk) ZDIT_SLAB(st1, st0, kt + 1)
+  if (kt + 2 < nk) ZDIT_SLAB(st2, st1, kt + 2)
+#undef ZDIT_SLAB
+  // Loads of the slabs past the end are still landing in dead stages.  Once every wave has
+  // drained its loads and passed this barrier, the LDS stages are free for the epilogue.
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  barrier_fenced();
+
+  const int sidx = wave >> 1;
+  char* const stg = (char*)(sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3) + (wave & 1) * 16384;
+  epilogue<EPI, 2>(g, acc, m0 + wm * 64, n0 + wn * ((EPI == EPI_SWIGLU) ? 64 : 128), stg, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -370,18 +458,12 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   const int nout_tile = (epi == EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + nout_tile - 1) / nout_tile);
-  dim3 grid(tiles);
-#ifdef ZDIT_GEMM_4WAVE
-  constexpr int W = 4;
-#else
-  constexpr int W = 8;
-#endif
-  dim3 block(64 * W);
+  dim3 grid(tiles), block(512);
   switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, W>), grid, block, 0, s, g); break;
-    case EPI_BIAS: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_BIAS, W>), grid, block, 0, s, g); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_RESID, W>), grid, block, 0, s, g); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, W>), grid, block, 0, s, g); break;
+    case EPI_STORE: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE>, grid, block, 0, s, g); break;
+    case EPI_BIAS: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_BIAS>, grid, block, 0, s, g); break;
+    case EPI_RESID: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_RESID>, grid, block, 0, s, g); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -572,6 +572,7 @@ zdit_status zdit_op_gemm(int32_t precision, int32_t epilogue, int32_t M, int32_t
   if (precision != ZDIT_BF16 && precision != ZDIT_FP32_DEBUG) return fail(ZDIT_EINVAL, "precision %d", precision);
   if (epilogue < ZDIT_EPI_STORE || epilogue > ZDIT_EPI_SWIGLU) return fail(ZDIT_EINVAL, "epilogue %d", epilogue);
   if (M < 0 || N < 1 || K < 1) return fail(ZDIT_EINVAL, "M %d N %d K %d", M, N, K);
+  if (M > (1 << 24)) return fail(ZDIT_EUNSUPPORTED, "M %d (at most 2^24 rows)", M);
   if (precision == ZDIT_BF16 && K % 64) return fail(ZDIT_EUNSUPPORTED, "K %d not a multiple of 64", K);
   if (K % 8) return fail(ZDIT_EUNSUPPORTED, "K %d not a multiple of 8", K);
   if (!A || !B || !C) return fail(ZDIT_EINVAL, "NULL operand");
