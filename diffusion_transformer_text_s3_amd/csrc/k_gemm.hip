@@ -1,14 +1,16 @@
 // Dense contractions of the S3-DiT block on gfx950: C = A B^T with A [M, K] and B [N, K]
 // both K-contiguous (activations [tokens, features] and weights [out, in]).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  One 512-thread workgroup owns a
-// 256 x 256 tile of C; each of its eight wavefronts owns 64 x 128 of it (2 x 4 MFMA tiles,
-// 128 fp32 accumulators per lane).  K advances in 32-wide slabs through a ring of four LDS
-// stages of 32 KB filled by direct-to-LDS buffer loads, issued three slabs ahead.
+// bf16 path: v_mfma_f32_16x16x32_bf16, fp32 accumulation.  One 512-thread workgroup owns a
+// 256 x 256 tile of C; each of its eight wavefronts owns 64 x 128 of it (4 x 8 MFMA tiles of
+// 16 x 16, 128 fp32 accumulators per lane).  K advances in 32-wide slabs (one MFMA k-step)
+// through a ring of four LDS stages of 32 KB filled by direct-to-LDS buffer loads, issued three
+// slabs ahead.  (The 16 x 16 x 32 form moves less accumulator data per flop than 32 x 32 x 16;
+// under the chip's power limit that runs at a higher clock for the same work.)
 //
 // The eight wavefronts form two groups of four, one wave of each group per SIMD (waves w and
 // w + 4 share a SIMD), run half a period apart ("ping-pong"): while one group issues the
-// sixteen MFMAs of a slab (with its share of the global loads spread between them), the other
+// thirty-two MFMAs of a slab (with its share of the global loads spread between them), the other
 // reads the fragments of its next slab from LDS.  A workgroup barrier separates the phases, so
 // each SIMD's matrix pipe is fed by one wave while the other waits on LDS.
 //
@@ -19,9 +21,9 @@
 // get consecutive tiles, and tiles are walked in groups of 8 row-panels, so each XCD's L2
 // sees a compact set of A and B panels.
 //
-// Epilogues run on the accumulators in registers: plain bf16 store (QKV), bias + fp32 store
-// into a branch-strided buffer (embeds, final layer), fp32 gated residual read-modify-write
-// (out projection, w2), and SwiGLU on paired W1 / W3 tiles (w1/w3).  There is no split-K:
+// Epilogues work from the accumulators, staged through LDS into 16-byte row chunks: plain bf16
+// store (QKV), bias + fp32 store into a branch-strided buffer (embeds, final layer), fp32 gated
+// residual read-modify-write (out projection, w2), and SwiGLU on paired W1 / W3 tiles (w1/w3).  There is no split-K:
 // each output's sum runs over K in one fixed order, independent of M and of the tile.
 #include "common.h"
 
@@ -103,50 +105,55 @@ __device__ __forceinline__ void barrier_fenced() {
 }
 
 // Per-wave state of the main loop.
+// v_mfma_f32_16x16x32_bf16: a wave's 64 x 128 is 4 x 8 tiles of 16 x 16; a fragment is 16 rows
+// x 32 k (lane l: row l % 16, k 8 (l / 16) .. + 7), i.e. one whole 32-wide slab.
 struct Frags {
-  bf16x8 a[2][2];  // [k16 step][32-row A tile]
-  bf16x8 b[2][4];  // [k16 step][32-row B tile]
+  bf16x8 a[4];  // [16-row A tile]
+  bf16x8 b[8];  // [16-row B tile]
 };
+typedef f32x4 AccT;
+constexpr int ACC_I = 4, ACC_J = 8;
 
 __device__ __forceinline__ void read_frags(const uint4* st, int arow, int brow, int fh, Frags& f) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int i = 0; i < 4; ++i) f.a[i] = __builtin_bit_cast(bf16x8, st[swz(arow + 16 * i, fh)]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[s][i] = __builtin_bit_cast(bf16x8, st[swz(arow + 32 * i, 2 * s + fh)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[s][j] = __builtin_bit_cast(bf16x8, st[BM * 4 + swz(brow + 32 * j, 2 * s + fh)]);
-  }
+  for (int j = 0; j < 8; ++j) f.b[j] = __builtin_bit_cast(bf16x8, st[BM * 4 + swz(brow + 16 * j, fh)]);
 }
 
-__device__ __forceinline__ void mma_slab(const Frags& f, f32x16 (&acc)[2][4]) {
+__device__ __forceinline__ void mma_slab(const Frags& f, AccT (&acc)[4][8]) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[s][i], f.b[s][j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 8; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Epilogue of one wave: its MT x 4 accumulator tiles cover rows m_wave .. m_wave + 32 MT - 1 and
 // 128 columns from ncol_wave (SwiGLU: 64 output columns, W1 / W3 tiles paired).  stg is this
 // wave's private staging space in LDS (at least 9216 bytes).
-template <int EPI, int MT>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 (&acc)[MT][4], int m_wave, int ncol_wave,
-                                         char* stg, int lane) {
-  const int fr = lane & 31, fh = lane >> 5;
-  // Accumulator (mt, nt) element r of this lane is C[row][col] with
-  // row = 8 (r / 4) + 4 (lane / 32) + r % 4 and col = lane % 32 within the 32 x 32 tile.  Each
-  // wave stages 32 x 64 sub-tiles of its results in its own 16 KB of LDS (row-major, rows
-  // padded so that both the staging writes and the 16-byte read-back are free of bank
-  // conflicts) and writes them out as 16-byte row chunks: fp32 4 values, bf16 8 values per
-  // lane, one row address per chunk.
-  constexpr bool kF32 = (EPI == EPI_BIAS || EPI == EPI_RESID);
-  constexpr int ES = kF32 ? 4 : 2;             // bytes per staged element
-  constexpr int VW = 16 / ES;                  // elements per 16-byte chunk
-  constexpr int CPR = 64 / VW;                 // chunks per 64-wide row
-  constexpr int STRIDE = 64 * ES + 16 * (ES / 2);  // fp32: 288 B, bf16: 144 B
-  constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;  // 64-column sub-tiles per 32-row band
+// Epilogue write-out of one wave's NBAND x 32 rows from m_wave and 64 NSUB columns from
+// ncol_wave (SwiGLU: 64 output columns).  stage(band, sub, stg) writes the 32 x 64 sub-tile into
+// the wave's private LDS staging space stg (row stride 288 B for fp32, 144 B for bf16, at least
+// 9216 bytes); the rows are then written out as 16-byte chunks: fp32 4 values, bf16 8 values
+// per lane, one row address per chunk.  The row padding keeps both the staging writes and the
+// 16-byte read-back free of bank conflicts.
+template <int EPI>
+struct EpiFmt {
+  static constexpr bool kF32 = (EPI == EPI_BIAS || EPI == EPI_RESID);
+  static constexpr int ES = kF32 ? 4 : 2;             // bytes per staged element
+  static constexpr int VW = 16 / ES;                  // elements per 16-byte chunk
+  static constexpr int CPR = 64 / VW;                 // chunks per 64-wide row
+  static constexpr int STRIDE = 64 * ES + 16 * (ES / 2);  // fp32: 288 B, bf16: 144 B
+  static constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;  // 64-column sub-tiles per band
+};
+
+template <int EPI, int NBAND, class Stage>
+__device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int ncol_wave, char* stg, int lane,
+                                             Stage stage) {
+  constexpr bool kF32 = EpiFmt<EPI>::kF32;
+  constexpr int VW = EpiFmt<EPI>::VW, CPR = EpiFmt<EPI>::CPR, STRIDE = EpiFmt<EPI>::STRIDE;
+  constexpr int NSUB = EpiFmt<EPI>::NSUB;
   const int rpb = g.out.rows_per_batch;
   const float rinv = 1.0f / (float)rpb;
   // 16-byte row chunks need 16-byte aligned rows
@@ -154,25 +161,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 (&acc)[
                       (EPI != EPI_RESID || g.vec == nullptr || (g.vec_bstride % VW == 0 && ((uintptr_t)g.vec & 15) == 0)) &&
                       (EPI != EPI_BIAS || ((uintptr_t)g.vec & 15) == 0);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < NBAND; ++mt) {
 #pragma unroll
     for (int p = 0; p < NSUB; ++p) {
-      // stage: half h covers columns h*32 .. h*32+31 of the sub-tile
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
-          char* dst = stg + row * STRIDE + (h * 32 + fr) * ES;
-          if constexpr (EPI == EPI_SWIGLU) {
-            *(bf16*)dst = (bf16)(silu_fast(acc[mt][2 * h][r]) * acc[mt][2 * h + 1][r]);
-          } else if constexpr (EPI == EPI_STORE) {
-            *(bf16*)dst = (bf16)acc[mt][2 * p + h][r];
-          } else {
-            *(float*)dst = acc[mt][2 * p + h][r];
-          }
-        }
-      }
+      stage(mt, p, stg);
       const int ncol0 = ncol_wave + p * 64;
       constexpr int NIT = 32 * CPR / 64;
       // addresses of this lane's chunks; all global loads are issued before any is used
@@ -255,6 +247,38 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 (&acc)[
 }
 
 
+// Epilogue from 16 x 16 MFMA accumulators of a 16 NI x 128 wave tile: tile (i, j) element r of
+// this lane is C[4 (lane / 16) + r][lane % 16] within the tile.  For SwiGLU, B tiles j and j + 2
+// (j % 4 < 2) are the W1 and W3 rows of the same 16 outputs.
+template <int EPI, int NI>
+__device__ __forceinline__ void epilogue16(const GemmArgs& g, const f32x4 (&acc)[NI][8], int m_wave, int ncol_wave,
+                                           char* stg, int lane) {
+  const int c16 = lane & 15, q4 = lane >> 4;
+  constexpr int ES = EpiFmt<EPI>::ES, STRIDE = EpiFmt<EPI>::STRIDE;
+  epilogue_out<EPI, NI / 2>(g, m_wave, ncol_wave, stg, lane, [&](int mt, int p, char* st) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = ii * 16 + 4 * q4 + r;
+          char* dst = st + row * STRIDE + (jj * 16 + c16) * ES;
+          const int i = 2 * mt + ii;
+          if constexpr (EPI == EPI_SWIGLU) {
+            const int j1 = (jj >> 1) * 4 + (jj & 1);
+            *(bf16*)dst = (bf16)(silu_fast(acc[i][j1][r]) * acc[i][j1 + 2][r]);
+          } else if constexpr (EPI == EPI_STORE) {
+            *(bf16*)dst = (bf16)acc[i][4 * p + jj][r];
+          } else {
+            *(float*)dst = acc[i][4 * p + jj][r];
+          }
+        }
+      }
+    }
+  });
+}
+
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   // one object per stage, so LDS reads of one stage are not ordered behind the in-flight
@@ -321,15 +345,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
     for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma_16(drs[i], stage + dma_dst + i * 64, voff[i], kb);
   };
 
-  f32x16 acc[2][4];
+  AccT acc[ACC_I][ACC_J];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < ACC_J; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < (int)(sizeof(AccT) / 4); ++r) acc[i][j][r] = 0.f;
 
-  const int fr = lane & 31, fh = lane >> 5;
+  const int fr = lane & 15, fh = lane >> 4;  // fragment row, 8-wide k group
   const int arow = wm * 64 + fr, brow = wn * 128 + fr;
   Frags f;
 
@@ -355,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
     mma_slab(f, acc);                                              \
     issue((KT) + NST - 1, FREE);                                   \
     for (int q = 0; q < DMA_PER_WAVE; ++q) {                       \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);           \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           \
     }                                                              \
     if (grp == 0) __builtin_amdgcn_s_waitcnt(kVmcntRing);          \
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int sidx = wave >> 1;
   char* const stg = (char*)(sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3) + (wave & 1) * 16384;
-  epilogue<EPI, 2>(g, acc, m0 + wm * 64, n0 + wn * ((EPI == EPI_SWIGLU) ? 64 : 128), stg, lane);
+  epilogue16<EPI, 4>(g, acc, m0 + wm * 64, n0 + wn * ((EPI == EPI_SWIGLU) ? 64 : 128), stg, lane);
 }
 
 // ---------------------------------------------------------------------------------------
