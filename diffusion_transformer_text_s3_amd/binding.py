@@ -24,7 +24,7 @@ EXPORTS = [
     "zdit_last_error", "zdit_abi_version", "zdit_block_workspace", "zdit_block_fwd",
     "zdit_stack_workspace", "zdit_stack_fwd", "zdit_sigmas", "zdit_n_cap", "zdit_euler_step",
     "zdit_sample_workspace", "zdit_sample", "zdit_rope_tables", "zdit_op_gemm",
-    "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn",
+    "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn", "zdit_op_qkv_attn",
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
 ]
 
@@ -98,6 +98,7 @@ def lib():
             "zdit_op_rope": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, vp]),
             "zdit_op_attn_workspace": (sz, [i32, i32, i32, i32]),
             "zdit_op_attn": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
+            "zdit_op_qkv_attn": (i32, [i32, i32, i32, pi32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "zdit_op_patchify": (i32, [i32, i32, i32, i32, vp, i64, vp, vp]),
             "zdit_op_unpatchify": (i32, [i32, i32, i32, i32, vp, vp, vp]),
             "zdit_op_cap_pad": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp]),
@@ -315,6 +316,11 @@ def zdit_op_attn_workspace(precision, batch, s_max, n_heads) -> int:
 def zdit_op_attn(precision, batch, s_max, n_heads, seq_len, qkv, out, ws, stream=None):
     return check(lib().zdit_op_attn(precision, batch, s_max, n_heads, i32_array(seq_len), ptr(qkv), ptr(out),
                                     ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_qkv_attn(batch, s_max, n_heads, seq_len, h, w_qkv, cos, sin, qkv, out, ws, stream=None):
+    return check(lib().zdit_op_qkv_attn(batch, s_max, n_heads, i32_array(seq_len), ptr(h), ptr(w_qkv), ptr(cos),
+                                        ptr(sin), ptr(qkv), ptr(out), ptr(ws), ws.numel(), stream_handle(stream)))
 
 
 def zdit_op_patchify(batch, Cch, h, w, lat, lat_batch_stride, tokens, stream=None):

@@ -25,7 +25,10 @@ struct RowMap {
   int valid[kMaxBatch];
 };
 
-enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_RESID = 2, EPI_SWIGLU = 3 };
+// EPI_QKV: the fused q/k/v projection of a block (bf16 only): q and k columns are rotated by
+// RoPE on rows below seq[b] and stored, v columns are not stored in C but written transposed
+// into vt (see k_attn.hip for its layout), zero on rows at or past seq[b].
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
 
 struct GemmArgs {
   const void* A;
@@ -37,6 +40,14 @@ struct GemmArgs {
   int M, N, K;
   int64_t lda, ldb;
   RowMap out;
+  // EPI_QKV only: RoPE tables [batch][rows_per_batch][64] (rope_bstride floats between
+  // branches), valid rows per branch, V^T destination [batch][n_heads][128][vt_pad]
+  const float* rope_cos;
+  const float* rope_sin;
+  int64_t rope_bstride;
+  void* vt;
+  int vt_pad, n_heads;
+  int seq[kMaxBatch];
 };
 
 // ---- launchers (return hipError_t of the launch) ----
@@ -48,10 +59,14 @@ struct AttnArgs {
   void* vt;          // bf16 path: [B, nh, 128, s_pad] transposed values (workspace)
   void* out;         // [B, s_max, D]
   int batch, s_max, s_pad, n_heads;
+  int vt_ready;      // vt already holds V^T (written by the QKV GEMM epilogue)
   int seq_len[kMaxBatch];
 };
 size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads);
 hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s);
+// Zero V^T tokens s_max .. s_pad - 1 of every (branch, head, dim) row (after the QKV epilogue
+// wrote tokens below s_max).
+hipError_t launch_vt_tail_zero(const AttnArgs& a, hipStream_t s);
 
 // Row r of branch b is x + b * x_bstride + r * dim; out is compact [batch * rows, dim].
 // shift / scale: fp32 [dim] vectors of branch 0, branch b at + b * mod_bstride; both NULL

@@ -58,6 +58,18 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
   }
 }
 
+// V^T tokens s_max .. s_pad - 1 (past every branch's rows) read as zero keys: one thread per
+// 16-byte chunk of those columns in every (branch, head, dim) row.
+__global__ __launch_bounds__(256) void vt_tail_zero_kernel(AttnArgs a) {
+  const int tail = (a.s_pad - a.s_max) >> 3;  // chunks per row
+  const int64_t rows = (int64_t)a.batch * a.n_heads * kHeadDim;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * tail) return;
+  const int64_t row = i / tail;
+  const int c = (int)(i % tail);
+  *(uint4*)((bf16*)a.vt + row * a.s_pad + a.s_max + c * 8) = make_uint4(0, 0, 0, 0);
+}
+
 // 8 wavefronts x 32 queries = 256 queries per workgroup (two wavefronts per SIMD, so one's
 // softmax can overlap the other's MFMAs).  K and V^T key blocks are double-buffered in LDS and
 // fetched with direct-to-LDS buffer loads one block ahead (no staging registers).  Per key
@@ -332,9 +344,17 @@ size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads) {
   return (size_t)batch * n_heads * kHeadDim * s_pad * sizeof(bf16);
 }
 
+hipError_t launch_vt_tail_zero(const AttnArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.batch * a.n_heads * kHeadDim * ((a.s_pad - a.s_max) >> 3);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(vt_tail_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s) {
   if (precision == 0) {
-    hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_heads, a.batch), dim3(256), 0, s, a);
+    if (!a.vt_ready)
+      hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_heads, a.batch), dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(((a.s_max + QTILE - 1) / QTILE) * a.n_heads * a.batch),
                        dim3(ATT_NT), 0, s, a);
   } else {

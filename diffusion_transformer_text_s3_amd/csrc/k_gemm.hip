@@ -148,6 +148,28 @@ struct EpiFmt {
   static constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;  // 64-column sub-tiles per band
 };
 
+// RoPE on 4 (x0, x1) pairs of a bf16 q or k chunk: y0 = x0 c - x1 s, y1 = x0 s + x1 c in fp32,
+// each product and sum rounded (no contraction), then rounded to bf16 -- the same arithmetic
+// as the stand-alone RoPE kernel.
+__device__ __forceinline__ uint4 rope_chunk(uint4 v, float4 c4, float4 s4) {
+#pragma clang fp contract(off)
+  const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+  const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+  const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
+  bf16x8 y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = (float)x[2 * i], x1 = (float)x[2 * i + 1];
+    const float p0 = x0 * cc[i];
+    const float p1 = x1 * ss[i];
+    const float p2 = x0 * ss[i];
+    const float p3 = x1 * cc[i];
+    y[2 * i] = (bf16)(p0 - p1);
+    y[2 * i + 1] = (bf16)(p2 + p3);
+  }
+  return __builtin_bit_cast(uint4, y);
+}
+
 template <int EPI, int NBAND, class Stage>
 __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int ncol_wave, char* stg, int lane,
                                              Stage stage) {
@@ -166,10 +188,39 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
     for (int p = 0; p < NSUB; ++p) {
       stage(mt, p, stg);
       const int ncol0 = ncol_wave + p * 64;
+      if constexpr (EPI == EPI_QKV) {
+        // v columns: the 32 rows of the sub-tile are 32 consecutive tokens of one branch
+        // (rows per branch are a multiple of 32); write them transposed into V^T, 8 keys per
+        // 16-byte chunk in the attention kernel's key order (chunk 2q of a 16-key group holds
+        // keys 0-3 and 8-11, chunk 2q + 1 keys 4-7 and 12-15), zero at or past seq[b].
+        const int D = g.N / 3;
+        if (ncol0 >= 2 * D) {
+          const int mrow = m_wave + mt * 32;
+          if (mrow >= g.M || ncol0 >= g.N) continue;  // rows past M, columns past the last head
+          const int b0 = div_rows(mrow, rpb, rinv), t0 = mrow - b0 * rpb;
+          const int hd = (ncol0 - 2 * D) >> 7, d0 = (ncol0 - 2 * D) & 127;
+          bf16* vt = (bf16*)g.vt + ((int64_t)(b0 * g.n_heads + hd) * kHeadDim + d0) * g.vt_pad + t0;
+          const int sq = g.seq[b0];
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int c = it * 64 + lane, d = c >> 2, ch = c & 3;
+            const int kb = (ch >> 1) * 16 + (ch & 1) * 4;
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int t = kb + (e & 3) + 8 * (e >> 2);
+              const bf16 val = *(const bf16*)(stg + t * STRIDE + d * 2);
+              o[e] = (t0 + t < sq) ? val : (bf16)0.f;
+            }
+            *(bf16x8*)(vt + (int64_t)d * g.vt_pad + ch * 8) = o;
+          }
+          continue;
+        }
+      }
       constexpr int NIT = 32 * CPR / 64;
       // addresses of this lane's chunks; all global loads are issued before any is used
       int64_t off[NIT];
-      int nn[NIT], bq[NIT];
+      int nn[NIT], bq[NIT], rq[NIT];
       bool ok[NIT], full[NIT];
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
@@ -179,6 +230,7 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
         const int mm = min(m, g.M - 1);
         bq[it] = div_rows(mm, rpb, rinv);
         const int rr = mm - bq[it] * rpb;
+        rq[it] = rr;
         ok[it] = m < g.M && nn[it] < g.N && rr < g.out.valid[bq[it]];
         off[it] = bq[it] * g.out.batch_stride + (int64_t)rr * g.out.ld + nn[it];
         full[it] = vec_ok && nn[it] + VW <= g.N;
@@ -231,6 +283,15 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
             } else {
               for (int e = 0; e < VW && n + e < g.N; ++e) C[e] = vf[e] + g.vec[n + e];
             }
+          } else if constexpr (EPI == EPI_QKV) {
+            // q / k columns (rows per branch, head dim and N are multiples of 8: always full)
+            const int b = bq[it], rr = rq[it];
+            uint4 y = v;
+            if (rr < g.seq[b]) {
+              const int64_t toff = b * g.rope_bstride + (int64_t)rr * 64 + ((n & 127) >> 1);
+              y = rope_chunk(v, *(const float4*)(g.rope_cos + toff), *(const float4*)(g.rope_sin + toff));
+            }
+            *(uint4*)((bf16*)g.C + off[it]) = y;
           } else {
             bf16* C = (bf16*)g.C + off[it];
             if (full[it]) {
@@ -268,7 +329,7 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& g, const f32x4 (&acc)
           if constexpr (EPI == EPI_SWIGLU) {
             const int j1 = (jj >> 1) * 4 + (jj & 1);
             *(bf16*)dst = (bf16)(silu_fast(acc[i][j1][r]) * acc[i][j1 + 2][r]);
-          } else if constexpr (EPI == EPI_STORE) {
+          } else if constexpr (EPI == EPI_STORE || EPI == EPI_QKV) {
             *(bf16*)dst = (bf16)acc[i][4 * p + jj][r];
           } else {
             *(float*)dst = acc[i][4 * p + jj][r];
@@ -488,6 +549,7 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s) {
     case EPI_BIAS: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_BIAS>, grid, block, 0, s, g); break;
     case EPI_RESID: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_RESID>, grid, block, 0, s, g); break;
     case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, s, g); break;
+    case EPI_QKV: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_QKV>, grid, block, 0, s, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -99,6 +99,42 @@ hipError_t gemm(int precision, int epi, const GemmArgs& g, hipStream_t s) {
   return precision == ZDIT_BF16 ? launch_gemm_bf16(epi, g, s) : launch_gemm_f32(epi, g, s);
 }
 
+// q, k, v projection of h [B * s, nh * 128] (rows of branch b at b * s), RoPE on q and k,
+// and joint attention into o.  In bf16 with s % 32 == 0 the projection's epilogue rotates q, k
+// and writes V^T itself (one kernel instead of GEMM + RoPE + transpose); otherwise the GEMM
+// stores q, k, v and separate kernels rotate and transpose.  The results are bit-identical.
+zdit_status qkv_attention(int P, int nh, int B, int s, const int* seq_len, const void* h, const void* w_qkv,
+                          void* qkv, void* vt, void* o, const float* cosT, const float* sinT,
+                          int64_t tab_bstride, hipStream_t st) {
+  const int D = nh * kHeadDim, M = B * s;
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.vt = vt; aa.out = o; aa.batch = B; aa.s_max = s; aa.s_pad = round_up(s, 64);
+  aa.n_heads = nh;
+  for (int b = 0; b < kMaxBatch; ++b) aa.seq_len[b] = b < B ? seq_len[b] : 0;
+
+  GemmArgs g{};
+  g.A = h; g.B = w_qkv; g.C = qkv; g.M = M; g.N = 3 * D; g.K = D; g.lda = D; g.ldb = D;
+  if (P == ZDIT_BF16 && s % 32 == 0) {
+    g.out.rows_per_batch = s; g.out.batch_stride = (int64_t)s * 3 * D; g.out.ld = 3 * D;
+    for (int b = 0; b < kMaxBatch; ++b) { g.out.valid[b] = b < B ? s : 0; g.seq[b] = b < B ? seq_len[b] : 0; }
+    g.rope_cos = cosT; g.rope_sin = sinT; g.rope_bstride = tab_bstride;
+    g.vt = vt; g.vt_pad = aa.s_pad; g.n_heads = nh;
+    HIP_TRY(launch_gemm_bf16(EPI_QKV, g, st));
+    HIP_TRY(launch_vt_tail_zero(aa, st));
+    aa.vt_ready = 1;
+  } else {
+    g.out = compact_rows(M, 3LL * D);
+    HIP_TRY(gemm(P, EPI_STORE, g, st));
+    RopeArgs ra;
+    ra.qkv = qkv; ra.cos = cosT; ra.sin = sinT; ra.tab_bstride = tab_bstride;
+    ra.batch = B; ra.s_max = s; ra.n_heads = nh;
+    for (int b = 0; b < kMaxBatch; ++b) ra.seq_len[b] = b < B ? seq_len[b] : 0;
+    HIP_TRY(launch_rope(P, ra, st));
+  }
+  HIP_TRY(launch_attn(P, aa, st));
+  return ZDIT_OK;
+}
+
 // One block on B branches of s rows each.  x rows are x + b * x_bstride + r * dim.
 // mod: [B][6][dim] fp32 already computed, or NULL (no adaLN).
 zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int s,
@@ -121,28 +157,17 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
   for (int b = 0; b < kMaxBatch; ++b) na.valid[b] = b < B ? seq_len[b] : 0;
   HIP_TRY(launch_rmsnorm_mod(P, na, st));
 
-  GemmArgs g{};
-  g.A = h; g.B = w.w_qkv; g.C = qkv; g.M = M; g.N = 3 * D; g.K = D; g.lda = D; g.ldb = D;
-  g.out = compact_rows(M, 3LL * D);
-  HIP_TRY(gemm(P, EPI_STORE, g, st));
-
-  RopeArgs ra;
-  ra.qkv = qkv; ra.cos = cosT; ra.sin = sinT; ra.tab_bstride = tab_bstride;
-  ra.batch = B; ra.s_max = s; ra.n_heads = d.n_heads;
-  for (int b = 0; b < kMaxBatch; ++b) ra.seq_len[b] = b < B ? seq_len[b] : 0;
-  HIP_TRY(launch_rope(P, ra, st));
-
-  AttnArgs aa;
-  aa.qkv = qkv; aa.vt = vt; aa.out = o; aa.batch = B; aa.s_max = s; aa.s_pad = round_up(s, 64);
-  aa.n_heads = d.n_heads;
-  for (int b = 0; b < kMaxBatch; ++b) aa.seq_len[b] = b < B ? seq_len[b] : 0;
-  HIP_TRY(launch_attn(P, aa, st));
+  {
+    const zdit_status rc = qkv_attention(P, d.n_heads, B, s, seq_len, h, w.w_qkv, qkv, vt, o, cosT, sinT,
+                                         tab_bstride, st);
+    if (rc != ZDIT_OK) return rc;
+  }
 
   RowMap xr;
   xr.rows_per_batch = s; xr.batch_stride = x_bstride; xr.ld = D;
   for (int b = 0; b < kMaxBatch; ++b) xr.valid[b] = b < B ? seq_len[b] : 0;
 
-  g = GemmArgs{};
+  GemmArgs g{};
   g.A = o; g.B = w.w_out; g.C = x; g.M = M; g.N = D; g.K = D; g.lda = D; g.ldb = D;
   g.vec = mod ? mod + 2LL * D : nullptr; g.vec_bstride = 6LL * D; g.out = xr;
   HIP_TRY(gemm(P, EPI_RESID, g, st));
@@ -630,12 +655,31 @@ zdit_status zdit_op_attn(int32_t precision, int32_t batch, int32_t s_max, int32_
     if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d", b, seq_len[b]);
   if (ws_bytes < zdit_op_attn_workspace(precision, batch, s_max, n_heads) || (precision == ZDIT_BF16 && !ws))
     return fail(ZDIT_EWORKSPACE, "workspace too small");
-  AttnArgs aa;
+  AttnArgs aa{};
   aa.qkv = qkv; aa.vt = ws; aa.out = out; aa.batch = batch; aa.s_max = s_max; aa.s_pad = round_up(s_max, 64);
   aa.n_heads = n_heads;
   for (int b = 0; b < kMaxBatch; ++b) aa.seq_len[b] = b < batch ? seq_len[b] : 0;
   HIP_TRY(launch_attn(precision, aa, (hipStream_t)hip_stream));
   return ok();
+}
+
+zdit_status zdit_op_qkv_attn(int32_t batch, int32_t s_max, int32_t n_heads, const int32_t* seq_len, const void* h,
+                             const void* w_qkv, const float* cos, const float* sin, void* qkv, void* out, void* ws,
+                             size_t ws_bytes, void* hip_stream) {
+  if (batch < 1 || batch > ZDIT_MAX_BATCH || s_max < 1 || n_heads < 1) return fail(ZDIT_EINVAL, "batch/s_max/n_heads");
+  if (s_max % 32) return fail(ZDIT_EUNSUPPORTED, "s_max %d not a multiple of 32", s_max);
+  if (n_heads > 32 || !seq_fits(s_max, n_heads * kHeadDim) || (int64_t)batch * s_max > (1 << 24))
+    return fail(ZDIT_EUNSUPPORTED, "s_max %d / n_heads %d too large", s_max, n_heads);
+  if (!seq_len || !h || !w_qkv || !cos || !sin || !qkv || !out) return fail(ZDIT_EINVAL, "NULL pointer argument");
+  if (!aligned16(h) || !aligned16(w_qkv) || !aligned16(cos) || !aligned16(sin) || !aligned16(qkv) || !aligned16(out))
+    return fail(ZDIT_EINVAL, "pointer not 16-byte aligned");
+  for (int b = 0; b < batch; ++b)
+    if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d", b, seq_len[b]);
+  if (!ws || !aligned16(ws) || ws_bytes < zdit_op_attn_workspace(ZDIT_BF16, batch, s_max, n_heads))
+    return fail(ZDIT_EWORKSPACE, "workspace too small");
+  const zdit_status rc = qkv_attention(ZDIT_BF16, n_heads, batch, s_max, seq_len, h, w_qkv, qkv, ws, out, cos, sin,
+                                       (int64_t)s_max * 64, (hipStream_t)hip_stream);
+  return rc == ZDIT_OK ? ok() : rc;
 }
 
 zdit_status zdit_op_patchify(int32_t batch, int32_t C, int32_t h, int32_t w, const float* lat,

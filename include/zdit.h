@@ -273,6 +273,18 @@ zdit_status zdit_op_attn(int32_t precision, int32_t batch, int32_t s_max, int32_
                          const int32_t* seq_len, const void* qkv, void* out, void* ws,
                          size_t ws_bytes, void* hip_stream);
 
+/* The block's attention half in its fused bf16 form: qkv = h W_qkv^T with q and k rotated by
+ * RoPE (rows < seq_len[b]; tables [batch, s_max, 64]) in the projection's epilogue, V
+ * transposed by that epilogue into the workspace, then joint attention into out [batch,
+ * s_max, n_heads * 128] as zdit_op_attn.  h bf16 [batch * s_max, n_heads * 128], w_qkv bf16
+ * [3 * n_heads * 128, n_heads * 128]; the v columns of qkv [batch, s_max, 3 * n_heads * 128]
+ * are not written.  s_max % 32 == 0 (else ZDIT_EUNSUPPORTED); ws: zdit_op_attn_workspace(
+ * ZDIT_BF16, ...) bytes, 16-byte aligned.  Bit-identical to zdit_op_gemm (ZDIT_EPI_STORE) +
+ * zdit_op_rope + zdit_op_attn on the same inputs. */
+zdit_status zdit_op_qkv_attn(int32_t batch, int32_t s_max, int32_t n_heads, const int32_t* seq_len,
+                             const void* h, const void* w_qkv, const float* cos, const float* sin,
+                             void* qkv, void* out, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Patchify latents [batch, C, h, w] (branch stride lat_batch_stride floats) into fp32 tokens
  * [batch, (h/2)(w/2), 4C], token r*(w/2)+c, feature (dy*2 + dx)*C + ch. */
 zdit_status zdit_op_patchify(int32_t batch, int32_t C, int32_t h, int32_t w, const float* lat,

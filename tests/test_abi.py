@@ -104,6 +104,23 @@ def test_block_fwd_rejects_bad_arguments_before_launch():
     assert rc == Z.ZDIT_EUNSUPPORTED
 
 
+def test_fused_qkv_attn_validates_before_launch():
+    L = Z.lib()
+    p = _fake()
+    seq = Z.i32_array([96])
+    # s_max not a multiple of 32
+    rc = L.zdit_op_qkv_attn(1, 100, 2, Z.i32_array([100]), p, p, p, p, p, p, p, 1 << 30, None)
+    assert rc == Z.ZDIT_EUNSUPPORTED and "multiple of 32" in Z.last_error()
+    # seq_len outside 1..s_max
+    rc = L.zdit_op_qkv_attn(1, 96, 2, Z.i32_array([97]), p, p, p, p, p, p, p, 1 << 30, None)
+    assert rc == Z.ZDIT_EINVAL and "seq_len" in Z.last_error()
+    # misaligned operand, then a workspace too small
+    rc = L.zdit_op_qkv_attn(1, 96, 2, seq, _fake((1 << 20) + 2), p, p, p, p, p, p, 1 << 30, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
+    rc = L.zdit_op_qkv_attn(1, 96, 2, seq, p, p, p, p, p, p, p, 1024, None)
+    assert rc == Z.ZDIT_EWORKSPACE
+
+
 def test_euler_step_rejects_missing_uncond_with_guidance():
     L = Z.lib()
     p = _fake()

@@ -288,6 +288,40 @@ def test_attention_full_size_sampled_queries():
         assert np.all(got[b, seq[b]:] == 0)
 
 
+@pytest.mark.parametrize("B,S,nh,seq", [(2, 160, 3, [160, 131]), (1, 96, 2, [57]), (2, 4160, 30, [4160, 4128])])
+def test_fused_qkv_rope_vt_bit_identical_to_separate_kernels(B, S, nh, seq):
+    """The projection epilogue that rotates q, k and writes V^T reproduces GEMM + RoPE kernel +
+    transpose kernel bit for bit: rotated q, k columns and the attention output."""
+    note(f"fused qkv/rope/vt B={B} S={S} nh={nh} seq={seq}")
+    D = nh * 128
+    g = _rng(31 + S)
+    h = bf16_values(g.standard_normal((B * S, D)).astype(np.float32))
+    w = bf16_values((0.05 * g.standard_normal((3 * D, D))).astype(np.float32))
+    cos = np.ones((B, S, 64), np.float32)
+    sin = np.zeros((B, S, 64), np.float32)
+    gh = 8 if S < 1000 else 64
+    for b in range(B):
+        c_, s_ = O.rope_tables(O.position_ids("joint", gh, gh, S - gh * gh))
+        cos[b], sin[b] = c_[:S], s_[:S]
+    ht, wt = dev(h, torch.bfloat16), dev(w, torch.bfloat16)
+    ct, st = dev(cos), dev(sin)
+    # separate kernels
+    q1 = torch.empty((B * S, 3 * D), dtype=torch.bfloat16, device="cuda")
+    Z.zdit_op_gemm(BF, Z.ZDIT_EPI_STORE, B * S, 3 * D, D, ht, wt, None, None, q1)
+    Z.zdit_op_rope(BF, B, S, nh, seq, q1, ct, st)
+    o1 = torch.empty((B, S, D), dtype=torch.bfloat16, device="cuda")
+    ws1 = Z.workspace(Z.zdit_op_attn_workspace(BF, B, S, nh))
+    Z.zdit_op_attn(BF, B, S, nh, seq, q1, o1, ws1)
+    # fused; poison the workspace and the v columns first: neither may leak into the result
+    q2 = torch.full((B * S, 3 * D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty((B, S, D), dtype=torch.bfloat16, device="cuda")
+    ws2 = Z.workspace(Z.zdit_op_attn_workspace(BF, B, S, nh))
+    ws2.fill_(0xFF)
+    Z.zdit_op_qkv_attn(B, S, nh, seq, ht, wt, ct, st, q2, o2, ws2)
+    np.testing.assert_array_equal(host(q2)[:, :2 * D], host(q1)[:, :2 * D])
+    np.testing.assert_array_equal(host(o2), host(o1))
+
+
 # ------------------------------------------------------------------------------- index work
 def test_patchify_unpatchify_bit_exact():
     B, C, h, w = 2, 16, 32, 48
