@@ -181,14 +181,14 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int i = 0; i < 2; ++i) att_dma_16(vrs, dst + (wave * 2 + i) * 64, vvo[i], t * KT * 2);
   };
   auto qk = [&](const uint4* Kb, f32x16 (&st)[2]) {
+    const f32x16 zero = {};
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[t2][r] = 0.f;
-#pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, Kb[k_slot(t2 * 32 + fr, 2 * s + fh)]);
-        st[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[t2], 0, 0, 0);
+        // the first k-step starts from a zero accumulator operand (no register clearing)
+        st[t2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s == 0 ? zero : st[t2], 0, 0, 0);
       }
     }
   };

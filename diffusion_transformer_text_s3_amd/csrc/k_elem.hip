@@ -27,64 +27,75 @@ template <> __device__ __forceinline__ float from_act<bf16>(bf16 v) { return (fl
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------------------------------
-// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift; one wavefront per row, the row kept
-// in registers (dim <= 4096: at most 16 float4 per lane).
+// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift.  A workgroup of 4 wavefronts takes 16
+// rows of one branch; gain, shift and scale of that branch are staged in LDS once, then each
+// wavefront normalises 4 rows, one at a time, keeping the row in registers (dim <= 4096: at
+// most 16 float4 per lane).
 // ---------------------------------------------------------------------------------------
 constexpr int kNormMaxChunks = 16;
+constexpr int kNormRowsPerBlock = 16;
 
 template <typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(NormArgs a) {
+  __shared__ float4 vg[1024], vsh[1024], vsc[1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * 4 + wave;
-  if (m >= (int64_t)a.batch * a.rows_per_batch) return;
-  const int b = (int)(m / a.rows_per_batch), r = (int)(m % a.rows_per_batch);
+  const int b = blockIdx.y;
   const int nchunk = a.dim >> 2;
-  TO* out = (TO*)a.out + m * a.dim;
-  if (r >= a.valid[b]) {
-    for (int c = lane; c < nchunk; c += 64) {
-      out[4 * c + 0] = to_act<TO>(0.f); out[4 * c + 1] = to_act<TO>(0.f);
-      out[4 * c + 2] = to_act<TO>(0.f); out[4 * c + 3] = to_act<TO>(0.f);
-    }
-    return;
-  }
-  const float4* x = (const float4*)(a.x + b * a.x_bstride + (int64_t)r * a.dim);
-  float4 v[kNormMaxChunks];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < kNormMaxChunks; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nchunk) {
-      v[j] = x[c];
-      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  const bool mod = a.shift != nullptr;
+  {
+    const float4* g = (const float4*)a.gain;
+    const float4* sh = mod ? (const float4*)(a.shift + b * a.mod_bstride) : nullptr;
+    const float4* sc = mod ? (const float4*)(a.scale + b * a.mod_bstride) : nullptr;
+    for (int c = threadIdx.x; c < nchunk; c += 256) {
+      vg[c] = g[c];
+      if (mod) { vsh[c] = sh[c]; vsc[c] = sc[c]; }
     }
   }
-  ss = wave_sum(ss);
-  const float rinv = 1.0f / sqrtf(ss / (float)a.dim + a.eps);
-  const float4* g = (const float4*)a.gain;
-  const float4* sh = nullptr;
-  const float4* sc = nullptr;
-  if (a.shift) {
-    sh = (const float4*)(a.shift + b * a.mod_bstride);
-    sc = (const float4*)(a.scale + b * a.mod_bstride);
-  }
-#pragma unroll
-  for (int j = 0; j < kNormMaxChunks; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nchunk) {
-      float4 gg = g[c];
-      float4 o;
-      o.x = v[j].x * rinv * gg.x; o.y = v[j].y * rinv * gg.y;
-      o.z = v[j].z * rinv * gg.z; o.w = v[j].w * rinv * gg.w;
-      if (sh) {
-        float4 s1 = sh[c], s2 = sc[c];
-        o.x = o.x * (1.f + s2.x) + s1.x; o.y = o.y * (1.f + s2.y) + s1.y;
-        o.z = o.z * (1.f + s2.z) + s1.z; o.w = o.w * (1.f + s2.w) + s1.w;
+  __syncthreads();
+  for (int i = 0; i < kNormRowsPerBlock / 4; ++i) {
+    const int r = blockIdx.x * kNormRowsPerBlock + i * 4 + wave;
+    if (r >= a.rows_per_batch) break;
+    const int64_t m = (int64_t)b * a.rows_per_batch + r;
+    TO* out = (TO*)a.out + m * a.dim;
+    if (r >= a.valid[b]) {
+      for (int c = lane; c < nchunk; c += 64) {
+        out[4 * c + 0] = to_act<TO>(0.f); out[4 * c + 1] = to_act<TO>(0.f);
+        out[4 * c + 2] = to_act<TO>(0.f); out[4 * c + 3] = to_act<TO>(0.f);
       }
-      if constexpr (sizeof(TO) == 2) {
-        bf16x4 ob = {(bf16)o.x, (bf16)o.y, (bf16)o.z, (bf16)o.w};
-        *(bf16x4*)(out + 4 * c) = ob;
-      } else {
-        *(float4*)(out + 4 * c) = o;
+      continue;
+    }
+    const float4* x = (const float4*)(a.x + b * a.x_bstride + (int64_t)r * a.dim);
+    float4 v[kNormMaxChunks];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kNormMaxChunks; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        v[j] = x[c];
+        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+      }
+    }
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss / (float)a.dim + a.eps);
+#pragma unroll
+    for (int j = 0; j < kNormMaxChunks; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nchunk) {
+        const float4 gg = vg[c];
+        float4 o;
+        o.x = v[j].x * rinv * gg.x; o.y = v[j].y * rinv * gg.y;
+        o.z = v[j].z * rinv * gg.z; o.w = v[j].w * rinv * gg.w;
+        if (mod) {
+          const float4 s1 = vsh[c], s2 = vsc[c];
+          o.x = o.x * (1.f + s2.x) + s1.x; o.y = o.y * (1.f + s2.y) + s1.y;
+          o.z = o.z * (1.f + s2.z) + s1.z; o.w = o.w * (1.f + s2.w) + s1.w;
+        }
+        if constexpr (sizeof(TO) == 2) {
+          bf16x4 ob = {(bf16)o.x, (bf16)o.y, (bf16)o.z, (bf16)o.w};
+          *(bf16x4*)(out + 4 * c) = ob;
+        } else {
+          *(float4*)(out + 4 * c) = o;
+        }
       }
     }
   }
@@ -349,7 +360,7 @@ inline unsigned blocks_for(int64_t n, int per = 256) { return (unsigned)((n + pe
 hipError_t launch_rmsnorm_mod(int precision, const NormArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.rows_per_batch;
   if (rows == 0) return hipSuccess;
-  dim3 grid(blocks_for(rows, 4));
+  dim3 grid((a.rows_per_batch + kNormRowsPerBlock - 1) / kNormRowsPerBlock, a.batch);
   if (precision == 0) hipLaunchKernelGGL(rmsnorm_mod_kernel<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(rmsnorm_mod_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
