@@ -236,35 +236,37 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
         full[it] = vec_ok && nn[it] + VW <= g.N;
       }
       if constexpr (EPI == EPI_RESID) {
-        // two batches of four chunks: loads of a batch are all in flight before the first use
+        // All eight x chunks of the lane are in flight before the first use.  A lane's column
+        // chunk is the same in every iteration, so its gate depends on the row's branch only:
+        // with at least 32 rows per branch the sub-tile's rows span at most two branches, whose
+        // gates are loaded once.
+        float4 x[NIT];
 #pragma unroll
-        for (int h0 = 0; h0 < NIT; h0 += 4) {
-          float4 x[4], gv[4];
+        for (int it = 0; it < NIT; ++it) {
+          x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (ok[it] && full[it]) x[it] = *(const float4*)((const float*)g.C + off[it]);
+        }
+        const bool two = g.vec && rpb >= 32 && full[0];
+        float4 g_lo = make_float4(1.f, 1.f, 1.f, 1.f), g_hi = g_lo;
+        if (two) {
+          g_lo = *(const float4*)(g.vec + bq[0] * g.vec_bstride + nn[0]);
+          g_hi = *(const float4*)(g.vec + bq[NIT - 1] * g.vec_bstride + nn[0]);
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int it = h0 + q;
-            x[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-            gv[q] = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (ok[it] && full[it]) {
-              x[q] = *(const float4*)((const float*)g.C + off[it]);
-              if (g.vec) gv[q] = *(const float4*)(g.vec + bq[it] * g.vec_bstride + nn[it]);
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int it = h0 + q;
-            if (!ok[it]) continue;
-            const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
-            const uint4 v = *(const uint4*)(stg + row * STRIDE + ch * 16);
-            const float* vf = (const float*)&v;
-            float* C = (float*)g.C + off[it];
-            if (full[it]) {
-              *(float4*)C = make_float4(x[q].x + gv[q].x * vf[0], x[q].y + gv[q].y * vf[1],
-                                        x[q].z + gv[q].z * vf[2], x[q].w + gv[q].w * vf[3]);
-            } else {
-              const float* gt = g.vec ? g.vec + bq[it] * g.vec_bstride + nn[it] : nullptr;
-              for (int e = 0; e < VW && nn[it] + e < g.N; ++e) C[e] = C[e] + (gt ? gt[e] : 1.0f) * vf[e];
-            }
+        for (int it = 0; it < NIT; ++it) {
+          if (!ok[it]) continue;
+          const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
+          const uint4 v = *(const uint4*)(stg + row * STRIDE + ch * 16);
+          const float* vf = (const float*)&v;
+          float* C = (float*)g.C + off[it];
+          if (full[it]) {
+            float4 gv = bq[it] == bq[0] ? g_lo : g_hi;
+            if (g.vec && !two) gv = *(const float4*)(g.vec + bq[it] * g.vec_bstride + nn[it]);
+            *(float4*)C = make_float4(x[it].x + gv.x * vf[0], x[it].y + gv.y * vf[1],
+                                      x[it].z + gv.z * vf[2], x[it].w + gv.w * vf[3]);
+          } else {
+            const float* gt = g.vec ? g.vec + bq[it] * g.vec_bstride + nn[it] : nullptr;
+            for (int e = 0; e < VW && nn[it] + e < g.N; ++e) C[e] = C[e] + (gt ? gt[e] : 1.0f) * vf[e];
           }
         }
       } else {
