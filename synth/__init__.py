@@ -246,3 +246,73 @@ def caption_features(batch: int, max_len: int, cap_dim: int, seed: int) -> np.nd
     """fp32 N(0,1) caption features [batch, max_len, cap_dim] (stand-in for the encoder's
     penultimate hidden state, which needs trained weights)."""
     return _normal(rng(seed, _T_CAP, 0), (batch, max_len, cap_dim))
+
+
+# --------------------------------------------------------------------------------------
+# text encoder that precedes the path (Qwen3-4B-shaped decoder stack, random weights)
+# --------------------------------------------------------------------------------------
+_T_ENC = 7
+_T_IDS = 8
+
+
+@dataclass(frozen=True)
+class EncDims:
+    """Shapes of the text encoder.  Depth, widths and head counts are the pinned encoder's
+    (FastVideo "Z-Image Port Status": 36 decoder blocks, hidden 2560, intermediate 9728,
+    32 attention heads, 8 KV heads, head dimension 128).  The vocabulary size, RoPE base and
+    norm epsilon are not on the pages: the published Qwen3 values are used (151936, 1e6,
+    1e-6); tests use a small vocabulary, which no arithmetic depends on."""
+    hidden: int = 2560
+    inter: int = 9728
+    n_heads: int = 32
+    n_kv_heads: int = 8
+    head_dim: int = 128
+    n_layers: int = 36
+    vocab: int = 151936
+    rope_theta: float = 1.0e6
+    norm_eps: float = 1e-6
+
+    def replace(self, **kw) -> "EncDims":
+        return dataclasses.replace(self, **kw)
+
+
+ENC_FULL = EncDims()
+ENC_TINY = EncDims(hidden=256, inter=512, n_heads=4, n_kv_heads=2, n_layers=3, vocab=1000)
+
+
+def encoder_layer_weights(ed: EncDims, seed: int, index: int) -> dict:
+    """Weights of one encoder block, [out, in] row-major, fp32 arrays with bf16-representable
+    matrices; norm gains 1 + 0.02 N(0,1) in fp32.  w_qkv rows: the n_heads query heads, then
+    the n_kv_heads key heads, then the n_kv_heads value heads, 128 rows each."""
+    D, I, hd = ed.hidden, ed.inter, ed.head_dim
+    nq, nkv = ed.n_heads * hd, ed.n_kv_heads * hd
+    base = 16 * index
+    return {
+        "in_norm": (1.0 + _normal(rng(seed, _T_ENC, base + 0), (D,), WEIGHT_STD)).astype(np.float32),
+        "w_qkv": _weight(rng(seed, _T_ENC, base + 1), (nq + 2 * nkv, D)),
+        "q_norm": (1.0 + _normal(rng(seed, _T_ENC, base + 2), (hd,), WEIGHT_STD)).astype(np.float32),
+        "k_norm": (1.0 + _normal(rng(seed, _T_ENC, base + 3), (hd,), WEIGHT_STD)).astype(np.float32),
+        "w_o": _weight(rng(seed, _T_ENC, base + 4), (D, nq)),
+        "post_norm": (1.0 + _normal(rng(seed, _T_ENC, base + 5), (D,), WEIGHT_STD)).astype(np.float32),
+        "w_gate": _weight(rng(seed, _T_ENC, base + 6), (I, D)),
+        "w_up": _weight(rng(seed, _T_ENC, base + 7), (I, D)),
+        "w_down": _weight(rng(seed, _T_ENC, base + 8), (D, I)),
+    }
+
+
+def encoder_weights(ed: EncDims, seed: int, n_layers: int | None = None) -> dict:
+    """Embedding table (bf16-representable N(0,1) rows) and the first n_layers blocks."""
+    n = ed.n_layers if n_layers is None else n_layers
+    return {
+        "embed": bf16_truncate(_normal(rng(seed, _T_ENC, 1 << 20), (ed.vocab, ed.hidden))),
+        "layers": [encoder_layer_weights(ed, seed, i) for i in range(n)],
+    }
+
+
+def token_ids(batch: int, max_len: int, lengths, vocab: int, seed: int) -> np.ndarray:
+    """int32 [batch, max_len]: uniform ids in [0, vocab) below each branch's length, the id
+    0 after it (right padding, as the host tokenizer step produces)."""
+    ids = rng(seed, _T_IDS, 0).integers(0, vocab, size=(batch, max_len), dtype=np.int64)
+    for b, L in enumerate(lengths):
+        ids[b, L:] = 0
+    return ids.astype(np.int32)

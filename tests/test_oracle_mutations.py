@@ -40,6 +40,26 @@ MUTATIONS = {
 }
 
 
+# planted in oracle/encoder_oracle.py, caught by tests/test_encoder_oracle_pins.py
+ENC_MUTATIONS = {
+    "GQA heads strided, not grouped": ("hk = h // group\n        s = (q[:, h, :]", "hk = h % nkv\n        s = (q[:, h, :]"),
+    "no causal mask": ("s = np.where(future, -np.inf, s)", "s = s + 0"),
+    "causal mask off by one": ("np.triu(np.ones((S, S), dtype=bool), 1)", "np.triu(np.ones((S, S), dtype=bool), 2)"),
+    "no attention scale": ("s = (q[:, h, :] @ k[:, hk, :].T) * scale", "s = (q[:, h, :] @ k[:, hk, :].T)"),
+    "RoPE pairs adjacent": ("x1, x2 = x[..., :half], x[..., half:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
+    "RoPE sign": ("x1 * c - x2 * s", "x1 * c + x2 * s"),
+    "RoPE base 1e4": ("rope_tables_1d(pos0 + L, ed.head_dim, ed.rope_theta)", "rope_tables_1d(pos0 + L, ed.head_dim, 10000.0)"),
+    "q and k norm gains swapped": ('head_norm(q, w["q_norm"], eps), cos, sin)\n    k = rope_rotate_half(head_norm(k, w["k_norm"], eps)',
+                                   'head_norm(q, w["k_norm"], eps), cos, sin)\n    k = rope_rotate_half(head_norm(k, w["q_norm"], eps)'),
+    "no key norm": ('k = rope_rotate_half(head_norm(k, w["k_norm"], eps), cos, sin)', "k = rope_rotate_half(k, cos, sin)"),
+    "v from the k slice": ("v = qkv[:, (nq + nkv) * hd:]", "v = qkv[:, nq * hd:(nq + nkv) * hd]"),
+    "gate and up swapped": ('silu(linear(h2, w["w_gate"])) * linear(h2, w["w_up"])',
+                            'silu(linear(h2, w["w_up"])) * linear(h2, w["w_gate"])'),
+    "MLP norm uses the attention gain": ('rmsnorm(x, w["post_norm"], eps)', 'rmsnorm(x, w["in_norm"], eps)'),
+    "penultimate reads the last block": ("ed.n_layers - 1, dtype)[-1]", "ed.n_layers, dtype)[-1]"),
+}
+
+
 @pytest.fixture(scope="module")
 def sandbox(tmp_path_factory):
     d = tmp_path_factory.mktemp("oracle_mut")
@@ -48,7 +68,7 @@ def sandbox(tmp_path_factory):
                         ignore=shutil.ignore_patterns("__pycache__"))
     os.makedirs(os.path.join(d, "tests"))
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(d, "tests", "golden"))
-    for f in ("conftest.py", "test_oracle_pins.py"):
+    for f in ("conftest.py", "test_oracle_pins.py", "test_encoder_oracle_pins.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(d, "tests", f))
     return str(d)
 
@@ -59,9 +79,41 @@ def test_pins_catch_planted_mistake(sandbox, name):
     src = open(src_path).read()
     a, b = MUTATIONS[name]
     assert src.count(a) >= 1, f"mutation anchor not found: {name}"
-    with open(os.path.join(sandbox, "oracle", "zdit_oracle.py"), "w") as f:
-        f.write(src.replace(a, b, 1))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=sandbox, capture_output=True, text=True,
-                       timeout=300)
+    dst = os.path.join(sandbox, "oracle", "zdit_oracle.py")
+    try:
+        with open(dst, "w") as f:
+            f.write(src.replace(a, b, 1))
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            "tests/test_oracle_pins.py"], cwd=sandbox, capture_output=True, text=True,
+                           timeout=300)
+    finally:
+        with open(dst, "w") as f:
+            f.write(src)
+    assert r.returncode != 0, f"pins did not catch: {name}"
+
+
+def test_sandbox_copy_passes_unmutated(sandbox):
+    """The unmutated sandbox passes both pin files, so a failure below is the mutation's."""
+    for f in ("tests/test_oracle_pins.py", "tests/test_encoder_oracle_pins.py"):
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", f],
+                           cwd=sandbox, capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(ENC_MUTATIONS))
+def test_encoder_pins_catch_planted_mistake(sandbox, name):
+    src_path = os.path.join(ROOT, "oracle", "encoder_oracle.py")
+    src = open(src_path).read()
+    a, b = ENC_MUTATIONS[name]
+    assert src.count(a) >= 1, f"mutation anchor not found: {name}"
+    dst = os.path.join(sandbox, "oracle", "encoder_oracle.py")
+    try:
+        with open(dst, "w") as f:
+            f.write(src.replace(a, b, 1))
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            "tests/test_encoder_oracle_pins.py"], cwd=sandbox, capture_output=True,
+                           text=True, timeout=300)
+    finally:
+        with open(dst, "w") as f:
+            f.write(src)
     assert r.returncode != 0, f"pins did not catch: {name}"
