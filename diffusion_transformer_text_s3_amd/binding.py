@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libzdit.so")
 
 ZDIT_OK, ZDIT_EINVAL, ZDIT_EUNSUPPORTED, ZDIT_EWORKSPACE, ZDIT_EHIP = 0, -1, -2, -3, -4
 ZDIT_BF16, ZDIT_FP32_DEBUG = 0, 1
-ZDIT_SEQ_IMAGE, ZDIT_SEQ_CAPTION, ZDIT_SEQ_JOINT = 0, 1, 2
+ZDIT_SEQ_IMAGE, ZDIT_SEQ_CAPTION, ZDIT_SEQ_JOINT, ZDIT_SEQ_TEXT = 0, 1, 2, 3
 ZDIT_EPI_STORE, ZDIT_EPI_BIAS, ZDIT_EPI_RESID, ZDIT_EPI_SWIGLU = 0, 1, 2, 3
 MAX_BATCH = 16
 
@@ -26,6 +26,8 @@ EXPORTS = [
     "zdit_sample_workspace", "zdit_sample", "zdit_rope_tables", "zdit_op_gemm",
     "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn", "zdit_op_qkv_attn",
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
+    "zdit_encoder_workspace", "zdit_encoder_fwd", "zdit_op_embed_workspace", "zdit_op_embed",
+    "zdit_op_qknorm_rope", "zdit_op_attn_gqa_workspace", "zdit_op_attn_gqa",
 ]
 
 
@@ -58,6 +60,22 @@ class zdit_model_w(C.Structure):
                 ("final_w", C.c_void_p), ("final_b", C.c_void_p)]
 
 
+class zdit_enc_cfg(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32),
+                ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("vocab", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float)]
+
+
+class zdit_enc_layer_w(C.Structure):
+    _fields_ = [("in_norm", C.c_void_p), ("w_qkv", C.c_void_p), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p), ("w_o", C.c_void_p), ("post_norm", C.c_void_p),
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p)]
+
+
+class zdit_enc_w(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("layers", C.POINTER(zdit_enc_layer_w))]
+
+
 class ZditError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"zdit error {code}: {msg}")
@@ -80,6 +98,7 @@ def lib():
         pf32 = C.POINTER(C.c_float)
         pd, pw = C.POINTER(zdit_dims), C.POINTER(zdit_block_w)
         pc, pm = C.POINTER(zdit_model_cfg), C.POINTER(zdit_model_w)
+        pe, pew = C.POINTER(zdit_enc_cfg), C.POINTER(zdit_enc_w)
         sig = {
             "zdit_last_error": (C.c_char_p, []),
             "zdit_abi_version": (i32, []),
@@ -104,6 +123,13 @@ def lib():
             "zdit_op_cap_pad": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp]),
             "zdit_op_temb": (i32, [i32, pf32, i32, i32, f32, vp, vp, vp, vp, vp, vp]),
             "zdit_op_adaln": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "zdit_encoder_workspace": (sz, [pe, i32, i32]),
+            "zdit_encoder_fwd": (i32, [pe, pew, i32, i32, pi32, pi32, vp, vp, sz, vp]),
+            "zdit_op_embed_workspace": (sz, [i32, i32]),
+            "zdit_op_embed": (i32, [i32, i32, i32, i32, pi32, pi32, vp, vp, vp, sz, vp]),
+            "zdit_op_qknorm_rope": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, vp, vp, f32, vp]),
+            "zdit_op_attn_gqa_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_attn_gqa": (i32, [i32, i32, i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -233,6 +259,45 @@ def upload_model(W: dict, precision=ZDIT_BF16, device="cuda") -> DeviceModel:
     return DeviceModel(t, nr, cr, mb)
 
 
+def make_enc_cfg(ed) -> zdit_enc_cfg:
+    """zdit_enc_cfg from any object with the encoder shape attributes (n_layers, hidden,
+    inter, n_heads, n_kv_heads, head_dim, vocab, rope_theta, norm_eps)."""
+    c = zdit_enc_cfg()
+    c.n_layers, c.hidden, c.inter = ed.n_layers, ed.hidden, ed.inter
+    c.n_heads, c.n_kv_heads, c.head_dim, c.vocab = ed.n_heads, ed.n_kv_heads, ed.head_dim, ed.vocab
+    c.rope_theta, c.norm_eps = ed.rope_theta, ed.norm_eps
+    return c
+
+
+class DeviceEncoder:
+    """Device copies of the encoder weights and the zdit_enc_w view (keeps them alive)."""
+
+    MATS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down")
+    VECS = ("in_norm", "q_norm", "k_norm", "post_norm")
+
+    def __init__(self, embed, layers: list):
+        self.embed = embed
+        self.layers = layers
+        self.lw = (zdit_enc_layer_w * max(1, len(layers)))()
+        for i, t in enumerate(layers):
+            for k in self.MATS + self.VECS:
+                setattr(self.lw[i], k, t[k].data_ptr())
+        self.w = zdit_enc_w()
+        self.w.embed = embed.data_ptr()
+        self.w.layers = C.cast(self.lw, C.POINTER(zdit_enc_layer_w))
+
+
+def upload_encoder(W: dict, device="cuda") -> DeviceEncoder:
+    """Device tensors (bf16 matrices, fp32 gains) for an encoder weight dict of fp32 arrays."""
+    emb = _to_dev(W["embed"], ZDIT_BF16, device, True)
+    layers = []
+    for lw in W["layers"]:
+        t = {k: _to_dev(lw[k], ZDIT_BF16, device, True) for k in DeviceEncoder.MATS}
+        t.update({k: _to_dev(lw[k], ZDIT_BF16, device, False) for k in DeviceEncoder.VECS})
+        layers.append(t)
+    return DeviceEncoder(emb, layers)
+
+
 # ----------------------------------------------------------------------------- calls
 def workspace(nbytes: int, device="cuda"):
     import torch
@@ -345,3 +410,46 @@ def zdit_op_temb(batch, t, t_freq, c_dim, t_scale, w1, b1, w2, b2, c_out, stream
 def zdit_op_adaln(precision, batch, c_dim, n_out, c, w, b, out, stream=None):
     return check(lib().zdit_op_adaln(precision, batch, c_dim, n_out, ptr(c), ptr(w), ptr(b), ptr(out),
                                      stream_handle(stream)))
+
+
+def zdit_encoder_workspace(cfg, batch, max_len) -> int:
+    return lib().zdit_encoder_workspace(C.byref(cfg), batch, max_len)
+
+
+def _ids_array(ids):
+    import numpy as np
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def zdit_encoder_fwd(cfg, m: DeviceEncoder, batch, max_len, ids, lengths, hidden_out, ws, stream=None):
+    a, p = _ids_array(ids)
+    return check(lib().zdit_encoder_fwd(C.byref(cfg), C.byref(m.w), batch, max_len, p, i32_array(lengths),
+                                        ptr(hidden_out), ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_embed_workspace(batch, max_len) -> int:
+    return lib().zdit_op_embed_workspace(batch, max_len)
+
+
+def zdit_op_embed(batch, max_len, dim, vocab, ids, lengths, table, out, ws, stream=None):
+    a, p = _ids_array(ids)
+    return check(lib().zdit_op_embed(batch, max_len, dim, vocab, p, i32_array(lengths), ptr(table), ptr(out),
+                                     ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_qknorm_rope(batch, s_max, n_heads, n_kv_heads, seq_len, qkv, q_norm, k_norm, cos, sin, eps,
+                        stream=None):
+    return check(lib().zdit_op_qknorm_rope(batch, s_max, n_heads, n_kv_heads, i32_array(seq_len), ptr(qkv),
+                                           ptr(q_norm), ptr(k_norm), ptr(cos), ptr(sin), eps,
+                                           stream_handle(stream)))
+
+
+def zdit_op_attn_gqa_workspace(precision, batch, s_max, n_kv_heads) -> int:
+    return lib().zdit_op_attn_gqa_workspace(precision, batch, s_max, n_kv_heads)
+
+
+def zdit_op_attn_gqa(precision, batch, s_max, n_heads, n_kv_heads, causal, seq_len, qkv, out, ws, stream=None):
+    return check(lib().zdit_op_attn_gqa(precision, batch, s_max, n_heads, n_kv_heads, int(causal),
+                                        i32_array(seq_len), ptr(qkv), ptr(out), ptr(ws), ws.numel(),
+                                        stream_handle(stream)))

@@ -54,14 +54,29 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const GemmArgs& g, hipStream_t s);
 
+// q, k, v rows: row r of branch b at qkv + (b * s_max + r) * row_stride elements, query head
+// h at column h * 128, key head j at k_col + j * 128, value head j at v_col + j * 128.  Query
+// head h reads key/value head h / (n_heads / n_kv_heads).  Zero row_stride / k_col / v_col /
+// n_kv_heads mean the DiT layout: n_kv_heads = n_heads, row_stride 3D, k_col D, v_col 2D
+// (D = n_heads * 128).  causal: key j is visible to query i only when j <= i.
 struct AttnArgs {
-  const void* qkv;   // [B, s_max, 3*D]
-  void* vt;          // bf16 path: [B, nh, 128, s_pad] transposed values (workspace)
-  void* out;         // [B, s_max, D]
+  const void* qkv;
+  void* vt;          // bf16 path: [B, n_kv_heads, 128, s_pad] transposed values (workspace)
+  void* out;         // [B, s_max, n_heads * 128]
   int batch, s_max, s_pad, n_heads;
+  int n_kv_heads, row_stride, k_col, v_col;
+  int causal;
   int vt_ready;      // vt already holds V^T (written by the QKV GEMM epilogue)
   int seq_len[kMaxBatch];
 };
+// DiT defaults filled in for zero fields (see AttnArgs)
+inline void attn_layout_defaults(AttnArgs& a) {
+  const int D = a.n_heads * kHeadDim;
+  if (a.n_kv_heads == 0) a.n_kv_heads = a.n_heads;
+  if (a.row_stride == 0) a.row_stride = 3 * D;
+  if (a.k_col == 0) a.k_col = D;
+  if (a.v_col == 0) a.v_col = 2 * D;
+}
 size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads);
 hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s);
 // Zero V^T tokens s_max .. s_pad - 1 of every (branch, head, dim) row (after the QKV epilogue
@@ -86,6 +101,37 @@ struct NormArgs {
   int valid[kMaxBatch];
 };
 hipError_t launch_rmsnorm_mod(int precision, const NormArgs& a, hipStream_t s);
+
+// Per-head RMSNorm (gain gq for query heads, gk for key heads, over the 128 dims of a head)
+// followed by RoPE that turns dims (i, i + 64) by the row's angle i, in place on the bf16
+// q and k heads of rows r < seq_len[b] (rows laid out as in AttnArgs).  cos / sin: fp32
+// [batch][s_max][64] with tab_bstride floats between branches (0 = shared).
+struct QkNormRopeArgs {
+  void* qkv;
+  int64_t row_stride;
+  int k_col;
+  int n_heads, n_kv_heads;
+  const float* gq;
+  const float* gk;
+  const float* cos;
+  const float* sin;
+  int64_t tab_bstride;
+  float eps;
+  int batch, s_max;
+  int seq_len[kMaxBatch];
+};
+hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t s);
+
+// out[b][r][:] = table[ids[b * s_max + r]][:] (bf16 table, fp32 out) for r < len[b], 0 for
+// r >= len[b] (ids there are not read).  dim a multiple of 8.
+struct EmbedArgs {
+  const int* ids;
+  const void* table;
+  float* out;
+  int batch, s_max, dim;
+  int len[kMaxBatch];
+};
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 
 struct RopeArgs {
   void* qkv;

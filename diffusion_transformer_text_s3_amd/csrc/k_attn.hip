@@ -1,6 +1,8 @@
-// Joint (bidirectional) softmax attention over the single-stream sequence, head_dim 128,
-// ragged per branch: keys j >= seq_len[b] are masked (batch-alignment padding), every key
-// below it (image tokens, caption tokens and learned caption pads) is context.
+// Softmax attention, head_dim 128, ragged per branch: keys j >= seq_len[b] are masked
+// (batch-alignment padding).  The DiT's joint attention is bidirectional: every key below
+// seq_len[b] (image tokens, caption tokens and learned caption pads) is context.  The text
+// encoder's is causal (key j visible to query i only when j <= i) with grouped key/value
+// heads (query head h reads key/value head h / (n_heads / n_kv_heads)).
 //
 // bf16 path on gfx950.  A 512-thread workgroup owns 256 queries of one (branch, head); each
 // wavefront owns 32 of them and keeps their 128-dim rows in registers as MFMA B operands.
@@ -25,10 +27,10 @@ namespace {
 constexpr int KT = 64;   // keys per LDS block
 constexpr int KROW = 17; // 16-byte chunks per row of the V transpose staging tile (16 + 1 pad)
 
+// One workgroup per (64 tokens, key/value head, branch).
 __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
   __shared__ uint4 t[64 * KROW];
   const int b = blockIdx.z, h = blockIdx.y, s0 = blockIdx.x * 64;
-  const int D = a.n_heads * kHeadDim;
   const int S = a.seq_len[b];
   const bf16* qkv = (const bf16*)a.qkv;
 #pragma unroll
@@ -37,12 +39,13 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
     const int tok = c >> 4, dc = c & 15;
     const int s = s0 + tok;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (s < S) v = *(const uint4*)(qkv + ((int64_t)b * a.s_max + s) * 3 * D + 2 * D + h * kHeadDim + dc * 8);
+    if (s < S)
+      v = *(const uint4*)(qkv + ((int64_t)b * a.s_max + s) * a.row_stride + a.v_col + h * kHeadDim + dc * 8);
     t[tok * KROW + dc] = v;
   }
   __syncthreads();
   const bf16* tb = (const bf16*)t;
-  bf16* vt = (bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
+  bf16* vt = (bf16*)a.vt + ((int64_t)(b * a.n_kv_heads + h) * kHeadDim) * a.s_pad;
   // Within every 16-key group the keys are stored in the order the 32x32 MFMA result hands
   // them to a lane half: chunk 2g holds keys {0-3, 8-11} of group g, chunk 2g+1 holds keys
   // {4-7, 12-15}, so the attention kernel reads a lane's 8 keys as one 16-byte chunk.
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(256) void vtrans_kernel(AttnArgs a) {
 // 16-byte chunk of those columns in every (branch, head, dim) row.
 __global__ __launch_bounds__(256) void vt_tail_zero_kernel(AttnArgs a) {
   const int tail = (a.s_pad - a.s_max) >> 3;  // chunks per row
-  const int64_t rows = (int64_t)a.batch * a.n_heads * kHeadDim;
+  const int64_t rows = (int64_t)a.batch * a.n_kv_heads * kHeadDim;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * tail) return;
   const int64_t row = i / tail;
@@ -126,7 +129,9 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int qt = lid % nqt, bh = lid / nqt;
   const int h = bh % a.n_heads, b = bh / a.n_heads, q0 = qt * QTILE;
-  const int D = a.n_heads * kHeadDim;
+  const int hk = h / (a.n_heads / a.n_kv_heads);  // key/value head of this query head
+  const int D = a.n_heads * kHeadDim;              // output row width
+  const int rs = a.row_stride;
   const int S = a.seq_len[b];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -145,18 +150,18 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   bf16x8 qf[8];
   {
-    const bf16* qp = qkv + ((int64_t)b * a.s_max + min(q, S - 1)) * 3 * D + h * kHeadDim + 8 * fh;
+    const bf16* qp = qkv + ((int64_t)b * a.s_max + min(q, S - 1)) * rs + h * kHeadDim + 8 * fh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = *(const bf16x8*)(qp + 16 * s);
   }
 
-  // K rows of this (branch, head): key k at k * 3D elements from kbase.  The resource ends
-  // after key S - 1's 128 dims, so keys >= S load as zero.
-  const int krow = 3 * D * 2;  // bytes between consecutive keys
-  const bf16* kbase = qkv + (int64_t)b * a.s_max * 3 * D + D + h * kHeadDim;
+  // K rows of this (branch, key head): key k at k * row_stride elements from kbase.  The
+  // resource ends after key S - 1's 128 dims, so keys >= S load as zero.
+  const int krow = rs * 2;  // bytes between consecutive keys
+  const bf16* kbase = qkv + (int64_t)b * a.s_max * rs + a.k_col + hk * kHeadDim;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, (S - 1) * krow + kHeadDim * 2, kAttBufFlags);
-  const bf16* vbase = (const bf16*)a.vt + ((int64_t)(b * a.n_heads + h) * kHeadDim) * a.s_pad;
+  const bf16* vbase = (const bf16*)a.vt + ((int64_t)(b * a.n_kv_heads + hk) * kHeadDim) * a.s_pad;
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, kHeadDim * a.s_pad * 2, kAttBufFlags);
   // Each key block is 16 KB of K and 16 KB of V^T: 16 wave loads of 1 KB each, two per wave.
@@ -200,13 +205,17 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  const int nkt = (S + KT - 1) / KT;
+  // causal: no key past the tile's last valid query is needed
+  const int nkt = (a.causal ? min(q0 + QTILE, S) + KT - 1 : S + KT - 1) / KT;
+  // largest key this lane's query sees (key 0 is always visible)
+  const int klim = a.causal ? min(S - 1, q) : S - 1;
 
   // One key block t, its K in Kc / V^T in Vc: loads of V^T block t+1 (into Vn) and K block
   // t+2 (into Kc, free since the scores of block t exist) start first; softmax of block t
   // (scores in `cur`), O^T += V^T P^T, QK^T of block t+1 (K in Kn) into `nxt`; then every
-  // wave waits for its loads and the workgroup meets at a barrier.  Only the final block can
-  // hold keys >= S (masked).
+  // wave waits for its loads and the workgroup meets at a barrier.  Only masked steps (the
+  // final block, and with causal masking the blocks from the tile's first query on) hold
+  // keys past a lane's limit; they are set to -inf.
   auto step = [&](auto masked, int t, uint4* Kc, uint4* Vc, uint4* Kn, uint4* Vn, f32x16 (&cur)[2],
                   f32x16 (&nxt)[2]) {
     const bool more = t + 1 < nkt;
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * KT + t2 * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-          if (key >= S) cur[t2][r] = -INFINITY;
+          if (key > klim) cur[t2][r] = -INFINITY;
         }
     }
 #pragma unroll
@@ -229,17 +238,20 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[t2][r]);
     mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx * sc);
-    // Lazy rescale: the reference max moves only when some lane's max rose by more than 8
+    // Lazy rescale: a query's reference max moves only when its max rose by more than 8
     // (log2 units), so p = exp2(s - m_run) stays below 2^8; O and l share the reference, so
-    // the result O / l is the same softmax.
-    if (__any(m_new > m_run + 8.0f)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // the result O / l is the same softmax.  The branch is taken when any lane needs it;
+    // the other lanes scale by exactly 1, so every query's arithmetic depends on its own
+    // scores only.
+    const bool move = m_new > m_run + 8.0f;
+    if (__any(move)) {
+      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      m_run = m_new;
+      m_run = move ? m_new : m_run;
     }
     bf16x8 pb[2][2];
 #pragma unroll
@@ -277,17 +289,20 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
   __syncthreads();
   using Plain = std::integral_constant<bool, false>;
   using Masked = std::integral_constant<bool, true>;
+  // steps t >= tm are masked: the last block (keys >= S), and with causal masking every
+  // block from the one holding the tile's first query.  tm is even, so the buffer roles at
+  // the switch are those of step 0.
+  const int tm = (a.causal ? min(nkt - 1, q0 / KT) : nkt - 1) & ~1;
   int t = 0;
-  for (; t + 2 < nkt; t += 2) {
+  for (; t < tm; t += 2) {
     step(Plain{}, t, K0, V0, K1, V1, sA, sB);
     step(Plain{}, t + 1, K1, V1, K0, V0, sB, sA);
   }
-  if (nkt - t == 2) {
-    step(Plain{}, t, K0, V0, K1, V1, sA, sB);
-    step(Masked{}, t + 1, K1, V1, K0, V0, sB, sA);
-  } else {
+  for (; t + 1 < nkt; t += 2) {
     step(Masked{}, t, K0, V0, K1, V1, sA, sB);
+    step(Masked{}, t + 1, K1, V1, K0, V0, sB, sA);
   }
+  if (t < nkt) step(Masked{}, t, K0, V0, K1, V1, sA, sB);
 
   const float l = xor32_sum(l_run);
   const float inv = 1.0f / l;
@@ -310,23 +325,26 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int b = blockIdx.z, h = blockIdx.y, q = blockIdx.x, lane = threadIdx.x;
   const int D = a.n_heads * kHeadDim;
+  const int hk = h / (a.n_heads / a.n_kv_heads);
   const int S = a.seq_len[b];
   const float* qkv = (const float*)a.qkv;
   float* op = (float*)a.out + ((int64_t)b * a.s_max + q) * D + h * kHeadDim + 2 * lane;
   if (q >= S) { op[0] = 0.f; op[1] = 0.f; return; }
-  const float* qp = qkv + ((int64_t)b * a.s_max + q) * 3 * D + h * kHeadDim + 2 * lane;
+  const float* qp = qkv + ((int64_t)b * a.s_max + q) * a.row_stride + h * kHeadDim + 2 * lane;
   const float q0 = qp[0], q1 = qp[1];
   const float scale = 1.0f / sqrtf((float)kHeadDim);
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int j = 0; j < S; ++j) {
-    const float* kp = qkv + ((int64_t)b * a.s_max + j) * 3 * D + D + h * kHeadDim + 2 * lane;
+  const int nk = a.causal ? q + 1 : S;
+  for (int j = 0; j < nk; ++j) {
+    const float* row = qkv + ((int64_t)b * a.s_max + j) * a.row_stride;
+    const float* kp = row + a.k_col + hk * kHeadDim + 2 * lane;
     float s = q0 * kp[0] + q1 * kp[1];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     s *= scale;
     const float mn = fmaxf(m, s);
     const float al = expf(m - mn), p = expf(s - mn);
-    const float* vp = kp + D;
+    const float* vp = row + a.v_col + hk * kHeadDim + 2 * lane;
     l = l * al + p;
     o0 = o0 * al + p * vp[0];
     o1 = o1 * al + p * vp[1];
@@ -344,17 +362,21 @@ size_t attn_vt_bytes(int precision, int batch, int s_max, int n_heads) {
   return (size_t)batch * n_heads * kHeadDim * s_pad * sizeof(bf16);
 }
 
-hipError_t launch_vt_tail_zero(const AttnArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.batch * a.n_heads * kHeadDim * ((a.s_pad - a.s_max) >> 3);
+hipError_t launch_vt_tail_zero(const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  attn_layout_defaults(a);
+  const int64_t n = (int64_t)a.batch * a.n_kv_heads * kHeadDim * ((a.s_pad - a.s_max) >> 3);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(vt_tail_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn(int precision, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn(int precision, const AttnArgs& args, hipStream_t s) {
+  AttnArgs a = args;
+  attn_layout_defaults(a);
   if (precision == 0) {
     if (!a.vt_ready)
-      hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_heads, a.batch), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(vtrans_kernel, dim3(a.s_pad / 64, a.n_kv_heads, a.batch), dim3(256), 0, s, a);
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(((a.s_max + QTILE - 1) / QTILE) * a.n_heads * a.batch),
                        dim3(ATT_NT), 0, s, a);
   } else {

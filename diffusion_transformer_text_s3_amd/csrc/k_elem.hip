@@ -171,6 +171,9 @@ __global__ __launch_bounds__(256) void rope_tables_kernel(RopeTabArgs a) {
   } else if (a.kind == 1) {  // caption
     len = a.n_cap[b];
     pos[0] = 1 + s;
+  } else if (a.kind == 3) {  // text encoder tokens: position = index from 0
+    len = a.n_cap[b];
+    pos[0] = s;
   } else {  // joint: image tokens then caption tokens
     len = nimg + a.n_cap[b];
     if (s < nimg) { pos[1] = s / a.grid_w; pos[2] = s % a.grid_w; }

@@ -11,40 +11,16 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
-#include "zdit.h"
+#include "api_util.h"
 
 using namespace zdit;
 
+std::string& zdit::api_error_text() {
+  thread_local std::string text;
+  return text;
+}
+
 namespace {
-
-thread_local std::string g_err;
-
-zdit_status fail(zdit_status code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_err = buf;
-  return code;
-}
-
-zdit_status ok() {
-  g_err.clear();
-  return ZDIT_OK;
-}
-
-#define HIP_TRY(expr)                                                                   \
-  do {                                                                                  \
-    hipError_t e_ = (expr);                                                             \
-    if (e_ != hipSuccess) return fail(ZDIT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
-  } while (0)
-
-inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
-inline int act_bytes(int precision) { return precision == ZDIT_BF16 ? 2 : 4; }
-inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 zdit_status check_dims(const zdit_dims* d) {
   if (!d) return fail(ZDIT_EINVAL, "dims is NULL");
@@ -86,18 +62,6 @@ BlockPlan plan_block(const zdit_dims& d, int B, int s) {
   return p;
 }
 
-RowMap compact_rows(int M, int64_t ld) {
-  RowMap r;
-  r.rows_per_batch = M > 0 ? M : 1;
-  r.batch_stride = 0;
-  r.ld = ld;
-  for (int i = 0; i < kMaxBatch; ++i) r.valid[i] = M;
-  return r;
-}
-
-hipError_t gemm(int precision, int epi, const GemmArgs& g, hipStream_t s) {
-  return precision == ZDIT_BF16 ? launch_gemm_bf16(epi, g, s) : launch_gemm_f32(epi, g, s);
-}
 
 // q, k, v projection of h [B * s, nh * 128] (rows of branch b at b * s), RoPE on q and k,
 // and joint attention into o.  In bf16 with s % 32 == 0 the projection's epilogue rotates q, k
@@ -430,7 +394,7 @@ double sigma_at(int i, int n, double shift) {
 
 extern "C" {
 
-const char* zdit_last_error(void) { return g_err.c_str(); }
+const char* zdit_last_error(void) { return api_error_text().c_str(); }
 int32_t zdit_abi_version(void) { return ZDIT_ABI_VERSION; }
 
 size_t zdit_block_workspace(const zdit_dims* dims, int32_t batch, int32_t s_max) {
@@ -571,7 +535,7 @@ zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_
 zdit_status zdit_rope_tables(int32_t kind, const int32_t rope_axes[3], float theta, int32_t batch, int32_t s_max,
                              int32_t grid_h, int32_t grid_w, const int32_t* n_cap, float* cos_out, float* sin_out,
                              void* hip_stream) {
-  if (kind < ZDIT_SEQ_IMAGE || kind > ZDIT_SEQ_JOINT) return fail(ZDIT_EINVAL, "kind %d", kind);
+  if (kind < ZDIT_SEQ_IMAGE || kind > ZDIT_SEQ_TEXT) return fail(ZDIT_EINVAL, "kind %d", kind);
   if (!rope_axes) return fail(ZDIT_EINVAL, "rope_axes NULL");
   for (int i = 0; i < 3; ++i)
     if (rope_axes[i] < 0 || rope_axes[i] % 2) return fail(ZDIT_EINVAL, "rope_axes[%d] = %d", i, rope_axes[i]);

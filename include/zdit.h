@@ -3,6 +3,9 @@
  * diffusion transformer block, its 2 + 2 + 30 block stack and the 8-step negated-CFG
  * FlowMatchEuler sampler.
  *
+ * Also the text encoder that produces its caption features (a Qwen3-shaped causal decoder
+ * read out at its penultimate hidden state), with random weights.
+ *
  * Sources (web pages; cited by title and section):
  *   [CoreAI]  Core AI model zoo, "Z-Image-Turbo port - a 6B diffusion DiT on Core AI, and
  *             why it is Mac-only".
@@ -15,7 +18,9 @@
  *     the call and must stay valid until the enqueued work completes.  The library allocates
  *     no device memory and keeps no pointer after returning.
  *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
- *     Nothing synchronises; no host<->device copy is made.
+ *     Nothing synchronises; no host<->device copy is made, except that the text-encoder
+ *     calls copy the host token ids into their workspace (the host array may be reused as
+ *     soon as the call returns).
  *   - Arguments are validated before anything is enqueued.  On error nothing runs, outputs
  *     are untouched, the return value is negative and zdit_last_error() says why.  Faults
  *     during execution surface at the caller's next synchronisation, as in any HIP library.
@@ -47,8 +52,8 @@ enum {
 
 enum { ZDIT_BF16 = 0, ZDIT_FP32_DEBUG = 1 };
 
-/* Token-sequence layouts for RoPE tables. */
-enum { ZDIT_SEQ_IMAGE = 0, ZDIT_SEQ_CAPTION = 1, ZDIT_SEQ_JOINT = 2 };
+/* Token-sequence layouts for RoPE tables (ZDIT_SEQ_TEXT: the text encoder's tokens). */
+enum { ZDIT_SEQ_IMAGE = 0, ZDIT_SEQ_CAPTION = 1, ZDIT_SEQ_JOINT = 2, ZDIT_SEQ_TEXT = 3 };
 
 #define ZDIT_MAX_BATCH 16
 #define ZDIT_ABI_VERSION 1
@@ -225,7 +230,8 @@ zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_
  * "Architecture -> export mapping", row DiT: precomputed cos/sin; [Status] issue I006:
  * RoPE buffers stay fp32).  Positions: image token (r, c) of a grid_h x grid_w grid ->
  * (0, r, c) in row-major order; caption token j -> (1 + j, 0, 0); ZDIT_SEQ_JOINT is the
- * image tokens followed by n_cap[b] caption tokens.  Column k enumerates rotation pairs:
+ * image tokens followed by n_cap[b] caption tokens; ZDIT_SEQ_TEXT token j -> (j, 0, 0) for
+ * j < n_cap[b] (the text encoder, with rope_axes {128, 0, 0}).  Column k enumerates rotation pairs:
  * axis 0's rope_axes[0]/2 pairs, then axis 1's, then axis 2's; pair p of axis a turns by
  * pos_a * theta^(-2p / rope_axes[a]).  Rows past a branch's length get cos 1, sin 0.
  * n_cap: host [batch] (ignored for ZDIT_SEQ_IMAGE).  cos_out, sin_out: device. */
@@ -310,6 +316,101 @@ zdit_status zdit_op_temb(int32_t batch, const float* t, int32_t t_freq, int32_t 
 zdit_status zdit_op_adaln(int32_t precision, int32_t batch, int32_t c_dim, int32_t n_out,
                           const float* c, const void* w, const float* b, float* out,
                           void* hip_stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Text encoder: the Qwen3-shaped causal decoder whose penultimate hidden state the DiT
+ * reads as caption features ([Status] "Current Phase" summary: 36 decoder blocks, hidden
+ * 2560, intermediate 9728, 32 attention heads, 8 KV heads, head dimension 128; component
+ * matrix, row Production text encoder: hidden_states[-2]; [CoreAI] "Architecture -> export
+ * mapping", row Text encoder: causal, additive causal and non-padding mask over right-padded
+ * ids, embed_tokens inside the graph, bf16 weights with an fp32 boundary).  Block (the
+ * published Qwen3 decoder; not spelled out on the pages):
+ *   h = RMSNorm(x; in_norm); [q | k | v] = h W_qkv^T (n_heads query heads, n_kv_heads key
+ *   and value heads of 128); q, k per head: RMSNorm over the 128 dims (q_norm / k_norm
+ *   gains), then RoPE turning dims (i, i + 64) by pos * rope_theta^(-2i/128), pos = token
+ *   index from 0; causal attention, query head h reading key/value head
+ *   h / (n_heads / n_kv_heads), scale 1/sqrt(128); x += o W_o^T;
+ *   h2 = RMSNorm(x; post_norm); x += (SiLU(h2 W_gate^T) * (h2 W_up^T)) W_down^T.
+ * Residual stream fp32, GEMM operands bf16, accumulation fp32, norms in fp32.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_layers;    /* blocks of the model (36); the output is taken after n_layers - 1 */
+  int32_t hidden;      /* 2560; multiple of 128, <= 4096 */
+  int32_t inter;       /* 9728; multiple of 128 */
+  int32_t n_heads;     /* 32 query heads */
+  int32_t n_kv_heads;  /* 8; divides n_heads */
+  int32_t head_dim;    /* 128 (the only value implemented) */
+  int32_t vocab;       /* embedding rows */
+  float rope_theta;    /* 1e6 */
+  float norm_eps;      /* 1e-6 */
+} zdit_enc_cfg;
+
+typedef struct {
+  const float* in_norm;    /* fp32 [hidden] */
+  const void* w_qkv;       /* bf16 [(n_heads + 2 n_kv_heads) * 128, hidden]: q heads, k heads, v heads */
+  const float* q_norm;     /* fp32 [128] */
+  const float* k_norm;     /* fp32 [128] */
+  const void* w_o;         /* bf16 [hidden, n_heads * 128] */
+  const float* post_norm;  /* fp32 [hidden] */
+  const void* w_gate;      /* bf16 [inter, hidden] */
+  const void* w_up;        /* bf16 [inter, hidden] */
+  const void* w_down;      /* bf16 [hidden, inter] */
+} zdit_enc_layer_w;
+
+typedef struct {
+  const void* embed;               /* bf16 [vocab, hidden] */
+  const zdit_enc_layer_w* layers;  /* host array of n_layers - 1 blocks (the last block does
+                                      not enter hidden_states[-2] and is not read) */
+} zdit_enc_w;
+
+/* hidden_states[-2] of `batch` right-padded id rows: the residual stream after the first
+ * n_layers - 1 blocks, fp32 [batch, max_len, hidden].  Row r of branch b is computed for
+ * r < len[b] and is 0 for r >= len[b] (padding keys are masked, so valid rows do not depend
+ * on max_len).
+ *   ids        host int32 [batch, max_len]; ids[b][r] in [0, vocab) for r < len[b] (others
+ *              not read)
+ *   len        host [batch], each in 1..max_len
+ *   hidden_out device fp32 [batch, max_len, hidden], written (it also holds the residual
+ *              stream while the blocks run)
+ *   batch 1..ZDIT_MAX_BATCH; max_len >= 1; ws: zdit_encoder_workspace() bytes. */
+size_t zdit_encoder_workspace(const zdit_enc_cfg* cfg, int32_t batch, int32_t max_len);
+zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32_t batch,
+                             int32_t max_len, const int32_t* ids, const int32_t* len,
+                             float* hidden_out, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Encoder kernels alone (tests and measurement). */
+/* Embedding gather: out [batch, max_len, dim] fp32 = rows of table (bf16 [vocab, dim]) for
+ * r < len[b], 0 after; ids / len host as in zdit_encoder_fwd; dim % 8 == 0; ws:
+ * zdit_op_embed_workspace() bytes (the ids are copied there). */
+size_t zdit_op_embed_workspace(int32_t batch, int32_t max_len);
+zdit_status zdit_op_embed(int32_t batch, int32_t max_len, int32_t dim, int32_t vocab,
+                          const int32_t* ids, const int32_t* len, const void* table, float* out,
+                          void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Per-head RMSNorm + RoPE on the q and k heads of a bf16 qkv buffer [batch, s_max,
+ * (n_heads + 2 n_kv_heads) * 128] in place, rows r < seq_len[b] (others untouched): each
+ * 128-dim head y = x / sqrt(mean(x^2) + eps) * g (g = q_norm for query heads, k_norm for
+ * key heads) in fp32, then y_i' = y_i c_i - y_{i+64} s_i, y_{i+64}' = y_{i+64} c_i + y_i s_i
+ * with the row's fp32 tables cos/sin [batch, s_max, 64] (each product and sum rounded), then
+ * rounded to bf16. */
+zdit_status zdit_op_qknorm_rope(int32_t batch, int32_t s_max, int32_t n_heads, int32_t n_kv_heads,
+                                const int32_t* seq_len, void* qkv, const float* q_norm,
+                                const float* k_norm, const float* cos, const float* sin,
+                                float eps, void* hip_stream);
+
+/* Attention with grouped key/value heads and an optional causal mask on a rotated qkv buffer
+ * [batch, s_max, (n_heads + 2 n_kv_heads) * 128] (q heads, k heads, v heads) -> out [batch,
+ * s_max, n_heads * 128] (activation type).  Query head h reads key/value head
+ * h / (n_heads / n_kv_heads); keys j >= seq_len[b] masked, and with causal != 0 keys j > i
+ * for query i; rows >= seq_len[b] of out written as 0.  n_heads 1..64, n_kv_heads divides
+ * n_heads, s_max * (n_heads + 2 n_kv_heads) * 256 <= 2^31 - 1 (else ZDIT_EUNSUPPORTED); ws:
+ * zdit_op_attn_gqa_workspace() bytes.  With n_kv_heads == n_heads and causal == 0 this is
+ * zdit_op_attn. */
+size_t zdit_op_attn_gqa_workspace(int32_t precision, int32_t batch, int32_t s_max, int32_t n_kv_heads);
+zdit_status zdit_op_attn_gqa(int32_t precision, int32_t batch, int32_t s_max, int32_t n_heads,
+                             int32_t n_kv_heads, int32_t causal, const int32_t* seq_len,
+                             const void* qkv, void* out, void* ws, size_t ws_bytes,
+                             void* hip_stream);
 
 #ifdef __cplusplus
 }

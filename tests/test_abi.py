@@ -176,3 +176,84 @@ def test_gemm_op_rejects_unsupported_k():
     assert L.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_STORE, 16, 16, 40, p, p, None, None, p, None) == Z.ZDIT_EUNSUPPORTED
     assert L.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, 16, 16, 64, p, p, None, None, p, None) == Z.ZDIT_EINVAL
     assert L.zdit_op_gemm(Z.ZDIT_BF16, 9, 16, 16, 64, p, p, None, None, p, None) == Z.ZDIT_EINVAL
+
+
+# ---------------------------------------------------------------- text encoder entry points
+def _enc_setup(**over):
+    ed = synth.ENC_TINY.replace(**over)
+    cfg = Z.make_enc_cfg(ed)
+    lw = (Z.zdit_enc_layer_w * 4)()
+    for i in range(4):
+        for f, _ in Z.zdit_enc_layer_w._fields_:
+            setattr(lw[i], f, 4096 * (i + 1))  # aligned, never dereferenced: validation fails first
+    w = Z.zdit_enc_w()
+    w.embed = 1 << 20
+    w.layers = C.cast(lw, C.POINTER(Z.zdit_enc_layer_w))
+    return ed, cfg, w, lw
+
+
+def _enc_call(cfg, w, batch, max_len, ids, lens, out=1 << 16, ws_bytes=1 << 30):
+    L = Z.lib()
+    ids = np.ascontiguousarray(ids, np.int32)
+    return L.zdit_encoder_fwd(C.byref(cfg), C.byref(w), batch, max_len,
+                              ids.ctypes.data_as(C.POINTER(C.c_int32)), Z.i32_array(lens),
+                              C.c_void_p(out), C.c_void_p(1 << 24), ws_bytes, None)
+
+
+def test_encoder_workspace_query():
+    ed, cfg, _, _ = _enc_setup()
+    n = Z.zdit_encoder_workspace(cfg, 2, 64)
+    # at least the fp32-free activations: h, qkv, attention output, tables and ids
+    M = 2 * 64
+    assert n >= M * ed.hidden * 2 + M * (ed.n_heads + 2 * ed.n_kv_heads) * 128 * 2
+    assert Z.zdit_encoder_workspace(cfg, 0, 64) == 0
+    bad = Z.make_enc_cfg(synth.ENC_TINY.replace(head_dim=64))
+    assert Z.zdit_encoder_workspace(bad, 2, 64) == 0
+
+
+def test_encoder_rejects_bad_arguments_before_launch():
+    ed, cfg, w, _ = _enc_setup()
+    ids = synth.token_ids(2, 16, [9, 4], ed.vocab, 0)
+    assert _enc_call(cfg, w, 2, 16, ids, [0, 4]) == Z.ZDIT_EINVAL          # empty row
+    assert _enc_call(cfg, w, 2, 16, ids, [17, 4]) == Z.ZDIT_EINVAL         # past max_len
+    bad_ids = ids.copy(); bad_ids[1, 3] = ed.vocab
+    assert _enc_call(cfg, w, 2, 16, bad_ids, [9, 4]) == Z.ZDIT_EINVAL      # id out of range
+    assert "ids[1][3]" in Z.last_error()
+    neg = ids.copy(); neg[0, 0] = -1
+    assert _enc_call(cfg, w, 2, 16, neg, [9, 4]) == Z.ZDIT_EINVAL
+    assert _enc_call(cfg, w, 2, 16, ids, [9, 4], ws_bytes=1024) == Z.ZDIT_EWORKSPACE
+    assert _enc_call(cfg, w, 0, 16, ids, [9, 4]) == Z.ZDIT_EINVAL
+    _, cfg2, w2, lw2 = _enc_setup()
+    lw2[1].w_up = None
+    assert _enc_call(cfg2, w2, 2, 16, ids, [9, 4]) == Z.ZDIT_EINVAL
+    assert "layer 1" in Z.last_error() and "w_up" in Z.last_error()
+    _, cfg3, w3, _ = _enc_setup(n_kv_heads=3)
+    assert _enc_call(cfg3, w3, 2, 16, ids, [9, 4]) == Z.ZDIT_EINVAL
+    _, cfg4, w4, _ = _enc_setup(head_dim=64)
+    assert _enc_call(cfg4, w4, 2, 16, ids, [9, 4]) == Z.ZDIT_EUNSUPPORTED
+    _, cfg5, w5, _ = _enc_setup(inter=500)
+    assert _enc_call(cfg5, w5, 2, 16, ids, [9, 4]) == Z.ZDIT_EUNSUPPORTED
+
+
+def test_encoder_ops_reject_bad_arguments_before_launch():
+    L = Z.lib()
+    ids = np.zeros((1, 8), np.int32)
+    pids = ids.ctypes.data_as(C.POINTER(C.c_int32))
+    # id past the vocabulary; dim not a multiple of 8
+    ids[0, 2] = 50
+    assert L.zdit_op_embed(1, 8, 64, 50, pids, Z.i32_array([8]), C.c_void_p(4096), C.c_void_p(8192),
+                           C.c_void_p(1 << 20), 1 << 20, None) == Z.ZDIT_EINVAL
+    ids[0, 2] = 0
+    assert L.zdit_op_embed(1, 8, 60, 50, pids, Z.i32_array([8]), C.c_void_p(4096), C.c_void_p(8192),
+                           C.c_void_p(1 << 20), 1 << 20, None) == Z.ZDIT_EINVAL
+    # n_kv_heads must divide n_heads; seq_len within s_max
+    assert L.zdit_op_attn_gqa(0, 1, 64, 6, 4, 1, Z.i32_array([64]), C.c_void_p(4096), C.c_void_p(8192),
+                              C.c_void_p(1 << 20), 1 << 22, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_attn_gqa(0, 1, 64, 8, 2, 1, Z.i32_array([65]), C.c_void_p(4096), C.c_void_p(8192),
+                              C.c_void_p(1 << 20), 1 << 22, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_attn_gqa(0, 1, 64, 8, 2, 1, Z.i32_array([64]), C.c_void_p(4096), C.c_void_p(8192),
+                              C.c_void_p(1 << 20), 16, None) == Z.ZDIT_EWORKSPACE
+    assert L.zdit_op_qknorm_rope(1, 8, 4, 2, Z.i32_array([9]), C.c_void_p(4096), C.c_void_p(4096),
+                                 C.c_void_p(4096), C.c_void_p(4096), C.c_void_p(4096), 1e-6, None) == Z.ZDIT_EINVAL
+    assert L.zdit_rope_tables(4, Z.i32_array([128, 0, 0]), 1e6, 1, 8, 0, 0, Z.i32_array([8]),
+                              C.c_void_p(4096), C.c_void_p(8192), None) == Z.ZDIT_EINVAL

@@ -1,0 +1,257 @@
+"""Text-encoder parity on the GPU: the encoder's kernels (embedding gather, per-head q/k norm +
+RoPE, causal grouped-query attention) and the whole forward to hidden_states[-2], against the
+encoder oracle on the same seeded inputs.  Bit-exact where the contract is (gather, RoPE
+tables, pad-length and causality invariances); elsewhere within the bf16 tolerance of the
+DiT path (rel-L2 <= 1e-2 and mean |error| <= 0.025 RMS)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from diffusion_transformer_text_s3_amd import binding as Z
+from gpu_util import bf16_values, dev, drift, host, note, rel_l2
+from oracle import encoder_oracle as E
+
+pytestmark = pytest.mark.gpu
+BF, F32P = Z.ZDIT_BF16, Z.ZDIT_FP32_DEBUG
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _text_tables(batch, s_max, lens, theta=1e6):
+    cos = torch.empty((batch, s_max, 64), device="cuda")
+    sin = torch.empty_like(cos)
+    Z.zdit_rope_tables(Z.ZDIT_SEQ_TEXT, [128, 0, 0], theta, batch, s_max, 0, 0, lens, cos, sin)
+    return cos, sin
+
+
+# ------------------------------------------------------------------------------- tables
+def test_text_rope_tables_match_oracle():
+    lens = [300, 77]
+    note(f"text rope tables lens={lens}")
+    cos, sin = _text_tables(2, 300, lens)
+    c, s = host(cos), host(sin)
+    rc, rs = E.rope_tables_1d(300, 128, 1e6)
+    for b, L in enumerate(lens):
+        # float64 angles rounded once on both sides: at most one fp32 ulp apart
+        np.testing.assert_allclose(c[b, :L], rc[:L], rtol=0, atol=1.2e-7)
+        np.testing.assert_allclose(s[b, :L], rs[:L], rtol=0, atol=1.2e-7)
+        assert np.all(c[b, L:] == 1) and np.all(s[b, L:] == 0)
+
+
+# ------------------------------------------------------------------------------- embedding
+def test_embed_gather_exact_and_padding_zero():
+    vocab, dim, lens, L = 1000, 256, [37, 5, 64], 64
+    note(f"embed vocab={vocab} dim={dim} lens={lens}")
+    table = bf16_values(_rng(1).standard_normal((vocab, dim)).astype(np.float32))
+    ids = synth.token_ids(3, L, lens, vocab, 2)
+    ids[0, 0], ids[1, 4] = vocab - 1, 0
+    out = torch.full((3, L, dim), 7.0, device="cuda")
+    ws = Z.workspace(Z.zdit_op_embed_workspace(3, L))
+    Z.zdit_op_embed(3, L, dim, vocab, ids, lens, dev(table, torch.bfloat16), out, ws)
+    got = host(out)
+    for b, n in enumerate(lens):
+        np.testing.assert_array_equal(got[b, :n], table[ids[b, :n]])
+        assert np.all(got[b, n:] == 0)
+
+
+# ------------------------------------------------------------------------------- q/k norm + RoPE
+def test_qknorm_rope_matches_oracle_within_one_bf16_ulp():
+    B, S, nq, nkv = 2, 70, 8, 2
+    lens = [70, 33]
+    note(f"qknorm+rope B={B} S={S} nq={nq} nkv={nkv} lens={lens}")
+    g = _rng(3)
+    W = (nq + 2 * nkv) * 128
+    x = bf16_values((g.standard_normal((B, S, W)) * 2.0).astype(np.float32))
+    gq = (1 + 0.1 * g.standard_normal(128)).astype(np.float32)
+    gk = (1 + 0.1 * g.standard_normal(128)).astype(np.float32)
+    cos, sin = _text_tables(B, S, lens)
+    t = dev(x, torch.bfloat16)
+    Z.zdit_op_qknorm_rope(B, S, nq, nkv, lens, t, dev(gq), dev(gk), cos, sin, 1e-6)
+    got = host(t)
+    rc, rs = E.rope_tables_1d(S)
+    for b, L in enumerate(lens):
+        q = x[b, :L, :nq * 128].reshape(L, nq, 128)
+        k = x[b, :L, nq * 128:(nq + nkv) * 128].reshape(L, nkv, 128)
+        rq = E.rope_rotate_half(E.head_norm(q, gq, 1e-6), rc[:L], rs[:L]).reshape(L, -1)
+        rk = E.rope_rotate_half(E.head_norm(k, gk, 1e-6), rc[:L], rs[:L]).reshape(L, -1)
+        for part, ref in ((got[b, :L, :nq * 128], rq), (got[b, :L, nq * 128:(nq + nkv) * 128], rk)):
+            # one rounding to bf16 of an fp32 value within a few fp32 ulps of the oracle's
+            err = np.abs(part - ref)
+            assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6), err.max()
+        np.testing.assert_array_equal(got[b, :L, (nq + nkv) * 128:], x[b, :L, (nq + nkv) * 128:])  # v untouched
+        np.testing.assert_array_equal(got[b, L:], x[b, L:])  # rows past the length untouched
+
+
+# ------------------------------------------------------------------------------- attention
+def _gqa_qkv(B, S, nq, nkv, seed, scale=1.0):
+    g = _rng(seed)
+    W = (nq + 2 * nkv) * 128
+    x = g.standard_normal((B, S, W)).astype(np.float32)
+    x[:, :, :(nq + nkv) * 128] *= scale
+    return bf16_values(x)
+
+
+def _attn_ref(x, L, nq, nkv, causal):
+    q = x[:L, :nq * 128].reshape(L, nq, 128)
+    k = x[:L, nq * 128:(nq + nkv) * 128].reshape(L, nkv, 128)
+    v = x[:L, (nq + nkv) * 128:].reshape(L, nkv, 128)
+    if causal:
+        return E.causal_gqa_attention(q, k, v).reshape(L, nq * 128)
+    g = nq // nkv
+    kk, vv = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    from oracle import attention
+    return attention(q, kk, vv).reshape(L, nq * 128)
+
+
+def _run_gqa(prec, x, B, S, nq, nkv, causal, lens):
+    dt = torch.bfloat16 if prec == BF else torch.float32
+    out = torch.full((B, S, nq * 128), 7.0, dtype=dt, device="cuda")
+    ws = Z.workspace(Z.zdit_op_attn_gqa_workspace(prec, B, S, nkv))
+    Z.zdit_op_attn_gqa(prec, B, S, nq, nkv, causal, lens, dev(x, dt), out, ws)
+    return host(out)
+
+
+@pytest.mark.parametrize("nq,nkv,causal", [(8, 2, 1), (8, 2, 0), (4, 4, 1), (32, 8, 1)])
+def test_attn_gqa_matches_oracle(nq, nkv, causal):
+    B, S, lens = 2, 200, [200, 131]
+    note(f"attn gqa nq={nq} nkv={nkv} causal={causal} lens={lens}")
+    x = _gqa_qkv(B, S, nq, nkv, 10 + nq + nkv + causal)
+    got = _run_gqa(BF, x, B, S, nq, nkv, causal, lens)
+    for b, L in enumerate(lens):
+        ref = _attn_ref(x[b], L, nq, nkv, causal)
+        assert rel_l2(got[b, :L], ref) < 1e-2
+        assert np.abs(got[b, :L] - ref).max() < 0.05
+        assert np.all(got[b, L:] == 0)
+
+
+def test_attn_gqa_causal_key_block_counts():
+    """Causal masking with tiles whose first query sits in every position of the key loop
+    (1 .. 9 key blocks, ragged last blocks), large scores so the running max moves."""
+    S, nq, nkv = 544, 4, 2
+    lens = [1, 63, 64, 65, 200, 257, 300, 513, 544]
+    note(f"attn gqa causal block counts lens={lens}")
+    x = _gqa_qkv(len(lens), S, nq, nkv, 20, scale=2.0)
+    got = _run_gqa(BF, x, len(lens), S, nq, nkv, 1, lens)
+    for b, L in enumerate(lens):
+        ref = _attn_ref(x[b], L, nq, nkv, True)
+        assert rel_l2(got[b, :L], ref) < 1e-2, L
+        assert np.abs(got[b, :L] - ref).max() < 0.05, L
+        assert np.all(got[b, L:] == 0)
+
+
+def test_attn_gqa_fp32_debug_path():
+    B, S, nq, nkv, lens = 2, 90, 8, 2, [90, 41]
+    note("attn gqa fp32 debug causal")
+    x = _gqa_qkv(B, S, nq, nkv, 30)
+    got = _run_gqa(F32P, x, B, S, nq, nkv, 1, lens)
+    for b, L in enumerate(lens):
+        np.testing.assert_allclose(got[b, :L], _attn_ref(x[b], L, nq, nkv, True), rtol=1e-5, atol=1e-5)
+
+
+def test_attn_gqa_equals_dit_attention_when_heads_match():
+    """n_kv_heads == n_heads and no causal mask is the DiT's joint attention, bit for bit."""
+    B, S, nh, lens = 2, 160, 3, [160, 97]
+    note("attn gqa == dit attention")
+    x = _gqa_qkv(B, S, nh, nh, 40)
+    got = _run_gqa(BF, x, B, S, nh, nh, 0, lens)
+    out = torch.empty((B, S, nh * 128), dtype=torch.bfloat16, device="cuda")
+    ws = Z.workspace(Z.zdit_op_attn_workspace(BF, B, S, nh))
+    Z.zdit_op_attn(BF, B, S, nh, lens, dev(x, torch.bfloat16), out, ws)
+    np.testing.assert_array_equal(got, host(out))
+
+
+def test_attn_gqa_causal_ignores_later_tokens_bit_exact():
+    B, S, nq, nkv, L = 1, 300, 8, 2, 300
+    note("attn gqa causal: later tokens change nothing")
+    x = _gqa_qkv(B, S, nq, nkv, 50)
+    a = _run_gqa(BF, x, B, S, nq, nkv, 1, [L])
+    y = x.copy()
+    y[:, 150:, nq * 128:] = bf16_values(_rng(51).standard_normal(y[:, 150:, nq * 128:].shape).astype(np.float32) * 5)
+    b = _run_gqa(BF, y, B, S, nq, nkv, 1, [L])
+    np.testing.assert_array_equal(a[0, :150], b[0, :150])
+    assert not np.array_equal(a[0, 150:], b[0, 150:])
+
+
+# ------------------------------------------------------------------------------- whole encoder
+def _encoder_run(ed, W, ids, lens, max_len=None):
+    B = ids.shape[0]
+    L = ids.shape[1] if max_len is None else max_len
+    if L != ids.shape[1]:
+        wide = np.zeros((B, L), np.int32)
+        wide[:, :ids.shape[1]] = ids
+        ids = wide
+    m = Z.upload_encoder(W)
+    cfg = Z.make_enc_cfg(ed)
+    out = torch.full((B, L, ed.hidden), 3.0, device="cuda")
+    ws = Z.workspace(Z.zdit_encoder_workspace(cfg, B, L))
+    Z.zdit_encoder_fwd(cfg, m, B, L, ids, lens, out, ws)
+    return host(out)
+
+
+def _check_vs_oracle(got, ref, lens):
+    for b, L in enumerate(lens):
+        assert rel_l2(got[b, :L], ref[b, :L]) <= 1e-2
+        assert drift(got[b, :L], ref[b, :L]) <= 0.025
+        assert np.all(got[b, L:] == 0)
+
+
+def test_encoder_tiny_matches_oracle():
+    ed = synth.ENC_TINY
+    lens = [37, 12]
+    note(f"encoder tiny {ed} lens={lens}")
+    W = synth.encoder_weights(ed, 5, ed.n_layers - 1)
+    ids = synth.token_ids(2, 40, lens, ed.vocab, 6)
+    got = _encoder_run(ed, W, ids, lens)
+    _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)
+
+
+def test_encoder_tiny_deep_matches_oracle():
+    """A 12-block tiny encoder (11 computed): bf16 drift stays within the tolerance."""
+    ed = synth.ENC_TINY.replace(n_layers=12)
+    lens = [64, 29, 1]
+    note(f"encoder tiny deep lens={lens}")
+    W = synth.encoder_weights(ed, 7, ed.n_layers - 1)
+    ids = synth.token_ids(3, 64, lens, ed.vocab, 8)
+    got = _encoder_run(ed, W, ids, lens)
+    _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)
+
+
+def test_encoder_valid_rows_do_not_depend_on_padding_length():
+    ed = synth.ENC_TINY
+    lens = [33, 7]
+    note("encoder pad-length independence")
+    W = synth.encoder_weights(ed, 9, ed.n_layers - 1)
+    ids = synth.token_ids(2, 33, lens, ed.vocab, 10)
+    a = _encoder_run(ed, W, ids, lens)
+    b = _encoder_run(ed, W, ids, lens, max_len=97)
+    for i, L in enumerate(lens):
+        np.testing.assert_array_equal(a[i, :L], b[i, :L])
+    assert np.all(b[:, 33:] == 0)
+
+
+def test_encoder_is_causal_bit_exact():
+    ed = synth.ENC_TINY
+    note("encoder causality")
+    W = synth.encoder_weights(ed, 11, ed.n_layers - 1)
+    ids = synth.token_ids(1, 48, [48], ed.vocab, 12)
+    a = _encoder_run(ed, W, ids, [48])
+    ids2 = ids.copy()
+    ids2[0, 20:] = (ids2[0, 20:] + 17) % ed.vocab
+    b = _encoder_run(ed, W, ids2, [48])
+    np.testing.assert_array_equal(a[0, :20], b[0, :20])
+    assert not np.array_equal(a[0, 20:], b[0, 20:])
+
+
+def test_encoder_full_width_two_blocks_matches_oracle():
+    """The pinned encoder's widths (hidden 2560, 32 / 8 heads, intermediate 9728), two blocks,
+    on the DiT's caption lengths (a 45-token prompt and a 10-token negative)."""
+    ed = synth.ENC_FULL.replace(n_layers=3, vocab=4096)
+    lens = [45, 10]
+    note(f"encoder full width 2 blocks lens={lens}")
+    W = synth.encoder_weights(ed, 13, ed.n_layers - 1)
+    ids = synth.token_ids(2, 64, lens, ed.vocab, 14)
+    got = _encoder_run(ed, W, ids, lens)
+    _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)

@@ -244,6 +244,48 @@ def test_attention_ragged(prec):
         assert np.all(got[b, seq[b]:] == 0)
 
 
+def test_attention_key_block_counts():
+    """Branches whose valid keys span 1, 2, 3, 4, 5 and 6 blocks of 64 (every first / last /
+    next-to-last block arrangement of the key loop), with ragged final blocks."""
+    S, nh = 384, 2
+    seq = [1, 64, 65, 129, 200, 257, 300, 384]
+    B = len(seq)
+    note(f"attention key block counts seq={seq}")
+    qkv = _qkv(B, S, nh, 23)
+    out = torch.full((B, S, nh * 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = Z.workspace(Z.zdit_op_attn_workspace(BF, B, S, nh))
+    Z.zdit_op_attn(BF, B, S, nh, seq, dev(qkv, torch.bfloat16), out, ws)
+    got = host(out)
+    for b in range(B):
+        ref = _attn_ref(qkv[b], seq[b], nh)
+        assert rel_l2(got[b, :seq[b]], ref) < 1e-2, seq[b]
+        assert np.abs(got[b, :seq[b]] - ref).max() < 0.05, seq[b]
+        assert np.all(got[b, seq[b]:] == 0)
+
+
+def test_attention_rising_scores_rescale():
+    """Scores that grow along the keys (key norms ramp up, large query norms), so the running
+    maximum keeps rising by more than the lazy-rescale threshold from block to block."""
+    B, S, nh = 2, 448, 2
+    seq = [448, 390]
+    note(f"attention rising scores seq={seq}")
+    g = _rng(24)
+    x = g.standard_normal((B, S, 3 * nh * 128)).astype(np.float32)
+    D = nh * 128
+    x[:, :, :D] *= 3.0
+    x[:, :, D:2 * D] *= (1.0 + 4.0 * np.arange(S, dtype=np.float32) / S)[None, :, None]
+    qkv = bf16_values(x)
+    out = torch.empty((B, S, D), dtype=torch.bfloat16, device="cuda")
+    ws = Z.workspace(Z.zdit_op_attn_workspace(BF, B, S, nh))
+    Z.zdit_op_attn(BF, B, S, nh, seq, dev(qkv, torch.bfloat16), out, ws)
+    got = host(out)
+    for b in range(B):
+        ref = _attn_ref(qkv[b], seq[b], nh)
+        assert rel_l2(got[b, :seq[b]], ref) < 1e-2
+        assert np.abs(got[b, :seq[b]] - ref).max() < 0.05
+        assert np.all(got[b, seq[b]:] == 0)
+
+
 def test_attention_padding_contents_are_invisible():
     """NaN in the batch-alignment padding rows changes no valid output bit."""
     B, S, nh = 2, 192, 2
