@@ -7,7 +7,10 @@ the timed region.  Prints one JSON line; its value is TFLOP/s over the FLOPs the
 (the shared image path and the step-invariant caption path are reused exactly, so those are
 counted once), its ms_per_step the wall time of one pass.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder]
+
+--workload encoder times the text encoder instead (its own JSON line): the Qwen3-4B-shaped
+decoder on two right-padded rows of 64 ids (45 and 10 valid) to hidden_states[-2].
 """
 from __future__ import annotations
 
@@ -187,6 +190,122 @@ def cpu_baseline(dims):
             "seconds": round(dt, 2)}
 
 
+ENC_METRIC = "text-encoder forwards/s to hidden_states[-2] (35 of 36 Qwen3-4B-shaped blocks, B=2, L_max 64)"
+
+
+def random_encoder_on_device(ed, n_blocks, seed):
+    """Seeded N(0, 0.02) bf16 matrices, N(0, 1) bf16 embedding rows, gains 1 + 0.02 N(0, 1),
+    generated on the device."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    D, I, hd = ed.hidden, ed.inter, ed.head_dim
+    nq, nkv = ed.n_heads * hd, ed.n_kv_heads * hd
+    mat = lambda r, c, std=0.02: (torch.randn((r, c), generator=g, device="cuda") * std).to(torch.bfloat16)
+    vec = lambda n: torch.randn(n, generator=g, device="cuda") * 0.02 + 1.0
+    layers = [{"in_norm": vec(D), "w_qkv": mat(nq + 2 * nkv, D), "q_norm": vec(hd), "k_norm": vec(hd),
+               "w_o": mat(D, nq), "post_norm": vec(D), "w_gate": mat(I, D), "w_up": mat(I, D),
+               "w_down": mat(D, I)} for _ in range(n_blocks)]
+    return Z.DeviceEncoder(mat(ed.vocab, D, 1.0), layers)
+
+
+def encoder_block_bytes(ed, M):
+    """HBM bytes one encoder block moves at M rows if every tensor is read or written once:
+    the bf16 weights, the bf16 activations between its kernels, the fp32 residual stream
+    read and written by the two residual GEMMs and the two norms."""
+    D, I, hd = ed.hidden, ed.inter, ed.head_dim
+    W = (ed.n_heads + 2 * ed.n_kv_heads) * hd
+    weights = 2 * (W * D + D * ed.n_heads * hd + 3 * I * D)
+    acts = 2 * M * (2 * D + 2 * W + 2 * ed.n_heads * hd + I + I) + 4 * M * D * 6
+    return weights + acts
+
+
+def encoder_bench(args):
+    """The text encoder at its pinned shape on the DiT's two caption rows."""
+    import numpy as np
+    import torch
+    import synth
+    from diffusion_transformer_text_s3_amd import binding as Z
+    ed = synth.ENC_FULL
+    B, L, lens = 2, 64, [45, 10]
+    nb = ed.n_layers - 1
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    m = random_encoder_on_device(ed, nb, args.seed)
+    ids = synth.token_ids(B, L, lens, ed.vocab, args.seed)
+    cfg = Z.make_enc_cfg(ed)
+    out = torch.empty((B, L, ed.hidden), device="cuda")
+    ws = Z.workspace(Z.zdit_encoder_workspace(cfg, B, L))
+    step = lambda: Z.zdit_encoder_fwd(cfg, m, B, L, ids, lens, out, ws, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    finite = bool(np.isfinite(out.cpu().numpy()).all())
+
+    # dominant kernel: the down projection (residual GEMM, K = 9728) at M = 128 rows
+    M, D, I = B * L, ed.hidden, ed.inter
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    A = torch.randn((M, I), generator=g, device="cuda").to(torch.bfloat16)
+    Wd = (torch.randn((D, I), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    X = torch.zeros((M, D), device="cuda")
+    gws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, M, D, I))
+    g_ms = time_op(lambda: Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, M, D, I, A, Wd, None, None, X, gws, stream),
+                   20, stream)
+    g_bytes = 2 * D * I + 2 * M * I + 2 * 4 * M * D
+    achieved = g_bytes / (g_ms * 1e-3) / 1e9
+    blk_bytes = encoder_block_bytes(ed, M)
+    rec = {
+        "metric": ENC_METRIC, "value": round(1.0 / dt, 2), "unit": "forwards/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded uniform token ids, random-init bf16 weights)",
+        "config": {"workload": "text encoder, B=2 right-padded rows of 64 ids (45 and 10 valid), hidden 2560, "
+                               "intermediate 9728, 32 / 8 heads, 35 blocks to hidden_states[-2]",
+                   "tokens": sum(lens), "weight_gb": round(nb * encoder_block_bytes(ed, 0) / 1e9, 3)},
+        "hbm_gbs_whole_forward": round(nb * blk_bytes / dt / 1e9, 1),
+        "roofline": {"kernel": "gemm_splitk_kernel + splitk_reduce_kernel<EPI_RESID> (down projection, 13 K "
+                               "ranges), M=128 N=2560 K=9728",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "avg_launch_ms": round(g_ms, 4),
+                     "traffic": traffic_from_profiles("gemm_enc_down")},
+        "output_finite": finite,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = encoder_cpu_baseline(ed, lens, nb)
+    print(json.dumps(rec), flush=True)
+
+
+def encoder_cpu_baseline(ed, lens, nb):
+    """The encoder oracle (as it stands) on the same two rows: its whole forward to
+    hidden_states[-2], with one block's weights reused for all 35 blocks and a 4096-row
+    embedding table (neither changes the arithmetic per block)."""
+    import numpy as np
+    import synth
+    from oracle import encoder_oracle as E
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    edc = ed.replace(vocab=4096)
+    w = synth.encoder_layer_weights(edc, 1, 0)
+    W = {"embed": synth.bf16_truncate(synth.residual_input((edc.vocab, edc.hidden), 1)), "layers": [w] * nb}
+    ids = synth.token_ids(len(lens), max(lens), lens, edc.vocab, 1)
+    t0 = time.perf_counter()
+    E.encoder_penultimate(ids, lens, W, edc)
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 4), "unit": "forwards/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the oracle's whole forward (fp32 NumPy) on rows of {lens[0]} and {lens[1]} tokens, "
+                      f"{nb} blocks sharing one block's weights", "seconds": round(dt, 2)}
+
+
 def kernel_only(which):
     """Three launches of the SwiGLU GEMM at the main-block 1024^2 pair shape, or three plain
     device copies of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written)."""
@@ -217,7 +336,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", choices=["1024", "1536"], default="1024")
+    ap.add_argument("--workload", choices=["1024", "1536", "encoder"], default="1024",
+                    help="the DiT pass at 1024^2 (default) or 1536x1024, or the text encoder forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--kernel-only", choices=["swiglu", "copy"], default=None,
@@ -236,6 +356,9 @@ def main():
 
     if args.kernel_only:
         kernel_only(args.kernel_only)
+        return
+    if args.workload == "encoder":
+        encoder_bench(args)
         return
 
     wl = synth.CFG5 if args.workload == "1024" else synth.CFG5_WIDE

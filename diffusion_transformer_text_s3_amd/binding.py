@@ -28,6 +28,7 @@ EXPORTS = [
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
     "zdit_encoder_workspace", "zdit_encoder_fwd", "zdit_op_embed_workspace", "zdit_op_embed",
     "zdit_op_qknorm_rope", "zdit_op_attn_gqa_workspace", "zdit_op_attn_gqa",
+    "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk",
 ]
 
 
@@ -130,6 +131,8 @@ def lib():
             "zdit_op_qknorm_rope": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, vp, vp, f32, vp]),
             "zdit_op_attn_gqa_workspace": (sz, [i32, i32, i32, i32]),
             "zdit_op_attn_gqa": (i32, [i32, i32, i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
+            "zdit_op_gemm_splitk_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_gemm_splitk": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -453,3 +456,12 @@ def zdit_op_attn_gqa(precision, batch, s_max, n_heads, n_kv_heads, causal, seq_l
     return check(lib().zdit_op_attn_gqa(precision, batch, s_max, n_heads, n_kv_heads, int(causal),
                                         i32_array(seq_len), ptr(qkv), ptr(out), ptr(ws), ws.numel(),
                                         stream_handle(stream)))
+
+
+def zdit_op_gemm_splitk_workspace(epilogue, M, N, K) -> int:
+    return lib().zdit_op_gemm_splitk_workspace(epilogue, M, N, K)
+
+
+def zdit_op_gemm_splitk(epilogue, M, N, K, A, B, B2, vec, Cout, ws, stream=None):
+    return check(lib().zdit_op_gemm_splitk(epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
+                                           ptr(ws), ws.numel(), stream_handle(stream)))

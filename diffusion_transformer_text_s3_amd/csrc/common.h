@@ -54,6 +54,25 @@ struct GemmArgs {
 hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const GemmArgs& g, hipStream_t s);
 
+// Split-K GEMM for few rows (M <= 256; N % 8 == 0, K % 64 == 0): fp32 partials of
+// [splits][M][Nv] in `part`, then a fixed-order sum and the epilogue (EPI_STORE, EPI_RESID,
+// EPI_SWIGLU; output through g.out as in the main GEMM).  The split of K depends on N and K
+// only.
+struct SplitKArgs {
+  const void* A;
+  const void* B;
+  const void* B2;
+  float* part;
+  int M, N, K, lda, ldb;
+  int ks;         // K columns per split (multiple of 32)
+  int splits;
+  int col_tiles;  // 64-column tiles per weight
+  int Nv;         // partial row width: N, or 2N for SwiGLU (W3 columns after W1's)
+};
+SplitKArgs splitk_plan(int epi, int M, int N, int K);
+size_t splitk_workspace(int epi, int M, int N, int K);
+hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s);
+
 // q, k, v rows: row r of branch b at qkv + (b * s_max + r) * row_stride elements, query head
 // h at column h * 128, key head j at k_col + j * 128, value head j at v_col + j * 128.  Query
 // head h reads key/value head h / (n_heads / n_kv_heads).  Zero row_stride / k_col / v_col /

@@ -34,13 +34,28 @@ int qkv_width(const zdit_enc_cfg& c) { return (c.n_heads + 2 * c.n_kv_heads) * k
 // the K resource of the attention kernel spans s_max rows of the qkv buffer in bytes
 bool qkv_fits(int64_t s_max, int64_t width) { return s_max * width * 2 <= INT32_MAX; }
 
+// Rows up to which the projections run as split-K GEMMs (the weights then stream from HBM
+// through ~512 workgroups instead of a few dozen 256 x 256 tiles).
+constexpr int kSplitKMaxRows = 256;
+
 struct EncPlan {
-  size_t ids, cos, sin, h, qkv, vt, o, u, total;
+  size_t ids, cos, sin, h, qkv, vt, o, u, part, total;
+  bool splitk;
 };
+
+size_t enc_part_bytes(const zdit_enc_cfg& c, int M) {
+  const int D = c.hidden, Dq = c.n_heads * kHeadDim;
+  size_t b = splitk_workspace(EPI_STORE, M, qkv_width(c), D);
+  b = std::max(b, splitk_workspace(EPI_RESID, M, D, Dq));
+  b = std::max(b, splitk_workspace(EPI_SWIGLU, M, c.inter, D));
+  b = std::max(b, splitk_workspace(EPI_RESID, M, D, c.inter));
+  return b;
+}
 
 EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   const size_t M = (size_t)B * L;
   EncPlan p;
+  p.splitk = M <= (size_t)kSplitKMaxRows;
   size_t off = 0;
   p.ids = off; off += al256(M * 4);
   p.cos = off; off += al256(M * 64 * 4);
@@ -52,8 +67,15 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   p.o = off;   off += al256(M * c.n_heads * kHeadDim * 2);
   p.u = r0;  // the SwiGLU activation reuses the attention region (dead by then)
   off = std::max(off, r0 + al256(M * (size_t)c.inter * 2));
+  p.part = off;
+  if (p.splitk) off += al256(enc_part_bytes(c, (int)M));
   p.total = off;
   return p;
+}
+
+// a projection of the block: split-K for few rows, else the main GEMM
+hipError_t enc_gemm(int epi, const GemmArgs& g, const EncPlan& pl, char* ws, hipStream_t st) {
+  return pl.splitk ? launch_gemm_splitk(epi, g, (float*)(ws + pl.part), st) : launch_gemm_bf16(epi, g, st);
 }
 
 zdit_status check_ids(int batch, int max_len, int vocab, const int32_t* ids, const int32_t* len) {
@@ -108,7 +130,7 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   GemmArgs g{};
   g.A = h; g.B = w.w_qkv; g.C = qkv; g.M = M; g.N = W; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, W);
-  HIP_TRY(launch_gemm_bf16(EPI_STORE, g, st));
+  HIP_TRY(enc_gemm(EPI_STORE, g, pl, ws, st));
 
   QkNormRopeArgs qa;
   qa.qkv = qkv; qa.row_stride = W; qa.k_col = Dq; qa.n_heads = c.n_heads; qa.n_kv_heads = c.n_kv_heads;
@@ -124,7 +146,7 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   for (int b = 0; b < kMaxBatch; ++b) xr.valid[b] = b < B ? len[b] : 0;
   g = GemmArgs{};
   g.A = o; g.B = w.w_o; g.C = x; g.M = M; g.N = D; g.K = Dq; g.lda = Dq; g.ldb = Dq; g.out = xr;
-  HIP_TRY(launch_gemm_bf16(EPI_RESID, g, st));
+  HIP_TRY(enc_gemm(EPI_RESID, g, pl, ws, st));
 
   na.gain = w.post_norm;
   HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
@@ -132,11 +154,11 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   g = GemmArgs{};
   g.A = h; g.B = w.w_gate; g.B2 = w.w_up; g.C = u; g.M = M; g.N = I; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, I);
-  HIP_TRY(launch_gemm_bf16(EPI_SWIGLU, g, st));
+  HIP_TRY(enc_gemm(EPI_SWIGLU, g, pl, ws, st));
 
   g = GemmArgs{};
   g.A = u; g.B = w.w_down; g.C = x; g.M = M; g.N = D; g.K = I; g.lda = I; g.ldb = I; g.out = xr;
-  HIP_TRY(launch_gemm_bf16(EPI_RESID, g, st));
+  HIP_TRY(enc_gemm(EPI_RESID, g, pl, ws, st));
   return ZDIT_OK;
 }
 
@@ -190,6 +212,34 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
     return s;
   for (int i = 0; i < c.n_layers - 1; ++i)
     if (zdit_status s = enc_block(c, w->layers[i], batch, max_len, len, hidden_out, pl, base, st)) return s;
+  return ok();
+}
+
+size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || M > kSplitKMaxRows || N < 8 || K < 64) return 0;
+  if (epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU) return 0;
+  return splitk_workspace(epilogue, M, N, K) + 256;
+}
+
+zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                                const void* B2, const float* vec, void* C, void* ws, size_t ws_bytes,
+                                void* hip_stream) {
+  if (epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU)
+    return fail(ZDIT_EINVAL, "epilogue %d", epilogue);
+  if (M < 1 || N < 1 || K < 1) return fail(ZDIT_EINVAL, "M %d N %d K %d", M, N, K);
+  if (M > kSplitKMaxRows || N % 8 || K % 64 || (int64_t)N * K * 2 > INT32_MAX)
+    return fail(ZDIT_EUNSUPPORTED, "M %d (<= %d), N %d (multiple of 8), K %d (multiple of 64)", M, kSplitKMaxRows,
+                N, K);
+  if (!A || !B || !C || (epilogue == ZDIT_EPI_SWIGLU && !B2)) return fail(ZDIT_EINVAL, "NULL operand");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (B2 && !aligned16(B2)) || (vec && !aligned16(vec)))
+    return fail(ZDIT_EINVAL, "operand not 16-byte aligned");
+  if (!ws || ws_bytes < zdit_op_gemm_splitk_workspace(epilogue, M, N, K)) return fail(ZDIT_EWORKSPACE, "workspace too small");
+  GemmArgs g{};
+  g.A = A; g.B = B; g.B2 = B2; g.C = C; g.M = M; g.N = N; g.K = K; g.lda = K; g.ldb = K;
+  g.vec = epilogue == ZDIT_EPI_RESID ? vec : nullptr;
+  g.out = compact_rows(M, N);
+  float* part = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  HIP_TRY(launch_gemm_splitk(epilogue, g, part, (hipStream_t)hip_stream));
   return ok();
 }
 

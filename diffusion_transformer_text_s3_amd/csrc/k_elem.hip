@@ -35,25 +35,30 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v));
 constexpr int kNormMaxChunks = 16;
 constexpr int kNormRowsPerBlock = 16;
 
-template <typename TO>
+// STAGED: 16 rows per workgroup with gain / shift / scale staged in LDS (many rows).  Else one
+// row per wavefront, 4 per workgroup, the vectors read from global memory where they stay in
+// L2 (few rows: more workgroups, no staging to amortise).
+template <typename TO, bool STAGED>
 __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(NormArgs a) {
-  __shared__ float4 vg[1024], vsh[1024], vsc[1024];
+  constexpr int kRows = STAGED ? kNormRowsPerBlock : 4;
+  __shared__ float4 vg_[STAGED ? 1024 : 1], vsh_[STAGED ? 1024 : 1], vsc_[STAGED ? 1024 : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.y;
   const int nchunk = a.dim >> 2;
   const bool mod = a.shift != nullptr;
-  {
-    const float4* g = (const float4*)a.gain;
-    const float4* sh = mod ? (const float4*)(a.shift + b * a.mod_bstride) : nullptr;
-    const float4* sc = mod ? (const float4*)(a.scale + b * a.mod_bstride) : nullptr;
+  const float4* vg = (const float4*)a.gain;
+  const float4* vsh = mod ? (const float4*)(a.shift + b * a.mod_bstride) : nullptr;
+  const float4* vsc = mod ? (const float4*)(a.scale + b * a.mod_bstride) : nullptr;
+  if constexpr (STAGED) {
     for (int c = threadIdx.x; c < nchunk; c += 256) {
-      vg[c] = g[c];
-      if (mod) { vsh[c] = sh[c]; vsc[c] = sc[c]; }
+      vg_[c] = vg[c];
+      if (mod) { vsh_[c] = vsh[c]; vsc_[c] = vsc[c]; }
     }
+    __syncthreads();
+    vg = vg_; vsh = vsh_; vsc = vsc_;
   }
-  __syncthreads();
-  for (int i = 0; i < kNormRowsPerBlock / 4; ++i) {
-    const int r = blockIdx.x * kNormRowsPerBlock + i * 4 + wave;
+  for (int i = 0; i < kRows / 4; ++i) {
+    const int r = blockIdx.x * kRows + i * 4 + wave;
     if (r >= a.rows_per_batch) break;
     const int64_t m = (int64_t)b * a.rows_per_batch + r;
     TO* out = (TO*)a.out + m * a.dim;
@@ -363,9 +368,15 @@ inline unsigned blocks_for(int64_t n, int per = 256) { return (unsigned)((n + pe
 hipError_t launch_rmsnorm_mod(int precision, const NormArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.rows_per_batch;
   if (rows == 0) return hipSuccess;
-  dim3 grid((a.rows_per_batch + kNormRowsPerBlock - 1) / kNormRowsPerBlock, a.batch);
-  if (precision == 0) hipLaunchKernelGGL(rmsnorm_mod_kernel<bf16>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(rmsnorm_mod_kernel<float>, grid, dim3(256), 0, s, a);
+  if (rows >= 2048) {
+    dim3 grid((a.rows_per_batch + kNormRowsPerBlock - 1) / kNormRowsPerBlock, a.batch);
+    if (precision == 0) hipLaunchKernelGGL((rmsnorm_mod_kernel<bf16, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rmsnorm_mod_kernel<float, true>), grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((a.rows_per_batch + 3) / 4, a.batch);
+    if (precision == 0) hipLaunchKernelGGL((rmsnorm_mod_kernel<bf16, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((rmsnorm_mod_kernel<float, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -379,6 +379,18 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
                              float* hidden_out, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Encoder kernels alone (tests and measurement). */
+/* Split-K GEMM for few rows, as the encoder's projections run when batch * max_len <= 256:
+ * C = A B^T with A bf16 [M, K], B (and B2) bf16 [N, K]; epilogues ZDIT_EPI_STORE (C bf16),
+ * ZDIT_EPI_RESID (C fp32 += vec[n] * (A B^T), vec NULL: gate 1) and ZDIT_EPI_SWIGLU (C bf16
+ * = SiLU(A B^T) * (A B2^T)).  K is cut into ranges by N and K alone, each range's fp32
+ * partial product goes to the workspace, and the partials are summed in range order, so a
+ * row's result does not depend on M.  M 1..256, N % 8 == 0, K % 64 == 0 (else
+ * ZDIT_EUNSUPPORTED); ws: zdit_op_gemm_splitk_workspace() bytes. */
+size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K);
+zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
+                                const void* B, const void* B2, const float* vec, void* C,
+                                void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Embedding gather: out [batch, max_len, dim] fp32 = rows of table (bf16 [vocab, dim]) for
  * r < len[b], 0 after; ids / len host as in zdit_encoder_fwd; dim % 8 == 0; ws:
  * zdit_op_embed_workspace() bytes (the ids are copied there). */

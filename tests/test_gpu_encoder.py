@@ -9,7 +9,7 @@ import torch
 
 import synth
 from diffusion_transformer_text_s3_amd import binding as Z
-from gpu_util import bf16_values, dev, drift, host, note, rel_l2
+from gpu_util import assert_bf16_result, bf16_values, dev, drift, host, note, rel_l2
 from oracle import encoder_oracle as E
 
 pytestmark = pytest.mark.gpu
@@ -25,6 +25,80 @@ def _text_tables(batch, s_max, lens, theta=1e6):
     sin = torch.empty_like(cos)
     Z.zdit_rope_tables(Z.ZDIT_SEQ_TEXT, [128, 0, 0], theta, batch, s_max, 0, 0, lens, cos, sin)
     return cos, sin
+
+
+# ------------------------------------------------------------------------------- split-K GEMM
+def _sk_inputs(M, N, K, seed):
+    g = _rng(seed)
+    A = bf16_values(g.standard_normal((M, K)).astype(np.float32))
+    B = bf16_values((0.05 * g.standard_normal((N, K))).astype(np.float32))
+    B2 = bf16_values((0.05 * g.standard_normal((N, K))).astype(np.float32))
+    return A, B, B2
+
+
+def _sk_tol(K):
+    """fp32 accumulation over K in ranges, then the ranges summed: relative to sum |a||b|."""
+    return 2e-6 + 1e-9 * K
+
+
+def _splitk(epi, M, N, K, A, B, B2, vec, C):
+    ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(epi, M, N, K))
+    Z.zdit_op_gemm_splitk(epi, M, N, K, dev(A, torch.bfloat16), dev(B, torch.bfloat16),
+                          None if B2 is None else dev(B2, torch.bfloat16), None if vec is None else dev(vec), C, ws)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 6144, 2560), (1, 64, 64), (77, 520, 192), (256, 2560, 9728)])
+def test_gemm_splitk_store(M, N, K):
+    note(f"gemm split-K STORE M={M} N={N} K={K}")
+    A, B, _ = _sk_inputs(M, N, K, 60)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _splitk(Z.ZDIT_EPI_STORE, M, N, K, A, B, None, None, C)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bound = np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T
+    assert_bf16_result(host(C), ref, _sk_tol(K) * bound)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 2560, 4096), (200, 264, 9728)])
+def test_gemm_splitk_resid_gate(M, N, K):
+    note(f"gemm split-K RESID M={M} N={N} K={K}")
+    A, B, _ = _sk_inputs(M, N, K, 61)
+    g = _rng(62)
+    C0 = (100 * g.standard_normal((M, N))).astype(np.float32)
+    gate = g.standard_normal(N).astype(np.float32)
+    for vec in (gate, None):
+        C = dev(C0)
+        _splitk(Z.ZDIT_EPI_RESID, M, N, K, A, B, None, vec, C)
+        gv = np.ones(N) if vec is None else gate.astype(np.float64)
+        ref = C0 + gv * (A.astype(np.float64) @ B.astype(np.float64).T)
+        bound = np.abs(gv) * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
+        assert np.all(np.abs(host(C) - ref) <= _sk_tol(K) * bound + 1e-6 * np.abs(C0) + 1e-6)
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 9728, 2560), (33, 136, 128)])
+def test_gemm_splitk_swiglu(M, N, K):
+    note(f"gemm split-K SWIGLU M={M} N={N} K={K}")
+    A, B, B2 = _sk_inputs(M, N, K, 63)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _splitk(Z.ZDIT_EPI_SWIGLU, M, N, K, A, B, B2, None, C)
+    A64, B64, B264 = A.astype(np.float64), B.astype(np.float64), B2.astype(np.float64)
+    a1, a3 = A64 @ B64.T, A64 @ B264.T
+    e1 = _sk_tol(K) * (np.abs(A64) @ np.abs(B64).T)
+    e3 = _sk_tol(K) * (np.abs(A64) @ np.abs(B264).T)
+    silu = lambda z: z / (1 + np.exp(-z))
+    u = silu(a1) * a3
+    assert_bf16_result(host(C), u, 1.1 * e1 * np.abs(a3) + np.abs(silu(a1)) * e3 + 1e-6 * np.abs(u) + e1 * e3)
+
+
+def test_gemm_splitk_rows_do_not_depend_on_m():
+    """The K ranges depend on N and K only: rows computed with 50 or 256 rows are identical."""
+    N, K = 2560, 9728
+    note("gemm split-K rows independent of M")
+    A, B, _ = _sk_inputs(256, N, K, 64)
+    C1 = torch.empty((256, N), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty((50, N), dtype=torch.bfloat16, device="cuda")
+    _splitk(Z.ZDIT_EPI_STORE, 256, N, K, A, B, None, None, C1)
+    _splitk(Z.ZDIT_EPI_STORE, 50, N, K, A[:50], B, None, None, C2)
+    np.testing.assert_array_equal(host(C1)[:50], host(C2))
 
 
 # ------------------------------------------------------------------------------- tables
@@ -215,6 +289,17 @@ def test_encoder_tiny_deep_matches_oracle():
     note(f"encoder tiny deep lens={lens}")
     W = synth.encoder_weights(ed, 7, ed.n_layers - 1)
     ids = synth.token_ids(3, 64, lens, ed.vocab, 8)
+    got = _encoder_run(ed, W, ids, lens)
+    _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)
+
+
+def test_encoder_main_gemm_path_matches_oracle():
+    """Over 256 rows in all (3 x 100) the projections run on the main GEMM instead of split-K."""
+    ed = synth.ENC_TINY
+    lens = [100, 61, 2]
+    note(f"encoder main-GEMM path lens={lens}")
+    W = synth.encoder_weights(ed, 15, ed.n_layers - 1)
+    ids = synth.token_ids(3, 100, lens, ed.vocab, 16)
     got = _encoder_run(ed, W, ids, lens)
     _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)
 
