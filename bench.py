@@ -307,8 +307,9 @@ def encoder_cpu_baseline(ed, lens, nb):
 
 
 def kernel_only(which):
-    """Three launches of the SwiGLU GEMM at the main-block 1024^2 pair shape, or three plain
-    device copies of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written)."""
+    """Three launches of the SwiGLU GEMM at the main-block 1024^2 pair shape, three plain
+    device copies of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written), or
+    three of the encoder's split-K down projection (M=128, N=2560, K=9728)."""
     import torch
     import synth
     from diffusion_transformer_text_s3_amd import binding as Z
@@ -320,6 +321,15 @@ def kernel_only(which):
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
+    elif which == "enc_down":
+        ed = synth.ENC_FULL
+        Me, D, I = 128, ed.hidden, ed.inter
+        A = torch.randn((Me, I), generator=g, device="cuda").to(torch.bfloat16)
+        Wd = (torch.randn((D, I), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        X = torch.zeros((Me, D), device="cuda")
+        ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, Me, D, I))
+        for _ in range(3):
+            Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, Me, D, I, A, Wd, None, None, X, ws)
     else:
         A = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
         W1 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
@@ -340,9 +350,10 @@ def main():
                     help="the DiT pass at 1024^2 (default) or 1536x1024, or the text encoder forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
-    ap.add_argument("--kernel-only", choices=["swiglu", "copy"], default=None,
+    ap.add_argument("--kernel-only", choices=["swiglu", "copy", "enc_down"], default=None,
                     help="launch only the dominant GEMM at its main-block shape (or a plain device copy of "
-                         "170,393,600 bytes, the counter calibration) three times, for rocprofv3 --pmc runs")
+                         "170,393,600 bytes, the counter calibration; or the encoder's split-K down projection) "
+                         "three times, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not part "
