@@ -28,7 +28,8 @@ EXPORTS = [
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
     "zdit_encoder_workspace", "zdit_encoder_fwd", "zdit_op_embed_workspace", "zdit_op_embed",
     "zdit_op_qknorm_rope", "zdit_op_attn_gqa_workspace", "zdit_op_attn_gqa",
-    "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk",
+    "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk", "zdit_op_mfma_peak",
+    "zdit_device_info",
 ]
 
 
@@ -133,6 +134,8 @@ def lib():
             "zdit_op_attn_gqa": (i32, [i32, i32, i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
             "zdit_op_gemm_splitk_workspace": (sz, [i32, i32, i32, i32]),
             "zdit_op_gemm_splitk": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_op_mfma_peak": (i32, [i32, i32, vp, vp]),
+            "zdit_device_info": (i32, [i32, pi32, pi32, pi32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -465,3 +468,13 @@ def zdit_op_gemm_splitk_workspace(epilogue, M, N, K) -> int:
 def zdit_op_gemm_splitk(epilogue, M, N, K, A, B, B2, vec, Cout, ws, stream=None):
     return check(lib().zdit_op_gemm_splitk(epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
                                            ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_mfma_peak(workgroups, iters, out, stream=None):
+    return check(lib().zdit_op_mfma_peak(workgroups, iters, ptr(out), stream_handle(stream)))
+
+
+def zdit_device_info(device=0) -> dict:
+    cu, clk, l2 = C.c_int32(), C.c_int32(), C.c_int32()
+    check(lib().zdit_device_info(device, C.byref(cu), C.byref(clk), C.byref(l2)))
+    return {"cu_count": cu.value, "max_sclk_mhz": clk.value / 1000.0, "l2_bytes": l2.value}

@@ -152,6 +152,10 @@ struct EmbedArgs {
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 
+// measurement: `workgroups` x 256 threads, each wave 4 x iters bf16 32x32x16 MFMAs; out
+// [workgroups * 256] fp32
+hipError_t launch_mfma_peak(int workgroups, int iters, float* out, hipStream_t s);
+
 struct RopeArgs {
   void* qkv;
   const float* cos;

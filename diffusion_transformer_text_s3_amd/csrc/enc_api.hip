@@ -310,4 +310,19 @@ zdit_status zdit_op_attn_gqa(int32_t precision, int32_t batch, int32_t s_max, in
   return ok();
 }
 
+zdit_status zdit_device_info(int32_t device, int32_t* cu_count, int32_t* max_sclk_khz, int32_t* l2_bytes) {
+  if (!cu_count || !max_sclk_khz || !l2_bytes) return fail(ZDIT_EINVAL, "NULL output");
+  HIP_TRY(hipDeviceGetAttribute(cu_count, hipDeviceAttributeMultiprocessorCount, device));
+  HIP_TRY(hipDeviceGetAttribute(max_sclk_khz, hipDeviceAttributeClockRate, device));
+  HIP_TRY(hipDeviceGetAttribute(l2_bytes, hipDeviceAttributeL2CacheSize, device));
+  return ok();
+}
+
+zdit_status zdit_op_mfma_peak(int32_t workgroups, int32_t iters, float* out, void* hip_stream) {
+  if (workgroups < 1 || iters < 1) return fail(ZDIT_EINVAL, "workgroups %d / iters %d", workgroups, iters);
+  if (!out || !aligned16(out)) return fail(ZDIT_EINVAL, "out NULL or not 16-byte aligned");
+  HIP_TRY(launch_mfma_peak(workgroups, iters, out, (hipStream_t)hip_stream));
+  return ok();
+}
+
 }  // extern "C"

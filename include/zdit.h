@@ -424,6 +424,17 @@ zdit_status zdit_op_attn_gqa(int32_t precision, int32_t batch, int32_t s_max, in
                              const void* qkv, void* out, void* ws, size_t ws_bytes,
                              void* hip_stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Measurement: the sustained bf16 MFMA rate, for roofline fractions against a measured
+ * ceiling.  `workgroups` x 256 threads; every wavefront issues 4 x iters
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands, with no memory traffic
+ * in the loop; out: device fp32 [workgroups * 256] (one value per thread, keeps the work live).
+ * ------------------------------------------------------------------------------------- */
+zdit_status zdit_op_mfma_peak(int32_t workgroups, int32_t iters, float* out, void* hip_stream);
+/* Compute units, peak engine clock (kHz) and L2 size (bytes) of HIP device `device`, as the
+ * runtime reports them (host only; no device work). */
+zdit_status zdit_device_info(int32_t device, int32_t* cu_count, int32_t* max_sclk_khz, int32_t* l2_bytes);
+
 #ifdef __cplusplus
 }
 #endif
