@@ -210,99 +210,138 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
   // largest key this lane's query sees (key 0 is always visible)
   const int klim = a.causal ? min(S - 1, q) : S - 1;
 
-  // One key block t, its K in Kc / V^T in Vc: loads of V^T block t+1 (into Vn) and K block
-  // t+2 (into Kc, free since the scores of block t exist) start first; softmax of block t
-  // (scores in `cur`), O^T += V^T P^T, QK^T of block t+1 (K in Kn) into `nxt`; then every
-  // wave waits for its loads and the workgroup meets at a barrier.  Only masked steps (the
-  // final block, and with causal masking the blocks from the tile's first query on) hold
-  // keys past a lane's limit; they are set to -inf.
-  auto step = [&](auto masked, int t, uint4* Kc, uint4* Vc, uint4* Kn, uint4* Vn, f32x16 (&cur)[2],
-                  f32x16 (&nxt)[2]) {
-    const bool more = t + 1 < nkt;
-    if (more) dma_v(t + 1, Vn);
-    if (t + 2 < nkt) dma_k(t + 2, Kc);
-
-    float mx = -INFINITY;
+  // Scores of one block as a lane holds them: keys past the lane's limit set to -inf when
+  // `masked`, then the maximum over the lane pair, in log2 units.
+  auto block_max = [&](auto masked, int t, f32x16 (&st)[2]) {
     if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * KT + t2 * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-          if (key > klim) cur[t2][r] = -INFINITY;
+          if (key > klim) st[t2][r] = -INFINITY;
         }
     }
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[t2][r]);
-    mx = xor32_max(mx);
-    const float m_new = fmaxf(m_run, mx * sc);
-    // Lazy rescale: a query's reference max moves only when its max rose by more than 8
-    // (log2 units), so p = exp2(s - m_run) stays below 2^8; O and l share the reference, so
-    // the result O / l is the same softmax.  The branch is taken when any lane needs it;
-    // the other lanes scale by exactly 1, so every query's arithmetic depends on its own
-    // scores only.
-    const bool move = m_new > m_run + 8.0f;
-    if (__any(move)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      m_run = move ? m_new : m_run;
-    }
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], st[t2][r]);
+    return xor32_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sc;
+  };
+
+  // One key block t: K(t+1) is in Kn, V^T(t) in Vc, block t's scores in `cur`, and m_run
+  // already covers them.  Loads of V^T block t+1 (into Vn) and K block t+2 (into Kc, last
+  // read in the previous step) start first; past the last block they repeat it into buffers
+  // no one reads again, so the step has no branch before its end.  Within one wave the MFMAs
+  // run beside independent VALU and transcendental work, so the instruction stream
+  // interleaves them: the 16 QK^T MFMAs of block t+1 with the exponentials of block t, then
+  // the 16 PV MFMAs of block t with the row sums and the maximum of block t+1; fragment reads
+  // run four ahead.  The (rare) rescale for block t+1 comes last.  NextMasked: block t+1 may
+  // hold keys past a lane's limit.  Last: block t is the final one (no block t+1).
+  auto step = [&](auto next_masked, auto last, int t, uint4* Kc, uint4* Vc, uint4* Kn, uint4* Vn,
+                  f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr bool LAST = decltype(last)::value;
+    dma_v(min(t + 1, nkt - 1), Vn);
+    dma_k(min(t + 2, nkt - 1), Kc);
+    if constexpr (!LAST) qk(Kn, nxt);
     bf16x8 pb[2][2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[t2][r], sc, -m_run));
-        l_run += p;
-        pb[t2][r >> 3][r & 7] = (bf16)p;
-      }
+      for (int r = 0; r < 16; ++r)
+        pb[t2][r >> 3][r & 7] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(cur[t2][r], sc, -m_run));
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           // logical chunk (t2 * 4 + j * 2 + fh) of the V^T row holds this lane half's 8 keys
           const bf16x8 vf = __builtin_bit_cast(bf16x8, Vc[v_slot(dt * 32 + fr, t2 * 4 + j * 2 + fh)]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t2][j], o[dt], 0, 0, 0);
         }
+    // row sum of the bf16 probabilities that enter O (so O / l weighs the values exactly as
+    // P V does), in four dot2 chains
+    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+    float l4[4] = {l_run, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pp = {pb[t2][j][2 * e], pb[t2][j][2 * e + 1]};
+          l4[2 * t2 + j] = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, l4[2 * t2 + j], false);
+        }
+    l_run = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    if constexpr (!LAST) {
+      const float m_new = fmaxf(m_run, block_max(next_masked, t + 1, nxt));
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      }
+      // Lazy rescale: a query's reference max moves only when its max rose by more than 8
+      // (log2 units), so p = exp2(s - m_run) stays below 2^8; O and l share the reference,
+      // so the result O / l is the same softmax.  The branch is taken when any lane needs
+      // it; the other lanes scale by exactly 1, so every query's arithmetic depends on its
+      // own scores only.
+      const bool move = m_new > m_run + 8.0f;
+      if (__any(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+        m_run = move ? m_new : m_run;
+      }
     }
-    if (more) qk(Kn, nxt);
     __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
     __syncthreads();
   };
 
+  // steps from tm on may hold keys past a lane's limit: the last block (keys >= S), and with
+  // causal masking every block from the one holding the tile's first query (tm is even)
+  const int tm = (a.causal ? min(nkt - 1, q0 / KT) : nkt - 1) & ~1;
   dma_k(0, K0);
   dma_v(0, V0);
-  if (nkt > 1) dma_k(1, K1);
+  dma_k(min(1, nkt - 1), K1);
   __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
   __syncthreads();
   f32x16 sA[2], sB[2];
   qk(K0, sA);
+  m_run = tm == 0 ? block_max(std::true_type{}, 0, sA) : block_max(std::false_type{}, 0, sA);
   // step 0 loads key block 2 into K0: every wave's reads of K0 must be done
   __syncthreads();
-  using Plain = std::integral_constant<bool, false>;
-  using Masked = std::integral_constant<bool, true>;
-  // steps t >= tm are masked: the last block (keys >= S), and with causal masking every
-  // block from the one holding the tile's first query.  tm is even, so the buffer roles at
-  // the switch are those of step 0.
-  const int tm = (a.causal ? min(nkt - 1, q0 / KT) : nkt - 1) & ~1;
+  using P = std::false_type;
+  using M = std::true_type;
+  // step t masks block t + 1 from t = tp on (tp even, at most tm - 1)
+  const int tp = max(tm - 1, 0) & ~1;
   int t = 0;
-  for (; t < tm; t += 2) {
-    step(Plain{}, t, K0, V0, K1, V1, sA, sB);
-    step(Plain{}, t + 1, K1, V1, K0, V0, sB, sA);
+  for (; t < tp; t += 2) {
+    step(P{}, P{}, t, K0, V0, K1, V1, sA, sB);
+    step(P{}, P{}, t + 1, K1, V1, K0, V0, sB, sA);
   }
-  for (; t + 1 < nkt; t += 2) {
-    step(Masked{}, t, K0, V0, K1, V1, sA, sB);
-    step(Masked{}, t + 1, K1, V1, K0, V0, sB, sA);
+  for (; t + 2 <= nkt - 1; t += 2) {
+    step(M{}, P{}, t, K0, V0, K1, V1, sA, sB);
+    step(M{}, P{}, t + 1, K1, V1, K0, V0, sB, sA);
   }
-  if (t < nkt) step(Masked{}, t, K0, V0, K1, V1, sA, sB);
+  if (t == nkt - 1) {
+    step(M{}, M{}, t, K0, V0, K1, V1, sA, sB);
+  } else {
+    step(M{}, P{}, t, K0, V0, K1, V1, sA, sB);
+    step(M{}, M{}, t + 1, K1, V1, K0, V0, sB, sA);
+  }
 
   const float l = xor32_sum(l_run);
   const float inv = 1.0f / l;
