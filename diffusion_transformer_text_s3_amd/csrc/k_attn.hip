@@ -75,8 +75,10 @@ __global__ __launch_bounds__(256) void vt_tail_zero_kernel(AttnArgs a) {
 
 // 8 wavefronts x 32 queries = 256 queries per workgroup (two wavefronts per SIMD, so one's
 // softmax can overlap the other's MFMAs).  K and V^T key blocks are double-buffered in LDS and
-// fetched with direct-to-LDS buffer loads one block ahead (no staging registers).  Per key
-// block t: softmax of the scores of block t, O^T += V^T P^T, then the QK^T MFMAs of block t+1.
+// fetched with direct-to-LDS buffer loads (no staging registers): V^T one block ahead, K two
+// (QK^T runs a block ahead of PV).  Per key block t, within one wavefront: the QK^T MFMAs of
+// block t+1 interleaved with the exponentials of block t, then the PV MFMAs of block t
+// interleaved with its row sums and the maximum of block t+1.
 constexpr int NWAVE = 8;
 constexpr int QTILE = 32 * NWAVE;
 constexpr int ATT_NT = 64 * NWAVE;  // threads per workgroup

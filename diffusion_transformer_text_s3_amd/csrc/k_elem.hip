@@ -314,43 +314,74 @@ __global__ __launch_bounds__(256) void temb_kernel(TArgs ta, int t_freq, int c_d
 }
 
 // ---------------------------------------------------------------------------------------
-// adaLN projection out[b, j] = sum_k W[j, k] SiLU(c[b, k]) + bias[j]; one thread per output
-// row, all branches at once, SiLU(c) staged in LDS.
+// adaLN projection out[b, j] = sum_k W[j, k] SiLU(c[b, k]) + bias[j], all branches at once,
+// SiLU(c) staged in LDS.  Weight rows are read coalesced: a group of L lanes (L a power of two,
+// 8 L >= min(c_dim, 512)) covers one row in 8-element chunks, a wavefront 64 / L rows at a
+// time, each lane with ADA_U rows' loads in flight; the group's partial sums meet by xor
+// shuffles.
 // ---------------------------------------------------------------------------------------
+constexpr int ADA_U = 4;
+
 template <typename TW>
-__global__ __launch_bounds__(256) void adaln_kernel(int batch, int c_dim, int n_out,
-                                                     const float* c, const TW* w,
-                                                     const float* bias, float* out) {
+__global__ __launch_bounds__(256) void adaln_kernel(int batch, int c_dim, int n_out, int lanes_per_row,
+                                                     const float* c, const TW* w, const float* bias,
+                                                     float* out) {
   extern __shared__ float sc[];  // [batch][c_dim]
   for (int i = threadIdx.x; i < batch * c_dim; i += blockDim.x) sc[i] = silu(c[i]);
   __syncthreads();
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= n_out) return;
-  float acc[kMaxBatch];
+  const int L = lanes_per_row, R = 64 / L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane / L, li = lane % L;
+  const int row0 = (blockIdx.x * 4 + wave) * R * ADA_U + g;  // rows row0 + u R
+  float acc[ADA_U][kMaxBatch];
 #pragma unroll
-  for (int b = 0; b < kMaxBatch; ++b) acc[b] = 0.f;
-  const TW* wr = w + (int64_t)j * c_dim;
-  for (int k = 0; k < c_dim; k += 8) {
-    float wv[8];
-    if constexpr (sizeof(TW) == 2) {
-      bf16x8 v = *(const bf16x8*)(wr + k);
+  for (int u = 0; u < ADA_U; ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wv[i] = (float)v[i];
-    } else {
-      float4 v0 = *(const float4*)(wr + k), v1 = *(const float4*)(wr + k + 4);
-      wv[0] = v0.x; wv[1] = v0.y; wv[2] = v0.z; wv[3] = v0.w;
-      wv[4] = v1.x; wv[5] = v1.y; wv[6] = v1.z; wv[7] = v1.w;
+    for (int b = 0; b < kMaxBatch; ++b) acc[u][b] = 0.f;
+  for (int k = li * 8; k < c_dim; k += L * 8) {
+    float wv[ADA_U][8];
+#pragma unroll
+    for (int u = 0; u < ADA_U; ++u) {
+      const int row = row0 + u * R;
+      const TW* wr = w + (int64_t)min(row, n_out - 1) * c_dim + k;
+      if constexpr (sizeof(TW) == 2) {
+        const bf16x8 v = *(const bf16x8*)wr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[u][i] = (float)v[i];
+      } else {
+        const float4 v0 = *(const float4*)wr, v1 = *(const float4*)(wr + 4);
+        wv[u][0] = v0.x; wv[u][1] = v0.y; wv[u][2] = v0.z; wv[u][3] = v0.w;
+        wv[u][4] = v1.x; wv[u][5] = v1.y; wv[u][6] = v1.z; wv[u][7] = v1.w;
+      }
     }
 #pragma unroll
     for (int b = 0; b < kMaxBatch; ++b) {
       if (b < batch) {
-        const float* s = sc + b * c_dim + k;
+        const float4 s0 = *(const float4*)(sc + b * c_dim + k), s1 = *(const float4*)(sc + b * c_dim + k + 4);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[b] += wv[i] * s[i];
+        for (int u = 0; u < ADA_U; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u][b] += wv[u][i] * sv[i];
       }
     }
   }
-  for (int b = 0; b < batch; ++b) out[(int64_t)b * n_out + j] = acc[b] + bias[j];
+#pragma unroll
+  for (int u = 0; u < ADA_U; ++u) {
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b < batch) {
+        for (int m = L >> 1; m >= 1; m >>= 1) acc[u][b] += __shfl_xor(acc[u][b], m, 64);
+      }
+    }
+    const int row = row0 + u * R;
+    if (li == 0 && row < n_out) {
+      const float bj = bias[row];
+#pragma unroll
+      for (int b = 0; b < kMaxBatch; ++b)
+        if (b < batch) out[(int64_t)b * n_out + row] = acc[u][b] + bj;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void copy_rows_kernel(const float4* src, int64_t src_bstride4,
@@ -455,11 +486,14 @@ hipError_t launch_temb(int batch, const float* t, int t_freq, int c_dim, float t
 hipError_t launch_adaln(int precision, int batch, int c_dim, int n_out, const float* c,
                         const void* w, const float* b, float* out, hipStream_t s) {
   const size_t shm = (size_t)batch * c_dim * sizeof(float);
-  dim3 grid(blocks_for(n_out));
+  int L = 1;
+  while (L < 64 && 8 * L < c_dim) L <<= 1;
+  const int rows_per_block = 4 * (64 / L) * ADA_U;
+  dim3 grid((unsigned)((n_out + rows_per_block - 1) / rows_per_block));
   if (precision == 0)
-    hipLaunchKernelGGL(adaln_kernel<bf16>, grid, dim3(256), shm, s, batch, c_dim, n_out, c, (const bf16*)w, b, out);
+    hipLaunchKernelGGL(adaln_kernel<bf16>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, (const bf16*)w, b, out);
   else
-    hipLaunchKernelGGL(adaln_kernel<float>, grid, dim3(256), shm, s, batch, c_dim, n_out, c, (const float*)w, b, out);
+    hipLaunchKernelGGL(adaln_kernel<float>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, (const float*)w, b, out);
   return hipGetLastError();
 }
 
