@@ -69,10 +69,16 @@ struct SplitKArgs {
   int splits;
   int col_tiles;  // 64-column tiles per weight
   int Nv;         // partial row width: N, or 2N for SwiGLU (W3 columns after W1's)
+  // Row gather / scatter (NULL: row m is row m).  A row m is row a_rows[m] of A, which has
+  // a_phys_rows rows; output row m goes to row c_rows[m] of C (RowMap ld, no batch stride).
+  const int* a_rows;
+  int a_phys_rows;
+  const int* c_rows;
 };
 SplitKArgs splitk_plan(int epi, int M, int N, int K);
 size_t splitk_workspace(int epi, int M, int N, int K);
-hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s);
+hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows = nullptr,
+                              int a_phys_rows = 0, const int* c_rows = nullptr);
 
 // q, k, v rows: row r of branch b at qkv + (b * s_max + r) * row_stride elements, query head
 // h at column h * 128, key head j at k_col + j * 128, value head j at v_col + j * 128.  Query
@@ -152,6 +158,10 @@ struct EmbedArgs {
   int len[kMaxBatch];
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+
+// The valid rows of a padded batch in order: entry i (i < sum of len) is b * s_max + r for
+// the i-th pair (b, r < len[b]).
+hipError_t launch_valid_rows(int batch, int s_max, const int* len, int* rows, hipStream_t s);
 
 // measurement: `workgroups` x 256 threads, each wave 4 x iters bf16 32x32x16 MFMAs; out
 // [workgroups * 256] fp32

@@ -39,7 +39,7 @@ bool qkv_fits(int64_t s_max, int64_t width) { return s_max * width * 2 <= INT32_
 constexpr int kSplitKMaxRows = 256;
 
 struct EncPlan {
-  size_t ids, cos, sin, h, qkv, vt, o, u, part, total;
+  size_t ids, rows, cos, sin, h, qkv, vt, o, u, part, total;
   bool splitk;
 };
 
@@ -58,6 +58,7 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   p.splitk = M <= (size_t)kSplitKMaxRows;
   size_t off = 0;
   p.ids = off; off += al256(M * 4);
+  p.rows = off; off += al256(M * 4);
   p.cos = off; off += al256(M * 64 * 4);
   p.sin = off; off += al256(M * 64 * 4);
   p.h = off;   off += al256(M * c.hidden * 2);
@@ -73,9 +74,17 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   return p;
 }
 
-// a projection of the block: split-K for few rows, else the main GEMM
-hipError_t enc_gemm(int epi, const GemmArgs& g, const EncPlan& pl, char* ws, hipStream_t st) {
-  return pl.splitk ? launch_gemm_splitk(epi, g, (float*)(ws + pl.part), st) : launch_gemm_bf16(epi, g, st);
+// A projection of the block.  Few rows: split-K over the valid rows only (A_GATHER: A is the
+// padded [B * L] layout, read through the valid-row list; C_SCATTER: C too), with M the
+// number of valid rows.  Else the main GEMM over the padded rows (the RowMap skips padding).
+hipError_t enc_gemm(int epi, GemmArgs g, bool a_gather, bool c_scatter, int B, int L, int Mc, const EncPlan& pl,
+                    char* ws, hipStream_t st) {
+  if (!pl.splitk) return launch_gemm_bf16(epi, g, st);
+  const int* rows = (const int*)(ws + pl.rows);
+  g.M = Mc;
+  if (!c_scatter) g.out = compact_rows(Mc, g.out.ld);
+  return launch_gemm_splitk(epi, g, (float*)(ws + pl.part), st, a_gather ? rows : nullptr, B * L,
+                            c_scatter ? rows : nullptr);
 }
 
 zdit_status check_ids(int batch, int max_len, int vocab, const int32_t* ids, const int32_t* len) {
@@ -114,6 +123,8 @@ AttnArgs enc_attn_args(const zdit_enc_cfg& c, int B, int L, const int32_t* len, 
 zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, int L, const int32_t* len,
                       float* x, const EncPlan& pl, char* ws, hipStream_t st) {
   const int D = c.hidden, I = c.inter, M = B * L, W = qkv_width(c), Dq = c.n_heads * kHeadDim;
+  int Mc = 0;  // valid rows
+  for (int b = 0; b < B; ++b) Mc += len[b];
   void* h = ws + pl.h;
   void* qkv = ws + pl.qkv;
   void* vt = ws + pl.vt;
@@ -130,7 +141,7 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   GemmArgs g{};
   g.A = h; g.B = w.w_qkv; g.C = qkv; g.M = M; g.N = W; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, W);
-  HIP_TRY(enc_gemm(EPI_STORE, g, pl, ws, st));
+  HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st));
 
   QkNormRopeArgs qa;
   qa.qkv = qkv; qa.row_stride = W; qa.k_col = Dq; qa.n_heads = c.n_heads; qa.n_kv_heads = c.n_kv_heads;
@@ -146,7 +157,7 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   for (int b = 0; b < kMaxBatch; ++b) xr.valid[b] = b < B ? len[b] : 0;
   g = GemmArgs{};
   g.A = o; g.B = w.w_o; g.C = x; g.M = M; g.N = D; g.K = Dq; g.lda = Dq; g.ldb = Dq; g.out = xr;
-  HIP_TRY(enc_gemm(EPI_RESID, g, pl, ws, st));
+  HIP_TRY(enc_gemm(EPI_RESID, g, true, true, B, L, Mc, pl, ws, st));
 
   na.gain = w.post_norm;
   HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
@@ -154,11 +165,12 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   g = GemmArgs{};
   g.A = h; g.B = w.w_gate; g.B2 = w.w_up; g.C = u; g.M = M; g.N = I; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, I);
-  HIP_TRY(enc_gemm(EPI_SWIGLU, g, pl, ws, st));
+  // split-K: u holds the valid rows only, in order
+  HIP_TRY(enc_gemm(EPI_SWIGLU, g, true, false, B, L, Mc, pl, ws, st));
 
   g = GemmArgs{};
   g.A = u; g.B = w.w_down; g.C = x; g.M = M; g.N = D; g.K = I; g.lda = I; g.ldb = I; g.out = xr;
-  HIP_TRY(enc_gemm(EPI_RESID, g, pl, ws, st));
+  HIP_TRY(enc_gemm(EPI_RESID, g, false, true, B, L, Mc, pl, ws, st));
   return ZDIT_OK;
 }
 
@@ -210,6 +222,7 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
 
   if (zdit_status s = embed_rows(batch, max_len, c.hidden, ids, len, w->embed, hidden_out, (int*)(base + pl.ids), st))
     return s;
+  if (pl.splitk) HIP_TRY(launch_valid_rows(batch, max_len, len, (int*)(base + pl.rows), st));
   for (int i = 0; i < c.n_layers - 1; ++i)
     if (zdit_status s = enc_block(c, w->layers[i], batch, max_len, len, hidden_out, pl, base, st)) return s;
   return ok();

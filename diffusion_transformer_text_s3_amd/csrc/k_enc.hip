@@ -1,5 +1,6 @@
-// Kernels of the text encoder that only it uses: the token-embedding gather and the per-head
-// q/k RMSNorm followed by RoPE over dimension pairs (i, i + 64).  The encoder's projections,
+// Kernels of the text encoder that only it uses: the token-embedding gather, the per-head
+// q/k RMSNorm followed by RoPE over dimension pairs (i, i + 64), and the list of valid rows
+// that lets the projections skip the padding.  The encoder's projections,
 // pre-norms, attention and residual adds run on the DiT's kernels.
 #include "common.h"
 
@@ -79,6 +80,22 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkNormRopeArgs a) {
   *(bf16x8*)p = out;
 }
 
+struct RowsArgs {
+  int batch, s_max;
+  int len[kMaxBatch];
+};
+
+// One thread per padded row (b, r): rows below len[b] write their compact index.
+__global__ __launch_bounds__(256) void valid_rows_kernel(RowsArgs a, int* rows) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.batch * a.s_max) return;
+  const int b = i / a.s_max, r = i - b * a.s_max;
+  if (r >= a.len[b]) return;
+  int before = 0;
+  for (int k = 0; k < b; ++k) before += a.len[k];
+  rows[before + r] = i;
+}
+
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
@@ -87,6 +104,14 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
   if (a.batch == 0 || a.s_max == 0) return hipSuccess;
   dim3 grid(blocks_for((int64_t)a.s_max * (a.dim >> 3)), a.batch);
   hipLaunchKernelGGL(embed_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_valid_rows(int batch, int s_max, const int* len, int* rows, hipStream_t s) {
+  RowsArgs a;
+  a.batch = batch; a.s_max = s_max;
+  for (int b = 0; b < kMaxBatch; ++b) a.len[b] = b < batch ? len[b] : 0;
+  hipLaunchKernelGGL(valid_rows_kernel, dim3(blocks_for((int64_t)batch * s_max)), dim3(256), 0, s, a, rows);
   return hipGetLastError();
 }
 

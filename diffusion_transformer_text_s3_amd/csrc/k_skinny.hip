@@ -1,140 +1,162 @@
-// C = A B^T for few rows (M <= 256): the text encoder's projections at 2 x 64 tokens, where
+// C = A B^T for few rows (M <= 256): the text encoder's projections on its valid tokens, where
 // the 256 x 256 tiles of the main GEMM would occupy a few dozen of the 256 CUs while the time
 // goes into streaming the weights from HBM.
 //
-// Split-K.  A 256-thread workgroup owns 128 rows x 64 columns of C and a K range of ks
-// columns; the number of ranges depends on N and K only (about 512 workgroups for one row
-// tile), so every output's sum has the same K split and the same order whatever M is.  Each
-// wavefront owns 32 rows x 64 columns (2 x 4 tiles of v_mfma_f32_16x16x32_bf16).  K advances in
-// 32-wide slabs through a ring of four LDS stages filled by direct-to-LDS buffer loads three
-// slabs ahead (rows past M or N load as zero from the bounds-checked buffer resource).  The
-// fp32 partial tiles go to a workspace [splits][M][Nv]; a second kernel sums them in split
-// order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
-// paired W1 / W3 partials (Nv = 2N: the W3 columns follow the W1 columns).
+// Split-K with the weights streamed into registers.  A 256-thread workgroup owns one tile of up
+// to 64 rows, 64 columns of C and one K range; wavefront w owns columns n0 + 16 w .. + 15.  Per
+// 32-wide slab a lane loads 16 bytes of its weight row (the B fragment of
+// v_mfma_f32_16x16x32_bf16: row l % 16, k 8 (l / 16) ..) KU_B slabs ahead, so each wavefront
+// keeps 16 KB of weights in flight, reads the four A fragments (16-row tiles) from LDS and
+// issues four MFMAs.  A arrives in LDS in chunks of 256 columns (32 KB), double-buffered and
+// fetched one chunk ahead by direct-to-LDS loads; one barrier per chunk.  The K ranges are whole
+// multiples of 256 columns except the last, their number depends on N and K only (about 512
+// workgroups per row tile), so every output's sum has the same K split and order whatever M
+// is.  The fp32 partial tiles go to a workspace [splits][M][Nv]; a second kernel sums them in
+// split order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
+// paired W1 / W3 partials (Nv = 2N: the W3 columns follow the W1 columns).  Optional row maps
+// gather the rows of A and scatter the rows of C, so a caller can run only the valid rows of a
+// padded batch.  Buffer resources make rows past M or N read as zero.
 #include "common.h"
 
 namespace zdit {
 
 namespace {
 
-constexpr int SBM = 128, SBN = 64, SBK = 32;
-constexpr int SA_CHUNKS = SBM * (SBK / 8);          // 512 16-byte chunks of A per slab
-constexpr int SB_CHUNKS = SBN * (SBK / 8);          // 256 of B
-constexpr int S_CHUNKS = SA_CHUNKS + SB_CHUNKS;     // 768 (12 KB) per stage
-constexpr int S_DMA = S_CHUNKS / 64 / 4;            // 3 wave loads per wave per slab
+constexpr int KM = 64;                  // rows per tile
+constexpr int KNW = 16;                 // columns per wavefront
+constexpr int KWG = 4 * KNW;            // columns per workgroup
+constexpr int KSL = 32;                 // slab width (one MFMA k-step)
+constexpr int KU_B = 16;                // weight slabs in flight per lane
+constexpr int KCH = 256;                // A chunk width (K columns)
+constexpr int KCH_SL = KCH / KSL;       // 8 slabs per chunk
+constexpr int KCH_CPR = KCH / 8;        // 32 16-byte chunks per A row of a chunk
+constexpr int KCH_CHUNKS = KM * KCH_CPR;  // 2048 (32 KB)
+constexpr int KCH_DMA = KCH_CHUNKS / 64 / 4;  // 8 wave loads per wave per chunk
 constexpr int kSBufFlags = 0x00020000;
 constexpr int s_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// slot (16-byte units from the operand's first row) of logical chunk c of row r
-__device__ __forceinline__ int sswz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float ssilu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
+
+// LDS slot of logical 16-byte chunk c of A row r within a chunk buffer: the 16 rows of one
+// fragment read hit 16 distinct bank groups
+__device__ __forceinline__ int aslot(int r, int c) { return r * KCH_CPR + (c ^ (r & 15)); }
 
 __device__ __forceinline__ void sdma_16(const __amdgpu_buffer_rsrc_t rs, const uint4* lds_base, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff,
                                            0, 0);
 }
 
-__device__ __forceinline__ float ssilu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
-
 __global__ __launch_bounds__(256) void gemm_splitk_kernel(SplitKArgs a) {
-  // four separate objects, so reads of one stage are not ordered behind the in-flight
-  // direct-to-LDS writes of another
-  __shared__ uint4 L0[S_CHUNKS], L1[S_CHUNKS], L2[S_CHUNKS], L3[S_CHUNKS];
-  const int ct = blockIdx.x, split = blockIdx.y, m0 = blockIdx.z * SBM;
-  const bool second = ct >= a.col_tiles;  // SwiGLU: the W3 half of the virtual columns
-  const int n0 = (second ? ct - a.col_tiles : ct) * SBN;
-  const int k0 = split * a.ks;
-  const int nk = (min(a.K, k0 + a.ks) - k0) / SBK;
+  // two separate objects, so reads of one chunk buffer are not ordered behind the in-flight
+  // direct-to-LDS writes of the other
+  __shared__ uint4 A0[KCH_CHUNKS], A1[KCH_CHUNKS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ct = blockIdx.x, split = blockIdx.y, m0 = blockIdx.z * KM;
+  const bool second = ct >= a.col_tiles;  // SwiGLU: the W3 half of the virtual columns
+  const int n0 = (second ? ct - a.col_tiles : ct) * KWG + wave * KNW;
+  const int k0 = split * a.ks;
+  const int kr = min(a.K, k0 + a.ks) - k0;  // K columns of this range
+  const int nk = kr / KSL;                  // slabs (>= 1)
+  const int nch = (kr + KCH - 1) / KCH;     // A chunks
+  const int fr = lane & 15, fh = lane >> 4;
 
-  const bf16* ab = (const bf16*)a.A + (int64_t)m0 * a.lda;
-  const bf16* bb = (const bf16*)(second ? a.B2 : a.B) + (int64_t)n0 * a.ldb;
-  const __amdgpu_buffer_rsrc_t ars =
-      __builtin_amdgcn_make_buffer_rsrc((void*)ab, 0, (a.M - m0) * a.lda * 2, kSBufFlags);
+  // weight rows n0 .. n0 + 15; rows past N fall outside the resource.  Offsets are unsigned.
+  const bf16* bb = (const bf16*)(second ? a.B2 : a.B) + (int64_t)min(n0, a.N) * a.ldb;
   const __amdgpu_buffer_rsrc_t brs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)bb, 0, (a.N - n0) * a.ldb * 2, kSBufFlags);
-
-  // wave load j of this wave fills stage slots (3 wave + j) * 64 + lane: slots below 512 are A
-  // (row s / 4), the rest B; the lane fetches the logical chunk that belongs in its slot
-  int voff[S_DMA];
-#pragma unroll
-  for (int j = 0; j < S_DMA; ++j) {
-    const int s = (S_DMA * wave + j) * 64 + lane;
-    const int sb = s < SA_CHUNKS ? s : s - SA_CHUNKS;
-    const int r = sb >> 2, c = (sb & 3) ^ ((r >> 2) & 3);
-    voff[j] = r * (s < SA_CHUNKS ? a.lda : a.ldb) * 2 + c * 16;
-  }
-  auto issue = [&](int kt, uint4* st) {
-    const int soff = (k0 + kt * SBK) * 2;
-#pragma unroll
-    for (int j = 0; j < S_DMA; ++j) {
-      const int w = S_DMA * wave + j;  // wave-uniform: A for w < 8
-      sdma_16(w < SA_CHUNKS / 64 ? ars : brs, st + w * 64, voff[j], soff);
-    }
+      __builtin_amdgcn_make_buffer_rsrc((void*)bb, 0, max(0, a.N - n0) * a.ldb * 2, kSBufFlags);
+  const unsigned bvo = (unsigned)(fr * a.ldb * 2 + fh * 16 + k0 * 2);
+  // slabs past the range reload the last one (branch-free); their weights are zeroed below
+  auto ldb = [&](int t) {
+    return __builtin_amdgcn_raw_buffer_load_b128(brs, (int)(bvo + (unsigned)min(t, nk - 1) * (KSL * 2)), 0, 0);
   };
 
-  f32x4 acc[2][4];
+  // A chunk loads: wave load j of this wave fills slots 64 (8 wave + j) + lane, i.e. row
+  // 2 (8 wave + j) + lane / 32 and physical chunk lane % 32; the lane fetches the logical chunk
+  // that belongs there.  A row past M gets an offset past the end of the resource (2^31 + k
+  // stays out of range), so it loads as zero.
+  const bool gather = a.a_rows != nullptr;
+  const bf16* ab = (const bf16*)a.A + (gather ? 0 : (int64_t)m0 * a.lda);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)ab, 0, (gather ? a.a_phys_rows : max(0, a.M - m0)) * a.lda * 2, kSBufFlags);
+  unsigned avo[KCH_DMA];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < KCH_DMA; ++j) {
+    const int r = 2 * (KCH_DMA * wave + j) + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 15);
+    const int m = m0 + r;
+    const unsigned row = m < a.M ? (unsigned)(gather ? a.a_rows[m] : r) * (unsigned)(a.lda * 2) : 0x80000000u;
+    avo[j] = row + (unsigned)(c * 16);
+  }
+  auto dma_a = [&](int ch, uint4* buf) {
+    const int soff = (k0 + min(ch, nch - 1) * KCH) * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int fr = lane & 15, fh = lane >> 4;
-  const int arow = wave * 32 + fr;
+    for (int j = 0; j < KCH_DMA; ++j) sdma_16(ars, buf + (KCH_DMA * wave + j) * 64, (int)avo[j], soff);
+  };
 
-  // Slab T is in stage CUR; the stage of slab T - 1 (NXT, free after this slab's barrier)
-  // receives slab T + 3.  The body has no branch (a branch would make the wait insertion
-  // forget which stage each in-flight load targets): past the last slab the load repeats the
-  // last one into a stage that is not read again, and the wait always leaves the two newer
-  // slabs' loads in flight.  A macro, so that each LDS access names its own stage object.
-#define ZDIT_SPLITK_SLAB(T, CUR, NXT)                                                                  \
+  u32x4 bq[KU_B];
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // One chunk of A in buffer CUR (every wave's loads landed), the next one's loads go to NXT
+  // (every wave finished reading it before the barrier that ended the previous chunk).  Its 8
+  // slabs: the weights of slab T from bq, the A fragments from CUR, four MFMAs, then the weight
+  // load of slab T + KU_B.  At the end: this wave's chunk loads (issued before the chunk's 8
+  // weight loads) are complete, then the barrier.  A macro, so that each LDS access names its
+  // own buffer object.
+#define ZDIT_SK_CHUNK(CH, CUR, NXT)                                                                    \
   {                                                                                                   \
-    const int t_ = (T);                                                                               \
-    __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(2 * S_DMA));                                              \
-    /* every wave's loads of slab T are complete (each waited for its own): a bare barrier,           \
-       without the fence that would also wait for the slabs still in flight */                       \
+    const int ch_ = (CH);                                                                             \
+    dma_a(ch_ + 1, NXT);                                                                              \
+    _Pragma("unroll") for (int s = 0; s < KCH_SL; ++s) {                                              \
+      const int tt = ch_ * KCH_SL + s;                                                                \
+      const int q = (ch_ & 1) * KCH_SL + s; /* ring slot: chunks alternate halves of bq */           \
+      const u32x4 bv = tt < nk ? bq[q] : zero4;                                                       \
+      const bf16x8 bf = __builtin_bit_cast(bf16x8, bv);                                               \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+        const int r = 16 * i + fr;                                                                    \
+        const bf16x8 af = __builtin_bit_cast(bf16x8, CUR[aslot(r, s * 4 + fh)]);                      \
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i], 0, 0, 0);                    \
+      }                                                                                               \
+      bq[q] = ldb(tt + KU_B);                                                                         \
+    }                                                                                                 \
+    __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(KCH_SL));                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                                \
     __builtin_amdgcn_s_barrier();                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                                \
-    bf16x8 fa[2], fb[4];                                                                              \
-    for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8, CUR[sswz(arow + 16 * i, fh)]);    \
-    for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8, CUR[SA_CHUNKS + sswz(16 * j + fr, fh)]); \
-    issue(min(t_ + 3, nk - 1), NXT);                                                                  \
-    for (int i = 0; i < 2; ++i)                                                                       \
-      for (int j = 0; j < 4; ++j)                                                                     \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);       \
   }
 
-  issue(0, L0);
-  issue(min(1, nk - 1), L1);
-  issue(min(2, nk - 1), L2);
-  int t = 0;
-  for (; t + 4 <= nk; t += 4) {
-    ZDIT_SPLITK_SLAB(t, L0, L3)
-    ZDIT_SPLITK_SLAB(t + 1, L1, L0)
-    ZDIT_SPLITK_SLAB(t + 2, L2, L1)
-    ZDIT_SPLITK_SLAB(t + 3, L3, L2)
+  dma_a(0, A0);
+#pragma unroll
+  for (int u = 0; u < KU_B; ++u) bq[u] = ldb(u);
+  __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(KU_B));
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  int ch = 0;
+  for (; ch + 2 <= nch; ch += 2) {
+    ZDIT_SK_CHUNK(ch, A0, A1)
+    ZDIT_SK_CHUNK(ch + 1, A1, A0)
   }
-  if (t < nk) ZDIT_SPLITK_SLAB(t, L0, L3)
-  if (t + 1 < nk) ZDIT_SPLITK_SLAB(t + 1, L1, L0)
-  if (t + 2 < nk) ZDIT_SPLITK_SLAB(t + 2, L2, L1)
-#undef ZDIT_SPLITK_SLAB
-  // the repeated loads past the last slab are still landing
+  if (ch < nch) ZDIT_SK_CHUNK(ch, A0, A1)
+#undef ZDIT_SK_CHUNK
+  // the loads past the range are still landing
   __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(0));
 
   // partial tile: lane holds rows 4 (lane / 16) + e of each 16 x 16 tile, column lane % 16
-  const int nv0 = (second ? a.N : 0) + n0;
-  float* part = a.part + (int64_t)split * a.M * a.Nv;
+  const int n = n0 + fr;
+  if (n >= a.N) return;
+  float* part = a.part + (int64_t)split * a.M * a.Nv + (second ? a.N : 0) + n;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 16 * j + fr;
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wave * 32 + 16 * i + 4 * fh + e;
-        if (m < a.M) part[(int64_t)m * a.Nv + nv0 + 16 * j + fr] = acc[i][j][e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + 16 * i + 4 * fh + e;
+      if (m < a.M) part[(int64_t)m * a.Nv] = acc[i][e];
     }
 }
 
@@ -154,9 +176,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmAr
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   const RowMap& rm = g.out;
-  const int b = m / rm.rows_per_batch, r = m - b * rm.rows_per_batch;
-  if (r >= rm.valid[b]) return;
-  const int64_t off = b * rm.batch_stride + (int64_t)r * rm.ld + n;
+  int b;
+  int64_t off;
+  if (a.c_rows) {
+    const int row = a.c_rows[m];
+    b = row / rm.rows_per_batch;
+    off = (int64_t)row * rm.ld + n;
+  } else {
+    b = m / rm.rows_per_batch;
+    const int r = m - b * rm.rows_per_batch;
+    if (r >= rm.valid[b]) return;
+    off = b * rm.batch_stride + (int64_t)r * rm.ld + n;
+  }
   if constexpr (EPI == EPI_RESID) {
     float* x = (float*)g.C + off;
     float4 xv = *(float4*)x;
@@ -189,13 +220,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmAr
 SplitKArgs splitk_plan(int epi, int M, int N, int K) {
   SplitKArgs a{};
   a.M = M; a.N = N; a.K = K;
-  a.col_tiles = (N + SBN - 1) / SBN;
+  a.col_tiles = (N + KWG - 1) / KWG;
   a.Nv = epi == EPI_SWIGLU ? 2 * N : N;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
-  // about 512 workgroups for one 128-row tile; ranges of at least 128 columns of K
-  int splits = (512 + vtiles - 1) / vtiles;
-  splits = max(1, min(splits, K / 128));
-  a.ks = ((K + splits - 1) / splits + SBK - 1) / SBK * SBK;
+  // at most about 512 workgroups for one row tile (two per CU); ranges of whole 256-column
+  // chunks
+  const int units = (K + KCH - 1) / KCH;
+  const int ranges = max(1, 512 / vtiles);
+  a.ks = ((units + ranges - 1) / ranges) * KCH;
   a.splits = (K + a.ks - 1) / a.ks;
   return a;
 }
@@ -205,12 +237,14 @@ size_t splitk_workspace(int epi, int M, int N, int K) {
   return (size_t)a.splits * M * a.Nv * sizeof(float);
 }
 
-hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s) {
+hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows,
+                              int a_phys_rows, const int* c_rows) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   SplitKArgs a = splitk_plan(epi, g.M, g.N, g.K);
   a.A = g.A; a.B = g.B; a.B2 = g.B2; a.part = part; a.lda = (int)g.lda; a.ldb = (int)g.ldb;
+  a.a_rows = a_rows; a.a_phys_rows = a_phys_rows; a.c_rows = c_rows;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
-  dim3 grid(vtiles, a.splits, (g.M + SBM - 1) / SBM);
+  dim3 grid(vtiles, a.splits, (g.M + KM - 1) / KM);
   hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(256), 0, s, a);
   const unsigned rb = (unsigned)(((int64_t)g.M * (g.N / 4) + 255) / 256);
   switch (epi) {
