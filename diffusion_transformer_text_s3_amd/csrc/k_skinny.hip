@@ -2,15 +2,16 @@
 // the 256 x 256 tiles of the main GEMM would occupy a few dozen of the 256 CUs while the time
 // goes into streaming the weights from HBM.
 //
-// Split-K with the weights streamed into registers.  A 256-thread workgroup owns one tile of up
-// to 64 rows, 64 columns of C and one K range; wavefront w owns columns n0 + 16 w .. + 15.  Per
+// Split-K with the weights streamed into registers.  A 512-thread workgroup owns one tile of up
+// to 64 rows, 128 columns of C and one K range; wavefront w owns columns n0 + 16 w .. + 15.  Per
 // 32-wide slab a lane loads 16 bytes of its weight row (the B fragment of
 // v_mfma_f32_16x16x32_bf16: row l % 16, k 8 (l / 16) ..) KU_B slabs ahead, so each wavefront
 // keeps 16 KB of weights in flight, reads the four A fragments (16-row tiles) from LDS and
 // issues four MFMAs.  A arrives in LDS in chunks of 256 columns (32 KB), double-buffered and
 // fetched one chunk ahead by direct-to-LDS loads; one barrier per chunk.  The K ranges are whole
-// multiples of 256 columns except the last, their number depends on N and K only (about 512
-// workgroups per row tile), so every output's sum has the same K split and order whatever M
+// multiples of 256 columns except the last, their number depends on N and K only (at most
+// about 256 workgroups per row tile, one per CU), so every output's sum has the same K split and
+// order whatever M
 // is.  The fp32 partial tiles go to a workspace [splits][M][Nv]; a second kernel sums them in
 // split order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
 // paired W1 / W3 partials (Nv = 2N: the W3 columns follow the W1 columns).  Optional row maps
@@ -24,14 +25,14 @@ namespace {
 
 constexpr int KM = 64;                  // rows per tile
 constexpr int KNW = 16;                 // columns per wavefront
-constexpr int KWG = 4 * KNW;            // columns per workgroup
+constexpr int KWG = 8 * KNW;            // columns per workgroup
 constexpr int KSL = 32;                 // slab width (one MFMA k-step)
 constexpr int KU_B = 16;                // weight slabs in flight per lane
 constexpr int KCH = 256;                // A chunk width (K columns)
 constexpr int KCH_SL = KCH / KSL;       // 8 slabs per chunk
 constexpr int KCH_CPR = KCH / 8;        // 32 16-byte chunks per A row of a chunk
 constexpr int KCH_CHUNKS = KM * KCH_CPR;  // 2048 (32 KB)
-constexpr int KCH_DMA = KCH_CHUNKS / 64 / 4;  // 8 wave loads per wave per chunk
+constexpr int KCH_DMA = KCH_CHUNKS / 64 / 8;  // 4 wave loads per wave per chunk
 constexpr int kSBufFlags = 0x00020000;
 constexpr int s_waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
@@ -48,7 +49,7 @@ __device__ __forceinline__ void sdma_16(const __amdgpu_buffer_rsrc_t rs, const u
                                            0, 0);
 }
 
-__global__ __launch_bounds__(256) void gemm_splitk_kernel(SplitKArgs a) {
+__global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
   // two separate objects, so reads of one chunk buffer are not ordered behind the in-flight
   // direct-to-LDS writes of the other
   __shared__ uint4 A0[KCH_CHUNKS], A1[KCH_CHUNKS];
@@ -223,10 +224,10 @@ SplitKArgs splitk_plan(int epi, int M, int N, int K) {
   a.col_tiles = (N + KWG - 1) / KWG;
   a.Nv = epi == EPI_SWIGLU ? 2 * N : N;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
-  // at most about 512 workgroups for one row tile (two per CU); ranges of whole 256-column
+  // at most about 256 workgroups for one row tile (one per CU); ranges of whole 256-column
   // chunks
   const int units = (K + KCH - 1) / KCH;
-  const int ranges = max(1, 512 / vtiles);
+  const int ranges = max(1, 256 / vtiles);
   a.ks = ((units + ranges - 1) / ranges) * KCH;
   a.splits = (K + a.ks - 1) / a.ks;
   return a;
@@ -245,7 +246,7 @@ hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream
   a.a_rows = a_rows; a.a_phys_rows = a_phys_rows; a.c_rows = c_rows;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
   dim3 grid(vtiles, a.splits, (g.M + KM - 1) / KM);
-  hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(512), 0, s, a);
   const unsigned rb = (unsigned)(((int64_t)g.M * (g.N / 4) + 255) / 256);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(rb), dim3(256), 0, s, a, g); break;
