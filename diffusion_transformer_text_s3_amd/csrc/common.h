@@ -77,8 +77,26 @@ struct SplitKArgs {
 };
 SplitKArgs splitk_plan(int epi, int M, int N, int K);
 size_t splitk_workspace(int epi, int M, int N, int K);
+// Work folded into the split-K reduction.  QK_NORM_ROPE (with EPI_STORE and a row scatter map
+// into rows b * L + r of C): the q and k heads of each row are RMS-normalised over their 128 dims
+// (gains gq / gk, in fp32 from the summed projection) and rotated by RoPE over dimension pairs
+// (i, i + 64) at position r (cos / sin [b][r][64]); v heads are rounded as they are.
+// RESID_NORM (with EPI_RESID and a row scatter map): after the residual add, each row of the
+// residual stream is RMS-normalised with `gain` and written as bf16 to row c_rows[m] of h.
+struct SplitKFuse {
+  enum Kind { NONE = 0, QK_NORM_ROPE = 1, RESID_NORM = 2 } kind = NONE;
+  const float* gq = nullptr;
+  const float* gk = nullptr;
+  const float* cos = nullptr;
+  const float* sin = nullptr;
+  int64_t tab_bstride = 0;
+  int n_heads = 0, n_kv_heads = 0, L = 0;
+  const float* gain = nullptr;
+  void* h = nullptr;
+  float eps = 0.f;
+};
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows = nullptr,
-                              int a_phys_rows = 0, const int* c_rows = nullptr);
+                              int a_phys_rows = 0, const int* c_rows = nullptr, const SplitKFuse* fuse = nullptr);
 
 // q, k, v rows: row r of branch b at qkv + (b * s_max + r) * row_stride elements, query head
 // h at column h * 128, key head j at k_col + j * 128, value head j at v_col + j * 128.  Query

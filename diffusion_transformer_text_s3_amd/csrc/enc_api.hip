@@ -78,13 +78,13 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
 // padded [B * L] layout, read through the valid-row list; C_SCATTER: C too), with M the
 // number of valid rows.  Else the main GEMM over the padded rows (the RowMap skips padding).
 hipError_t enc_gemm(int epi, GemmArgs g, bool a_gather, bool c_scatter, int B, int L, int Mc, const EncPlan& pl,
-                    char* ws, hipStream_t st) {
+                    char* ws, hipStream_t st, const SplitKFuse* fuse = nullptr) {
   if (!pl.splitk) return launch_gemm_bf16(epi, g, st);
   const int* rows = (const int*)(ws + pl.rows);
   g.M = Mc;
   if (!c_scatter) g.out = compact_rows(Mc, g.out.ld);
   return launch_gemm_splitk(epi, g, (float*)(ws + pl.part), st, a_gather ? rows : nullptr, B * L,
-                            c_scatter ? rows : nullptr);
+                            c_scatter ? rows : nullptr, fuse);
 }
 
 zdit_status check_ids(int batch, int max_len, int vocab, const int32_t* ids, const int32_t* len) {
@@ -119,9 +119,14 @@ AttnArgs enc_attn_args(const zdit_enc_cfg& c, int B, int L, const int32_t* len, 
   return aa;
 }
 
-// One block on B branches of L rows (x fp32 [B * L, hidden], rows >= len[b] stay 0).
+// One block on B branches of L rows (x fp32 [B * L, hidden], rows >= len[b] stay 0).  On the
+// split-K path the q/k norm + RoPE ride on the q/k/v reduction and each residual reduction also
+// writes the RMSNorm that follows it: the post-attention norm, and the next block's input norm
+// (next_in_norm; NULL after the last block).  There the input norm of this block is already in h
+// except for the first block (in_normed false).
 zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, int L, const int32_t* len,
-                      float* x, const EncPlan& pl, char* ws, hipStream_t st) {
+                      float* x, const EncPlan& pl, char* ws, hipStream_t st, bool in_normed,
+                      const float* next_in_norm) {
   const int D = c.hidden, I = c.inter, M = B * L, W = qkv_width(c), Dq = c.n_heads * kHeadDim;
   int Mc = 0;  // valid rows
   for (int b = 0; b < B; ++b) Mc += len[b];
@@ -136,31 +141,45 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   na.gain = w.in_norm; na.shift = nullptr; na.scale = nullptr; na.mod_bstride = 0;
   na.eps = c.norm_eps; na.out = h;
   for (int b = 0; b < kMaxBatch; ++b) na.valid[b] = b < B ? len[b] : 0;
-  HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
+  if (!pl.splitk || !in_normed) HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
 
   GemmArgs g{};
   g.A = h; g.B = w.w_qkv; g.C = qkv; g.M = M; g.N = W; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, W);
-  HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st));
-
-  QkNormRopeArgs qa;
-  qa.qkv = qkv; qa.row_stride = W; qa.k_col = Dq; qa.n_heads = c.n_heads; qa.n_kv_heads = c.n_kv_heads;
-  qa.gq = w.q_norm; qa.gk = w.k_norm; qa.cos = (const float*)(ws + pl.cos); qa.sin = (const float*)(ws + pl.sin);
-  qa.tab_bstride = (int64_t)L * 64; qa.eps = c.norm_eps; qa.batch = B; qa.s_max = L;
-  for (int b = 0; b < kMaxBatch; ++b) qa.seq_len[b] = b < B ? len[b] : 0;
-  HIP_TRY(launch_qknorm_rope(qa, st));
+  if (pl.splitk) {
+    SplitKFuse f;
+    f.kind = SplitKFuse::QK_NORM_ROPE;
+    f.gq = w.q_norm; f.gk = w.k_norm; f.cos = (const float*)(ws + pl.cos); f.sin = (const float*)(ws + pl.sin);
+    f.tab_bstride = (int64_t)L * 64; f.n_heads = c.n_heads; f.n_kv_heads = c.n_kv_heads; f.L = L; f.eps = c.norm_eps;
+    HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st, &f));
+  } else {
+    HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st));
+    QkNormRopeArgs qa;
+    qa.qkv = qkv; qa.row_stride = W; qa.k_col = Dq; qa.n_heads = c.n_heads; qa.n_kv_heads = c.n_kv_heads;
+    qa.gq = w.q_norm; qa.gk = w.k_norm; qa.cos = (const float*)(ws + pl.cos); qa.sin = (const float*)(ws + pl.sin);
+    qa.tab_bstride = (int64_t)L * 64; qa.eps = c.norm_eps; qa.batch = B; qa.s_max = L;
+    for (int b = 0; b < kMaxBatch; ++b) qa.seq_len[b] = b < B ? len[b] : 0;
+    HIP_TRY(launch_qknorm_rope(qa, st));
+  }
 
   HIP_TRY(launch_attn(ZDIT_BF16, enc_attn_args(c, B, L, len, qkv, vt, o), st));
 
   RowMap xr;
   xr.rows_per_batch = L; xr.batch_stride = (int64_t)L * D; xr.ld = D;
   for (int b = 0; b < kMaxBatch; ++b) xr.valid[b] = b < B ? len[b] : 0;
+  SplitKFuse rn;  // residual reduction + the RMSNorm after it (split-K path)
+  rn.kind = SplitKFuse::RESID_NORM;
+  rn.h = h; rn.eps = c.norm_eps;
   g = GemmArgs{};
   g.A = o; g.B = w.w_o; g.C = x; g.M = M; g.N = D; g.K = Dq; g.lda = Dq; g.ldb = Dq; g.out = xr;
-  HIP_TRY(enc_gemm(EPI_RESID, g, true, true, B, L, Mc, pl, ws, st));
-
-  na.gain = w.post_norm;
-  HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
+  if (pl.splitk) {
+    rn.gain = w.post_norm;
+    HIP_TRY(enc_gemm(EPI_RESID, g, true, true, B, L, Mc, pl, ws, st, &rn));
+  } else {
+    HIP_TRY(enc_gemm(EPI_RESID, g, true, true, B, L, Mc, pl, ws, st));
+    na.gain = w.post_norm;
+    HIP_TRY(launch_rmsnorm_mod(ZDIT_BF16, na, st));
+  }
 
   g = GemmArgs{};
   g.A = h; g.B = w.w_gate; g.B2 = w.w_up; g.C = u; g.M = M; g.N = I; g.K = D; g.lda = D; g.ldb = D;
@@ -170,7 +189,12 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
 
   g = GemmArgs{};
   g.A = u; g.B = w.w_down; g.C = x; g.M = M; g.N = D; g.K = I; g.lda = I; g.ldb = I; g.out = xr;
-  HIP_TRY(enc_gemm(EPI_RESID, g, false, true, B, L, Mc, pl, ws, st));
+  if (pl.splitk && next_in_norm) {
+    rn.gain = next_in_norm;
+    HIP_TRY(enc_gemm(EPI_RESID, g, false, true, B, L, Mc, pl, ws, st, &rn));
+  } else {
+    HIP_TRY(enc_gemm(EPI_RESID, g, false, true, B, L, Mc, pl, ws, st));
+  }
   return ZDIT_OK;
 }
 
@@ -223,8 +247,12 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
   if (zdit_status s = embed_rows(batch, max_len, c.hidden, ids, len, w->embed, hidden_out, (int*)(base + pl.ids), st))
     return s;
   if (pl.splitk) HIP_TRY(launch_valid_rows(batch, max_len, len, (int*)(base + pl.rows), st));
-  for (int i = 0; i < c.n_layers - 1; ++i)
-    if (zdit_status s = enc_block(c, w->layers[i], batch, max_len, len, hidden_out, pl, base, st)) return s;
+  const int nb = c.n_layers - 1;
+  for (int i = 0; i < nb; ++i) {
+    const float* next = i + 1 < nb ? w->layers[i + 1].in_norm : nullptr;
+    if (zdit_status s = enc_block(c, w->layers[i], batch, max_len, len, hidden_out, pl, base, st, i > 0, next))
+      return s;
+  }
   return ok();
 }
 

@@ -16,7 +16,9 @@
 // split order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
 // paired W1 / W3 partials (Nv = 2N: the W3 columns follow the W1 columns).  Optional row maps
 // gather the rows of A and scatter the rows of C, so a caller can run only the valid rows of a
-// padded batch.  Buffer resources make rows past M or N read as zero.
+// padded batch.  The reduction can also carry the work that follows it (SplitKFuse): the
+// encoder's q/k RMSNorm + RoPE after the q/k/v projection, or the RMSNorm after a residual add.
+// Buffer resources make rows past M or N read as zero.
 #include "common.h"
 
 namespace zdit {
@@ -216,6 +218,113 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmAr
   }
 }
 
+// The q/k/v reduction with the encoder's per-head RMSNorm and RoPE: 16 lanes per (row, head),
+// lane j holding dims 8 j .. 8 j + 7; the partner of dim i < 64 is dim i + 64, in lane j ^ 8.
+// Sums in split order, then for q and k heads y = x / sqrt(mean(x^2) + eps) * g and
+// y_i c - y_{i+64} s, y_{i+64} c + y_i s (each product and sum rounded separately), one rounding
+// to bf16; v heads are rounded as summed.
+__global__ __launch_bounds__(256) void splitk_reduce_qkv_kernel(SplitKArgs a, GemmArgs g, SplitKFuse f) {
+#pragma clang fp contract(off)
+  const int nh = f.n_heads + 2 * f.n_kv_heads;
+  const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int j = threadIdx.x & 15;
+  if (item >= (int64_t)a.M * nh) return;  // whole 16-lane groups leave together
+  const int m = (int)(item / nh), hh = (int)(item % nh);
+  const int col = hh * kHeadDim + j * 8;
+  const int64_t plane = (int64_t)a.M * a.Nv;
+  const float* p = a.part + (int64_t)m * a.Nv + col;
+  float4 lo = *(const float4*)p, hi = *(const float4*)(p + 4);
+  for (int k = 1; k < a.splits; ++k) {
+    const float4 u = *(const float4*)(p + k * plane), v = *(const float4*)(p + k * plane + 4);
+    lo.x += u.x; lo.y += u.y; lo.z += u.z; lo.w += u.w;
+    hi.x += v.x; hi.y += v.y; hi.z += v.z; hi.w += v.w;
+  }
+  const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int row = a.c_rows[m];
+  bf16x8 out;
+  if (hh < f.n_heads + f.n_kv_heads) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) ss += __shfl_xor(ss, d, 64);
+    const float den = sqrtf(ss / (float)kHeadDim + f.eps);
+    const float* gv = (hh < f.n_heads ? f.gq : f.gk) + j * 8;
+    float y[8], yp[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] / den * gv[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yp[e] = __shfl_xor(y[e], 8, 64);
+    const int b = row / f.L, r = row - b * f.L;
+    const int64_t tb = b * f.tab_bstride + (int64_t)r * 64 + (j & 7) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = f.cos[tb + e], sn = f.sin[tb + e];
+      const float t0 = y[e] * c, t1 = yp[e] * sn;
+      out[e] = (bf16)(j < 8 ? t0 - t1 : t0 + t1);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (bf16)x[e];
+  }
+  *(bf16x8*)((bf16*)g.C + (int64_t)row * g.out.ld + col) = out;
+}
+
+// The residual reduction with the following RMSNorm: one workgroup per row.  x += sum of the
+// partials (times the gate if any), then h = x / sqrt(mean(x^2) + eps) * gain as bf16 (the same
+// formula as the RMSNorm kernel).  Rows up to 4096 wide (4 float4 per thread).
+__global__ __launch_bounds__(256) void splitk_reduce_resid_norm_kernel(SplitKArgs a, GemmArgs g, SplitKFuse f) {
+  __shared__ float wsum[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int nq = a.N >> 2;
+  const int64_t plane = (int64_t)a.M * a.Nv;
+  const int row = a.c_rows[m];
+  const int b = row / g.out.rows_per_batch;
+  float* x = (float*)g.C + (int64_t)row * g.out.ld;
+  const float* gate = g.vec ? g.vec + b * g.vec_bstride : nullptr;
+  float4 xv[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nq) {
+      const float* p = a.part + (int64_t)m * a.Nv + 4 * c;
+      float4 s4 = *(const float4*)p;
+      for (int k = 1; k < a.splits; ++k) {
+        const float4 v = *(const float4*)(p + k * plane);
+        s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
+      }
+      float4 v = *(float4*)(x + 4 * c);
+      if (gate) {
+        v.x += gate[4 * c] * s4.x; v.y += gate[4 * c + 1] * s4.y; v.z += gate[4 * c + 2] * s4.z; v.w += gate[4 * c + 3] * s4.w;
+      } else {
+        v.x += s4.x; v.y += s4.y; v.z += s4.z; v.w += s4.w;
+      }
+      *(float4*)(x + 4 * c) = v;
+      xv[i] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  ss = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const float rinv = 1.0f / sqrtf(ss / (float)a.N + f.eps);
+  bf16* h = (bf16*)f.h + (int64_t)row * a.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nq) {
+      const float4 gg = *(const float4*)(f.gain + 4 * c);
+      bf16x4 o;
+      o[0] = (bf16)(xv[i].x * rinv * gg.x); o[1] = (bf16)(xv[i].y * rinv * gg.y);
+      o[2] = (bf16)(xv[i].z * rinv * gg.z); o[3] = (bf16)(xv[i].w * rinv * gg.w);
+      *(bf16x4*)(h + 4 * c) = o;
+    }
+  }
+}
+
 }  // namespace
 
 SplitKArgs splitk_plan(int epi, int M, int N, int K) {
@@ -239,7 +348,7 @@ size_t splitk_workspace(int epi, int M, int N, int K) {
 }
 
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows,
-                              int a_phys_rows, const int* c_rows) {
+                              int a_phys_rows, const int* c_rows, const SplitKFuse* fuse) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   SplitKArgs a = splitk_plan(epi, g.M, g.N, g.K);
   a.A = g.A; a.B = g.B; a.B2 = g.B2; a.part = part; a.lda = (int)g.lda; a.ldb = (int)g.ldb;
@@ -247,6 +356,17 @@ hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
   dim3 grid(vtiles, a.splits, (g.M + KM - 1) / KM);
   hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(512), 0, s, a);
+  if (fuse && fuse->kind == SplitKFuse::QK_NORM_ROPE) {
+    if (epi != EPI_STORE || !c_rows) return hipErrorInvalidValue;
+    const int64_t lanes = (int64_t)g.M * (fuse->n_heads + 2 * fuse->n_kv_heads) * 16;
+    hipLaunchKernelGGL(splitk_reduce_qkv_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s, a, g, *fuse);
+    return hipGetLastError();
+  }
+  if (fuse && fuse->kind == SplitKFuse::RESID_NORM) {
+    if (epi != EPI_RESID || !c_rows || g.N > 4096 || g.N % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_reduce_resid_norm_kernel, dim3(g.M), dim3(256), 0, s, a, g, *fuse);
+    return hipGetLastError();
+  }
   const unsigned rb = (unsigned)(((int64_t)g.M * (g.N / 4) + 255) / 256);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(rb), dim3(256), 0, s, a, g); break;
