@@ -11,9 +11,8 @@
 // fetched one chunk ahead by direct-to-LDS loads; one barrier per chunk.  The K ranges are whole
 // multiples of 256 columns except the last, their number depends on N and K only (at most
 // about 256 workgroups per row tile, one per CU), so every output's sum has the same K split and
-// order whatever M
-// is.  The fp32 partial tiles go to a workspace [splits][M][Nv]; a second kernel sums them in
-// split order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
+// order whatever M is.  The fp32 partial tiles go to a workspace [splits][M][Nv]; a second
+// kernel sums them in split order and applies the epilogue: bf16 store, fp32 gated residual add, or SwiGLU on the
 // paired W1 / W3 partials (Nv = 2N: the W3 columns follow the W1 columns).  Optional row maps
 // gather the rows of A and scatter the rows of C, so a caller can run only the valid rows of a
 // padded batch.  The reduction can also carry the work that follows it (SplitKFuse): the
@@ -76,8 +75,8 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
     return __builtin_amdgcn_raw_buffer_load_b128(brs, (int)(bvo + (unsigned)min(t, nk - 1) * (KSL * 2)), 0, 0);
   };
 
-  // A chunk loads: wave load j of this wave fills slots 64 (8 wave + j) + lane, i.e. row
-  // 2 (8 wave + j) + lane / 32 and physical chunk lane % 32; the lane fetches the logical chunk
+  // A chunk loads: wave load j of this wave fills slots 64 (KCH_DMA wave + j) + lane, i.e. row
+  // 2 (KCH_DMA wave + j) + lane / 32 and physical chunk lane % 32; the lane fetches the logical chunk
   // that belongs there.  A row past M gets an offset past the end of the resource (2^31 + k
   // stays out of range), so it loads as zero.
   const bool gather = a.a_rows != nullptr;
