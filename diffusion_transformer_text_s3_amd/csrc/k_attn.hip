@@ -320,6 +320,24 @@ __global__ __launch_bounds__(ATT_NT) __attribute__((amdgpu_waves_per_eu(2))) voi
   dma_k(min(1, nkt - 1), K1);
   __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
   __syncthreads();
+  if (q0 + wave * 32 >= S) {
+    // Every query of this wavefront is padding (the tile's last rows): it keeps loading its
+    // share of each key block and meets every barrier of the working wavefronts (the prologue's
+    // second one and one per step), and writes zeros.
+    __syncthreads();
+    for (int t = 0; t < nkt; ++t) {
+      dma_v(min(t + 1, nkt - 1), (t & 1) ? V0 : V1);
+      dma_k(min(t + 2, nkt - 1), (t & 1) ? K1 : K0);
+      __builtin_amdgcn_s_waitcnt(kAttVmcnt0);
+      __syncthreads();
+    }
+    if (q < a.s_max) {
+      bf16* op = out + ((int64_t)b * a.s_max + q) * D + h * kHeadDim;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) *(bf16x4*)(op + 8 * c + 4 * fh) = bf16x4{};
+    }
+    return;
+  }
   f32x16 sA[2], sB[2];
   qk(K0, sA);
   m_run = tm == 0 ? block_max(std::true_type{}, 0, sA) : block_max(std::false_type{}, 0, sA);
