@@ -94,6 +94,10 @@ struct SplitKFuse {
   const float* gain = nullptr;
   void* h = nullptr;
   float eps = 0.f;
+  // QK_NORM_ROPE: when set, v heads go transposed into vt [b][n_kv_heads][128][s_pad] in the
+  // attention kernel's key order (and not into C)
+  void* vt = nullptr;
+  int s_pad = 0;
 };
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows = nullptr,
                               int a_phys_rows = 0, const int* c_rows = nullptr, const SplitKFuse* fuse = nullptr);
@@ -180,6 +184,9 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 // The valid rows of a padded batch in order: entry i (i < sum of len) is b * s_max + r for
 // the i-th pair (b, r < len[b]).
 hipError_t launch_valid_rows(int batch, int s_max, const int* len, int* rows, hipStream_t s);
+
+// zero `bytes` (a multiple of 16) at 16-byte aligned p
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 
 // measurement: `workgroups` x 256 threads, each wave 4 x iters bf16 32x32x16 MFMAs; out
 // [workgroups * 256] fp32

@@ -66,8 +66,15 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   p.qkv = off; off += al256(M * qkv_width(c) * 2);
   p.vt = off;  off += al256(attn_vt_bytes(0, B, L, c.n_kv_heads));
   p.o = off;   off += al256(M * c.n_heads * kHeadDim * 2);
-  p.u = r0;  // the SwiGLU activation reuses the attention region (dead by then)
-  off = std::max(off, r0 + al256(M * (size_t)c.inter * 2));
+  if (p.splitk) {
+    // V^T is written by the q/k/v reduction and its padding is zeroed once per forward, so
+    // nothing else may write there
+    p.u = off;
+    off += al256(M * (size_t)c.inter * 2);
+  } else {
+    p.u = r0;  // the SwiGLU activation reuses the attention region (dead by then)
+    off = std::max(off, r0 + al256(M * (size_t)c.inter * 2));
+  }
   p.part = off;
   if (p.splitk) off += al256(enc_part_bytes(c, (int)M));
   p.total = off;
@@ -151,6 +158,7 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
     f.kind = SplitKFuse::QK_NORM_ROPE;
     f.gq = w.q_norm; f.gk = w.k_norm; f.cos = (const float*)(ws + pl.cos); f.sin = (const float*)(ws + pl.sin);
     f.tab_bstride = (int64_t)L * 64; f.n_heads = c.n_heads; f.n_kv_heads = c.n_kv_heads; f.L = L; f.eps = c.norm_eps;
+    f.vt = vt; f.s_pad = round_up(L, 64);
     HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st, &f));
   } else {
     HIP_TRY(enc_gemm(EPI_STORE, g, true, true, B, L, Mc, pl, ws, st));
@@ -162,7 +170,9 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
     HIP_TRY(launch_qknorm_rope(qa, st));
   }
 
-  HIP_TRY(launch_attn(ZDIT_BF16, enc_attn_args(c, B, L, len, qkv, vt, o), st));
+  AttnArgs aa = enc_attn_args(c, B, L, len, qkv, vt, o);
+  aa.vt_ready = pl.splitk ? 1 : 0;  // the q/k/v reduction wrote V^T
+  HIP_TRY(launch_attn(ZDIT_BF16, aa, st));
 
   RowMap xr;
   xr.rows_per_batch = L; xr.batch_stride = (int64_t)L * D; xr.ld = D;
@@ -246,7 +256,11 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
 
   if (zdit_status s = embed_rows(batch, max_len, c.hidden, ids, len, w->embed, hidden_out, (int*)(base + pl.ids), st))
     return s;
-  if (pl.splitk) HIP_TRY(launch_valid_rows(batch, max_len, len, (int*)(base + pl.rows), st));
+  if (pl.splitk) {
+    HIP_TRY(launch_valid_rows(batch, max_len, len, (int*)(base + pl.rows), st));
+    // V^T positions of padding keys (never written by the q/k/v reduction) read as zero
+    HIP_TRY(launch_zero_fill(base + pl.vt, al256(attn_vt_bytes(0, batch, max_len, c.n_kv_heads)), st));
+  }
   const int nb = c.n_layers - 1;
   for (int i = 0; i < nb; ++i) {
     const float* next = i + 1 < nb ? w->layers[i + 1].in_norm : nullptr;

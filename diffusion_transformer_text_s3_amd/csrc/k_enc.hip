@@ -2,6 +2,8 @@
 // q/k RMSNorm followed by RoPE over dimension pairs (i, i + 64), and the list of valid rows
 // that lets the projections skip the padding.  The encoder's projections,
 // pre-norms, attention and residual adds run on the DiT's kernels.
+#include <algorithm>
+
 #include "common.h"
 
 namespace zdit {
@@ -96,6 +98,11 @@ __global__ __launch_bounds__(256) void valid_rows_kernel(RowsArgs a, int* rows) 
   rows[before + r] = i;
 }
 
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
 inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
@@ -112,6 +119,14 @@ hipError_t launch_valid_rows(int batch, int s_max, const int* len, int* rows, hi
   a.batch = batch; a.s_max = s_max;
   for (int b = 0; b < kMaxBatch; ++b) a.len[b] = b < batch ? len[b] : 0;
   hipLaunchKernelGGL(valid_rows_kernel, dim3(blocks_for((int64_t)batch * s_max)), dim3(256), 0, s, a, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 2048)), dim3(256), 0, s,
+                     (uint4*)p, n);
   return hipGetLastError();
 }
 

@@ -265,6 +265,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv_kernel(SplitKArgs a, Ge
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (bf16)x[e];
+    if (f.vt) {
+      // value head hk, token r of branch b -> V^T row (b, hk, d), key position: within each
+      // 16-key group, key t sits in chunk (t >> 2) & 1 at element (t & 3) + 4 (t >> 3)
+      const int b = row / f.L, r = row - b * f.L;
+      const int hk = hh - f.n_heads - f.n_kv_heads;
+      const int t = r & 15;
+      const int pos = ((r >> 4) * 2 + ((t >> 2) & 1)) * 8 + (t & 3) + 4 * (t >> 3);
+      bf16* vt = (bf16*)f.vt + ((int64_t)(b * f.n_kv_heads + hk) * kHeadDim + j * 8) * f.s_pad + pos;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(int64_t)e * f.s_pad] = out[e];
+      return;
+    }
   }
   *(bf16x8*)((bf16*)g.C + (int64_t)row * g.out.ld + col) = out;
 }
