@@ -226,6 +226,10 @@ hipError_t launch_temb(int batch, const float* t, int t_freq, int c_dim, float t
                        float* c, hipStream_t s);
 hipError_t launch_adaln(int precision, int batch, int c_dim, int n_out, const float* c,
                         const void* w, const float* b, float* out, hipStream_t s);
+// up to kMaxAdaJobs projections of the same c (weights w[i], bias b[i] -> out[i]) in one launch
+constexpr int kMaxAdaJobs = 40;
+hipError_t launch_adaln_multi(int precision, int batch, int c_dim, int n_out, const float* c, const void* const* w,
+                              const float* const* b, float* const* out, int n_jobs, hipStream_t s);
 hipError_t launch_copy_rows(const float* src, int64_t src_bstride, float* dst,
                             int64_t dst_bstride, int batch, int64_t n, hipStream_t s);
 

@@ -322,10 +322,20 @@ __global__ __launch_bounds__(256) void temb_kernel(TArgs ta, int t_freq, int c_d
 // ---------------------------------------------------------------------------------------
 constexpr int ADA_U = 4;
 
+// Several projections of the same c in one launch: blockIdx.y selects one (weights, bias,
+// output) triple.
+struct AdaJobs {
+  const void* w[kMaxAdaJobs];
+  const float* b[kMaxAdaJobs];
+  float* out[kMaxAdaJobs];
+};
+
 template <typename TW>
 __global__ __launch_bounds__(256) void adaln_kernel(int batch, int c_dim, int n_out, int lanes_per_row,
-                                                     const float* c, const TW* w, const float* bias,
-                                                     float* out) {
+                                                     const float* c, AdaJobs jobs) {
+  const TW* w = (const TW*)jobs.w[blockIdx.y];
+  const float* bias = jobs.b[blockIdx.y];
+  float* out = jobs.out[blockIdx.y];
   extern __shared__ float sc[];  // [batch][c_dim]
   for (int i = threadIdx.x; i < batch * c_dim; i += blockDim.x) sc[i] = silu(c[i]);
   __syncthreads();
@@ -483,18 +493,26 @@ hipError_t launch_temb(int batch, const float* t, int t_freq, int c_dim, float t
   return hipGetLastError();
 }
 
-hipError_t launch_adaln(int precision, int batch, int c_dim, int n_out, const float* c,
-                        const void* w, const float* b, float* out, hipStream_t s) {
+hipError_t launch_adaln_multi(int precision, int batch, int c_dim, int n_out, const float* c, const void* const* w,
+                              const float* const* b, float* const* out, int n_jobs, hipStream_t s) {
+  if (n_jobs < 1 || n_jobs > kMaxAdaJobs) return hipErrorInvalidValue;
+  AdaJobs jobs{};
+  for (int i = 0; i < n_jobs; ++i) { jobs.w[i] = w[i]; jobs.b[i] = b[i]; jobs.out[i] = out[i]; }
   const size_t shm = (size_t)batch * c_dim * sizeof(float);
   int L = 1;
   while (L < 64 && 8 * L < c_dim) L <<= 1;
   const int rows_per_block = 4 * (64 / L) * ADA_U;
-  dim3 grid((unsigned)((n_out + rows_per_block - 1) / rows_per_block));
+  dim3 grid((unsigned)((n_out + rows_per_block - 1) / rows_per_block), (unsigned)n_jobs);
   if (precision == 0)
-    hipLaunchKernelGGL(adaln_kernel<bf16>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, (const bf16*)w, b, out);
+    hipLaunchKernelGGL(adaln_kernel<bf16>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, jobs);
   else
-    hipLaunchKernelGGL(adaln_kernel<float>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, (const float*)w, b, out);
+    hipLaunchKernelGGL(adaln_kernel<float>, grid, dim3(256), shm, s, batch, c_dim, n_out, L, c, jobs);
   return hipGetLastError();
+}
+
+hipError_t launch_adaln(int precision, int batch, int c_dim, int n_out, const float* c,
+                        const void* w, const float* b, float* out, hipStream_t s) {
+  return launch_adaln_multi(precision, batch, c_dim, n_out, c, &w, &b, &out, 1, s);
 }
 
 hipError_t launch_copy_rows(const float* src, int64_t src_bstride, float* dst,

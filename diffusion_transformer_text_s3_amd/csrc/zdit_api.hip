@@ -175,6 +175,26 @@ struct StackPlan {
   BlockPlan bp;
 };
 
+// The adaLN modulations of the n blocks of a stage (the same c for all), in launches of up to
+// kMaxAdaJobs blocks: block i's six vectors at mod + i * batch * 6 * dim.
+hipError_t stage_adaln(int precision, int batch, const zdit_dims& d, const float* c, const zdit_block_w* blocks, int n,
+                       float* mod, hipStream_t st) {
+  const int D = d.dim;
+  for (int i0 = 0; i0 < n; i0 += kMaxAdaJobs) {
+    const int nj = std::min(kMaxAdaJobs, n - i0);
+    const void* w[kMaxAdaJobs];
+    const float* b[kMaxAdaJobs];
+    float* out[kMaxAdaJobs];
+    for (int j = 0; j < nj; ++j) {
+      w[j] = blocks[i0 + j].w_ada;
+      b[j] = blocks[i0 + j].b_ada;
+      out[j] = mod + (size_t)(i0 + j) * batch * 6 * D;
+    }
+    if (hipError_t e = launch_adaln_multi(precision, batch, d.c_dim, 6 * D, c, w, b, out, nj, st)) return e;
+  }
+  return hipSuccess;
+}
+
 StackPlan plan_stack(const zdit_model_cfg& cfg, int B, int lat_h, int lat_w, int max_cap_len,
                      const int* cap_len) {
   StackPlan p;
@@ -197,7 +217,9 @@ StackPlan plan_stack(const zdit_model_cfg& cfg, int B, int lat_h, int lat_w, int
   size_t off = 0;
   p.x = off; off += al256((size_t)B * p.s_max * D * 4);
   p.c = off; off += al256((size_t)B * d.c_dim * 4);
-  p.mod = off; off += al256((size_t)B * 6 * D * 4);
+  // one modulation set per adaLN block of a stage (noise refiners, or main blocks), computed by one launch
+  const int nmod = std::max(1, std::max(cfg.n_noise_ref, cfg.n_main));
+  p.mod = off; off += al256((size_t)nmod * B * 6 * D * 4);
   p.fmod = off; off += al256((size_t)B * 2 * D * 4);
   p.tab_img_c = off; off += al256((size_t)p.nimg * hp * 4);
   p.tab_img_s = off; off += al256((size_t)p.nimg * hp * 4);
@@ -330,10 +352,11 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   int len[kMaxBatch];
   // noise refiners: image rows only (branch 0 only when the image rows are shared)
   for (int b = 0; b < B; ++b) len[b] = p.nimg;
+  HIP_TRY(stage_adaln(P, Bi, d, c, w.noise_ref, cfg.n_noise_ref, mod, st));
   for (int i = 0; i < cfg.n_noise_ref; ++i) {
     const zdit_block_w& bw = w.noise_ref[i];
-    HIP_TRY(launch_adaln(P, Bi, d.c_dim, 6 * D, c, bw.w_ada, bw.b_ada, mod, st));
-    if (zdit_status s = block_forward(d, bw, Bi, p.nimg, len, x, xb, mod, ti_c, ti_s, 0, bws, st)) return s;
+    float* mod_i = mod + (size_t)i * Bi * 6 * D;
+    if (zdit_status s = block_forward(d, bw, Bi, p.nimg, len, x, xb, mod_i, ti_c, ti_s, 0, bws, st)) return s;
   }
   if (same_img)
     HIP_TRY(launch_copy_rows(x, 0, x + xb, xb, B - 1, (int64_t)p.nimg * D, st));
@@ -363,10 +386,11 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
 
   // main blocks on the joint sequence
   for (int b = 0; b < B; ++b) len[b] = p.S[b];
+  HIP_TRY(stage_adaln(P, B, d, c, w.main, cfg.n_main, mod, st));
   for (int i = 0; i < cfg.n_main; ++i) {
     const zdit_block_w& bw = w.main[i];
-    HIP_TRY(launch_adaln(P, B, d.c_dim, 6 * D, c, bw.w_ada, bw.b_ada, mod, st));
-    if (zdit_status s = block_forward(d, bw, B, p.s_max, len, x, xb, mod, tj_c, tj_s, 0, bws, st)) return s;
+    float* mod_i = mod + (size_t)i * B * 6 * D;
+    if (zdit_status s = block_forward(d, bw, B, p.s_max, len, x, xb, mod_i, tj_c, tj_s, 0, bws, st)) return s;
   }
   // final layer on the image rows
   HIP_TRY(launch_adaln(P, B, d.c_dim, 2 * D, c, w.final_ada_w, w.final_ada_b, fmod, st));
