@@ -59,6 +59,19 @@ def test_stack_tiny_full_depth_bf16():
         assert e <= 1e-2 and dr <= 0.025
 
 
+def test_stack_tiny_41_main_blocks_two_adaln_launches():
+    """The modulations of a stage are projected at most 40 blocks per launch: 41 main blocks
+    take two launches, the 41st block's slice written by the second."""
+    note("stack tiny 2+2+41 bf16 pair")
+    case = stack_case(synth.TINY.replace(n_main=41), 16, 16, (32, 7), seed=78)
+    got, _ = gpu_stack(case)
+    for b in range(2):
+        ref = oracle_stack(case, b)
+        e, dr = rel_l2(got[b], ref), drift(got[b], ref)
+        print(f"41-block stack branch {b}: rel-L2 {e:.2e} drift {dr:.2e}", flush=True)
+        assert e <= 1e-2 and dr <= 0.025
+
+
 def test_stack_tiny_fp32_debug_atol_1e4():
     note("stack tiny fp32 debug")
     case = stack_case(synth.TINY, 16, 16, (20,), seed=71)
