@@ -164,6 +164,34 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
 
 // One thread per 4 consecutive output columns of a row: the partials summed in split order,
 // then the epilogue.
+// Sums of the float4 at p0 + k * plane (and at p1 + k * plane) over the ranges k, in order;
+// the loads of up to 8 ranges are issued before their adds.
+__device__ __forceinline__ void sum_ranges(const float* p0, const float* p1, int64_t plane, int splits, float4& s0,
+                                           float4& s1) {
+  constexpr int KB = 8;
+  s0 = s1 = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < splits; k0 += KB) {
+    float4 t0[KB], t1[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (k0 + i < splits) {
+        t0[i] = *(const float4*)(p0 + (k0 + i) * plane);
+        if (p1) t1[i] = *(const float4*)(p1 + (k0 + i) * plane);
+      }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (k0 + i >= splits) break;
+      if (k0 + i == 0) {
+        s0 = t0[i];
+        if (p1) s1 = t1[i];
+      } else {
+        s0.x += t0[i].x; s0.y += t0[i].y; s0.z += t0[i].z; s0.w += t0[i].w;
+        if (p1) { s1.x += t1[i].x; s1.y += t1[i].y; s1.z += t1[i].z; s1.w += t1[i].w; }
+      }
+    }
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmArgs g) {
   const int nq = a.N >> 2;
@@ -172,11 +200,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmAr
   const int m = (int)(i / nq), n = (int)(i % nq) * 4;
   const int64_t plane = (int64_t)a.M * a.Nv;
   const float* p = a.part + (int64_t)m * a.Nv + n;
-  float4 s = *(const float4*)p;
-  for (int k = 1; k < a.splits; ++k) {
-    const float4 v = *(const float4*)(p + k * plane);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
+  float4 s, u;
+  sum_ranges(p, EPI == EPI_SWIGLU ? p + a.N : nullptr, plane, a.splits, s, u);
   const RowMap& rm = g.out;
   int b;
   int64_t off;
@@ -203,11 +228,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(SplitKArgs a, GemmAr
   } else {
     float o[4] = {s.x, s.y, s.z, s.w};
     if constexpr (EPI == EPI_SWIGLU) {
-      float4 u = *(const float4*)(p + a.N);
-      for (int k = 1; k < a.splits; ++k) {
-        const float4 v = *(const float4*)(p + a.N + k * plane);
-        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
-      }
       o[0] = ssilu(s.x) * u.x; o[1] = ssilu(s.y) * u.y; o[2] = ssilu(s.z) * u.z; o[3] = ssilu(s.w) * u.w;
     }
     bf16x4 ob;
@@ -232,12 +252,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv_kernel(SplitKArgs a, Ge
   const int col = hh * kHeadDim + j * 8;
   const int64_t plane = (int64_t)a.M * a.Nv;
   const float* p = a.part + (int64_t)m * a.Nv + col;
-  float4 lo = *(const float4*)p, hi = *(const float4*)(p + 4);
-  for (int k = 1; k < a.splits; ++k) {
-    const float4 u = *(const float4*)(p + k * plane), v = *(const float4*)(p + k * plane + 4);
-    lo.x += u.x; lo.y += u.y; lo.z += u.z; lo.w += u.w;
-    hi.x += v.x; hi.y += v.y; hi.z += v.z; hi.w += v.w;
-  }
+  float4 lo, hi;
+  sum_ranges(p, p + 4, plane, a.splits, lo, hi);
   const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   const int row = a.c_rows[m];
   bf16x8 out;
@@ -283,56 +299,47 @@ __global__ __launch_bounds__(256) void splitk_reduce_qkv_kernel(SplitKArgs a, Ge
 
 // The residual reduction with the following RMSNorm: one workgroup per row.  x += sum of the
 // partials (times the gate if any), then h = x / sqrt(mean(x^2) + eps) * gain as bf16 (the same
-// formula as the RMSNorm kernel).  Rows up to 4096 wide (4 float4 per thread).
-__global__ __launch_bounds__(256) void splitk_reduce_resid_norm_kernel(SplitKArgs a, GemmArgs g, SplitKFuse f) {
-  __shared__ float wsum[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
+// formula as the RMSNorm kernel).  Rows up to 4096 wide: one 4-column group per thread
+// (blockDim = N / 4 rounded up to a wavefront), the row's x and gate loads issued before the sums.
+__global__ __launch_bounds__(1024) void splitk_reduce_resid_norm_kernel(SplitKArgs a, GemmArgs g, SplitKFuse f) {
+  __shared__ float wsum[16];
+  const int m = blockIdx.x, c = threadIdx.x;
   const int nq = a.N >> 2;
+  const bool on = c < nq;
   const int64_t plane = (int64_t)a.M * a.Nv;
   const int row = a.c_rows[m];
   const int b = row / g.out.rows_per_batch;
-  float* x = (float*)g.C + (int64_t)row * g.out.ld;
-  const float* gate = g.vec ? g.vec + b * g.vec_bstride : nullptr;
-  float4 xv[4];
+  float* x = (float*)g.C + (int64_t)row * g.out.ld + 4 * c;
+  const float* gate = g.vec ? g.vec + b * g.vec_bstride + 4 * c : nullptr;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f), gv = make_float4(1.f, 1.f, 1.f, 1.f);
   float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    if (c < nq) {
-      const float* p = a.part + (int64_t)m * a.Nv + 4 * c;
-      float4 s4 = *(const float4*)p;
-      for (int k = 1; k < a.splits; ++k) {
-        const float4 v = *(const float4*)(p + k * plane);
-        s4.x += v.x; s4.y += v.y; s4.z += v.z; s4.w += v.w;
-      }
-      float4 v = *(float4*)(x + 4 * c);
-      if (gate) {
-        v.x += gate[4 * c] * s4.x; v.y += gate[4 * c + 1] * s4.y; v.z += gate[4 * c + 2] * s4.z; v.w += gate[4 * c + 3] * s4.w;
-      } else {
-        v.x += s4.x; v.y += s4.y; v.z += s4.z; v.w += s4.w;
-      }
-      *(float4*)(x + 4 * c) = v;
-      xv[i] = v;
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (on) {
+    v = *(const float4*)x;
+    if (gate) gv = *(const float4*)gate;
+    float4 s4, unused;
+    sum_ranges(a.part + (int64_t)m * a.Nv + 4 * c, nullptr, plane, a.splits, s4, unused);
+    if (gate) {
+      v.x += gv.x * s4.x; v.y += gv.y * s4.y; v.z += gv.z * s4.z; v.w += gv.w * s4.w;
+    } else {
+      v.x += s4.x; v.y += s4.y; v.z += s4.z; v.w += s4.w;
     }
+    *(float4*)x = v;
+    ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  if ((c & 63) == 0) wsum[c >> 6] = ss;
   __syncthreads();
-  ss = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const int nw = blockDim.x >> 6;
+  ss = wsum[0];
+  for (int w = 1; w < nw; ++w) ss += wsum[w];
   const float rinv = 1.0f / sqrtf(ss / (float)a.N + f.eps);
-  bf16* h = (bf16*)f.h + (int64_t)row * a.N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    if (c < nq) {
-      const float4 gg = *(const float4*)(f.gain + 4 * c);
-      bf16x4 o;
-      o[0] = (bf16)(xv[i].x * rinv * gg.x); o[1] = (bf16)(xv[i].y * rinv * gg.y);
-      o[2] = (bf16)(xv[i].z * rinv * gg.z); o[3] = (bf16)(xv[i].w * rinv * gg.w);
-      *(bf16x4*)(h + 4 * c) = o;
-    }
+  if (on) {
+    const float4 gg = *(const float4*)(f.gain + 4 * c);
+    bf16x4 o;
+    o[0] = (bf16)(v.x * rinv * gg.x); o[1] = (bf16)(v.y * rinv * gg.y);
+    o[2] = (bf16)(v.z * rinv * gg.z); o[3] = (bf16)(v.w * rinv * gg.w);
+    *(bf16x4*)((bf16*)f.h + (int64_t)row * a.N + 4 * c) = o;
   }
 }
 
@@ -375,7 +382,8 @@ hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream
   }
   if (fuse && fuse->kind == SplitKFuse::RESID_NORM) {
     if (epi != EPI_RESID || !c_rows || g.N > 4096 || g.N % 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(splitk_reduce_resid_norm_kernel, dim3(g.M), dim3(256), 0, s, a, g, *fuse);
+    const unsigned threads = (unsigned)((g.N / 4 + 63) / 64 * 64);
+    hipLaunchKernelGGL(splitk_reduce_resid_norm_kernel, dim3(g.M), dim3(threads), 0, s, a, g, *fuse);
     return hipGetLastError();
   }
   const unsigned rb = (unsigned)(((int64_t)g.M * (g.N / 4) + 255) / 256);
