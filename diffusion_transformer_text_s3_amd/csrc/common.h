@@ -74,6 +74,12 @@ struct SplitKArgs {
   const int* a_rows;
   int a_phys_rows;
   const int* c_rows;
+  // SwiGLU over one K range with unmapped output rows: a workgroup's waves 0-3 take 64 W1
+  // columns and waves 4-7 the same 64 W3 columns, and the GEMM writes u (bf16, row m at
+  // u_out + m * u_ld) itself; no partials, no reduction launch
+  int swiglu_direct;
+  void* u_out;
+  int64_t u_ld;
 };
 SplitKArgs splitk_plan(int epi, int M, int N, int K);
 size_t splitk_workspace(int epi, int M, int N, int K);

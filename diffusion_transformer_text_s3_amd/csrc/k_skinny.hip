@@ -57,8 +57,10 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ct = blockIdx.x, split = blockIdx.y, m0 = blockIdx.z * KM;
-  const bool second = ct >= a.col_tiles;  // SwiGLU: the W3 half of the virtual columns
-  const int n0 = (second ? ct - a.col_tiles : ct) * KWG + wave * KNW;
+  const bool direct = a.swiglu_direct != 0;
+  // SwiGLU: the W3 half of the virtual columns (direct: of the workgroup's waves)
+  const bool second = direct ? wave >= 4 : ct >= a.col_tiles;
+  const int n0 = direct ? ct * (KWG / 2) + (wave & 3) * KNW : (second ? ct - a.col_tiles : ct) * KWG + wave * KNW;
   const int k0 = split * a.ks;
   const int kr = min(a.K, k0 + a.ks) - k0;  // K columns of this range
   const int nk = kr / KSL;                  // slabs (>= 1)
@@ -149,7 +151,34 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
   // the loads past the range are still landing
   __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(0));
 
-  // partial tile: lane holds rows 4 (lane / 16) + e of each 16 x 16 tile, column lane % 16
+  // lane holds rows 4 (lane / 16) + e of each 16 x 16 tile, column lane % 16
+  if (direct) {
+    // after this barrier every chunk read and every direct-to-LDS write has completed, so A0
+    // carries the W3 sums of waves 4-7 to waves 0-3 (same lane, same rows and columns)
+    float* w3s = (float*)A0;
+    __syncthreads();
+    if (wave >= 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w3s[((wave - 4) * 16 + i * 4 + e) * 64 + lane] = acc[i][e];
+    }
+    __syncthreads();
+    const int n = n0 + fr;
+    if (wave < 4 && n < a.N) {
+      bf16* u = (bf16*)a.u_out + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + 16 * i + 4 * fh + e;
+          const float w3 = w3s[(wave * 16 + i * 4 + e) * 64 + lane];
+          if (m < a.M) u[(int64_t)m * a.u_ld] = (bf16)(ssilu(acc[i][e]) * w3);
+        }
+    }
+    return;
+  }
+  // partial tile
   const int n = n0 + fr;
   if (n >= a.N) return;
   float* part = a.part + (int64_t)split * a.M * a.Nv + (second ? a.N : 0) + n;
@@ -372,8 +401,16 @@ hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream
   a.A = g.A; a.B = g.B; a.B2 = g.B2; a.part = part; a.lda = (int)g.lda; a.ldb = (int)g.ldb;
   a.a_rows = a_rows; a.a_phys_rows = a_phys_rows; a.c_rows = c_rows;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;
-  dim3 grid(vtiles, a.splits, (g.M + KM - 1) / KM);
+  const bool direct = epi == EPI_SWIGLU && a.splits == 1 && !c_rows && (!fuse || fuse->kind == SplitKFuse::NONE) &&
+                      g.out.rows_per_batch >= g.M && g.out.valid[0] >= g.M;
+  if (direct) {
+    a.swiglu_direct = 1;
+    a.u_out = g.C;
+    a.u_ld = g.out.ld;
+  }
+  dim3 grid(direct ? (g.N + KWG / 2 - 1) / (KWG / 2) : vtiles, a.splits, (g.M + KM - 1) / KM);
   hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(512), 0, s, a);
+  if (direct) return hipGetLastError();
   if (fuse && fuse->kind == SplitKFuse::QK_NORM_ROPE) {
     if (epi != EPI_STORE || !c_rows) return hipErrorInvalidValue;
     const int64_t lanes = (int64_t)g.M * (fuse->n_heads + 2 * fuse->n_kv_heads) * 16;

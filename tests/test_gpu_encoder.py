@@ -74,7 +74,7 @@ def test_gemm_splitk_resid_gate(M, N, K):
         assert np.all(np.abs(host(C) - ref) <= _sk_tol(K) * bound + 1e-6 * np.abs(C0) + 1e-6)
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 9728, 2560), (33, 136, 128)])
+@pytest.mark.parametrize("M,N,K", [(128, 9728, 2560), (33, 136, 128), (70, 200, 256), (33, 136, 2560)])
 def test_gemm_splitk_swiglu(M, N, K):
     note(f"gemm split-K SWIGLU M={M} N={N} K={K}")
     A, B, B2 = _sk_inputs(M, N, K, 63)
