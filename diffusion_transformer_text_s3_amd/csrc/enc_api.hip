@@ -271,7 +271,7 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
 }
 
 size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K) {
-  if (M < 1 || M > kSplitKMaxRows || N < 8 || K < 64) return 0;
+  if (M < 1 || M > kSplitKMaxRows || N < 8 || N % 8 || K < 64 || K % 64 || (int64_t)N * K * 2 > INT32_MAX) return 0;
   if (epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU) return 0;
   return splitk_workspace(epilogue, M, N, K) + 256;
 }

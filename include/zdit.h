@@ -384,8 +384,10 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
  * ZDIT_EPI_RESID (C fp32 += vec[n] * (A B^T), vec NULL: gate 1) and ZDIT_EPI_SWIGLU (C bf16
  * = SiLU(A B^T) * (A B2^T)).  K is cut into ranges by N and K alone, each range's fp32
  * partial product goes to the workspace, and the partials are summed in range order, so a
- * row's result does not depend on M.  M 1..256, N % 8 == 0, K % 64 == 0 (else
- * ZDIT_EUNSUPPORTED); ws: zdit_op_gemm_splitk_workspace() bytes. */
+ * row's result does not depend on M (SwiGLU over a single range applies SiLU and the product
+ * in the GEMM itself, with the same arithmetic).  M 1..256, N % 8 == 0, K % 64 == 0 (else
+ * ZDIT_EUNSUPPORTED); ws: zdit_op_gemm_splitk_workspace() bytes, which is 0 for a shape or
+ * epilogue the GEMM rejects. */
 size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K);
 zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
                                 const void* B, const void* B2, const float* vec, void* C,

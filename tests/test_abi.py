@@ -257,3 +257,18 @@ def test_encoder_ops_reject_bad_arguments_before_launch():
                                  C.c_void_p(4096), C.c_void_p(4096), C.c_void_p(4096), 1e-6, None) == Z.ZDIT_EINVAL
     assert L.zdit_rope_tables(4, Z.i32_array([128, 0, 0]), 1e6, 1, 8, 0, 0, Z.i32_array([8]),
                               C.c_void_p(4096), C.c_void_p(8192), None) == Z.ZDIT_EINVAL
+
+
+def test_splitk_workspace_depends_on_rows_only_through_m():
+    """The split-K GEMM cuts K into ranges chosen from N and K alone, so its partial-sum workspace
+    is (ranges x M x row width x 4 bytes) + 256 for every M: a row's summation order cannot
+    depend on how many rows are present.  The encoder's down projection (N 2560, K 9728) runs
+    10 ranges of 1024 columns; the gate/up projection (SwiGLU, row width 2N) one range."""
+    for epi, N, K, ranges, width in [(Z.ZDIT_EPI_RESID, 2560, 9728, 10, 2560),
+                                     (Z.ZDIT_EPI_SWIGLU, 9728, 2560, 1, 2 * 9728),
+                                     (Z.ZDIT_EPI_STORE, 6144, 2560, 5, 6144)]:
+        for M in (1, 55, 64, 65, 128, 256):
+            assert Z.zdit_op_gemm_splitk_workspace(epi, M, N, K) == ranges * M * width * 4 + 256, (epi, M)
+    assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_STORE, 257, 2560, 9728) == 0
+    assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_STORE, 64, 2560, 9700) == 0
+    assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_BIAS, 64, 2560, 9728) == 0
