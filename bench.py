@@ -380,8 +380,8 @@ def main():
                          "three times, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not part "
-              "of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
+              "path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
