@@ -194,10 +194,10 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
 // One thread per 4 consecutive output columns of a row: the partials summed in split order,
 // then the epilogue.
 // Sums of the float4 at p0 + k * plane (and at p1 + k * plane) over the ranges k, in order;
-// the loads of up to 8 ranges are issued before their adds.
+// the loads of up to 16 ranges are issued before their adds.
 __device__ __forceinline__ void sum_ranges(const float* p0, const float* p1, int64_t plane, int splits, float4& s0,
                                            float4& s1) {
-  constexpr int KB = 8;
+  constexpr int KB = 16;
   s0 = s1 = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k0 = 0; k0 < splits; k0 += KB) {
     float4 t0[KB], t1[KB];
