@@ -37,6 +37,12 @@ MUTATIONS = {
     "unscale inverted": ("/ F32(0.3611) + F32(0.1159)", "* F32(0.3611) + F32(0.1159)"),
     "caption position ids from 0": ("cap[j] = (1 + j, 0, 0)", "cap[j] = (j, 0, 0)"),
     "n_cap rounds down": ("return multiple * math.ceil(L / multiple)", "return multiple * max(1, L // multiple)"),
+    "SiLU dropped in the timestep MLP": ('hdn = silu(linear(e, ew["t_w1"], ew["t_b1"]))', 'hdn = linear(e, ew["t_w1"], ew["t_b1"])'),
+    "timestep MLP linears swapped": ('hdn = silu(linear(e, ew["t_w1"], ew["t_b1"]))\n    return linear(hdn, ew["t_w2"], ew["t_b2"])',
+                                     'hdn = silu(linear(e, ew["t_w2"], ew["t_b1"]))\n    return linear(hdn, ew["t_w1"], ew["t_b2"])'),
+    "adaLN chunks reordered (shift/scale)": ("    return m.reshape(6, -1)\n", "    return m.reshape(6, -1)[[1, 0, 2, 4, 3, 5]]\n"),
+    "adaLN chunks interleaved": ("    return m.reshape(6, -1)\n", "    return m.reshape(-1, 6).T\n"),
+    "RoPE frequency theta^(-k/d)": ("omega = theta ** (-2.0 * k / da)", "omega = theta ** (-1.0 * k / da)"),
 }
 
 

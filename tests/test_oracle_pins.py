@@ -139,6 +139,21 @@ def test_rope_axes_own_their_dims():
         assert abs(y[lo] - (math.cos(7) - math.sin(7))) < 1e-6
 
 
+def test_rope_frequencies_of_every_axis_hand_worked():
+    """Frequencies of pairs k = 0..3 (and the last pair) of each axis against the hand-reduced
+    powers of ten in tests/golden/rope_frequencies.txt: 10000^(-2k/32) = 10^(-k/4) on axis 0,
+    10000^(-2k/48) = 10^(-k/6) on axes 1 and 2, at a position whose three coordinates differ."""
+    pos = np.array([[5, 7, 11]])
+    cos, sin = O.rope_tables(pos)
+    assert cos.shape == (1, 64)
+    for col, axis, k, num, den in golden("rope_frequencies.txt"):
+        col, axis, num, den = int(col), int(axis), int(num), int(den)
+        ang = float(pos[0, axis]) * 10.0 ** (-num / den)
+        for got, want in ((cos[0, col], math.cos(ang)), (sin[0, col], math.sin(ang))):
+            # the tables are fp32: within one fp32 ulp of the exact value
+            assert abs(float(got) - want) <= np.spacing(np.float32(abs(want))), (col, axis, k)
+
+
 def test_rope_zero_position_is_identity():
     x = _rand_qk(5, 2, 128, 6)
     c, s = O.rope_tables(np.zeros((5, 3), dtype=np.int64))
@@ -201,6 +216,30 @@ def test_timestep_embedding_closed_forms():
     assert abs(e[0, 127] - math.cos(500 * f)) < 1e-12
 
 
+def test_t_condition_closed_form_mlp():
+    """Timestep MLP with coordinate weights: W1 = a I, W2 = g P for a non-symmetric permutation
+    P (row j reads column pi(j)), so c_j = g SiLU(a e_pi(j) + b1_pi(j)) + b2_j on the already
+    pinned sinusoid e.  Pins the SiLU between the two linears, which linear comes first, W2's
+    orientation and both biases."""
+    dims = synth.TINY
+    n = dims.c_dim
+    assert dims.t_freq == n
+    g = np.random.default_rng(60)
+    a, gm = 1.7, -0.6
+    pi = np.roll(np.arange(n), 5)  # pi(j) = j - 5 mod n
+    P = np.zeros((n, n))
+    P[np.arange(n), pi] = 1.0
+    ew = {"t_w1": a * np.eye(n), "t_b1": g.standard_normal(n), "t_w2": gm * P, "t_b2": g.standard_normal(n)}
+    t = np.array([0.3, 0.85])
+    c = O.t_condition(t, ew, dims, dtype=np.float64)
+    e = O.timestep_embedding(t, dims.t_freq, dims.t_scale, dtype=np.float64)
+    for b in range(2):
+        for j in range(n):
+            z = a * e[b, pi[j]] + ew["t_b1"][pi[j]]
+            want = gm * (z / (1.0 + math.exp(-z))) + ew["t_b2"][j]
+            assert abs(c[b, j] - want) < 1e-12 * (1 + abs(want)), (b, j)
+
+
 # ---------------------------------------------------------------- block-level invariants
 def _tiny_block(seed=11, S=40):
     dims = synth.TINY
@@ -228,6 +267,37 @@ def test_block_shift_scale_zero_gate_one_equals_context_refiner_block():
     mod[2] = 1
     mod[5] = 1
     np.testing.assert_array_equal(O.block(x, w, mod, cos, sin, dims), O.block(x, w, None, cos, sin, dims))
+
+
+def test_block_mod_chunk_order():
+    """W_ada = 0 makes the modulation the bias b_ada, read as six chunks (shift1, scale1, gate1,
+    shift2, scale2, gate2).  One chunk at a time: only the gates move x (chunk 2 through the
+    attention branch, chunk 5 through the FFN); a scale chunk of -1 with a zero shift zeroes its
+    branch's normed input (so its update vanishes) while a shift chunk of -1 does not."""
+    dims, w, x, cos, sin, c, _ = _tiny_block(S=24)
+    d = dims.dim
+    w = dict(w, w_ada=np.zeros_like(w["w_ada"]))
+
+    def update(chunks, **wover):
+        b = np.zeros(6 * d, dtype=F32)
+        for i, v in chunks.items():
+            b[i * d:(i + 1) * d] = v
+        ww = dict(w, b_ada=b, **wover)
+        return O.block(x, ww, O.block_mod(c, ww), cos, sin, dims) - x
+
+    for i in (0, 1, 3, 4):  # shift / scale alone, both gates 0
+        assert np.all(update({i: 0.5}) == 0), i
+    # chunk 2 gates the attention branch: dead with W_out = 0, alive otherwise
+    assert np.abs(update({2: 1.0})).max() > 1e-3
+    assert np.all(update({2: 1.0}, w_out=np.zeros_like(w["w_out"])) == 0)
+    # chunk 5 gates the FFN: dead with W3 = 0, alive otherwise
+    assert np.abs(update({5: 1.0})).max() > 1e-3
+    assert np.all(update({5: 1.0}, w3=np.zeros_like(w["w3"])) == 0)
+    # scale chunks: -1 zeroes the modulated input (h = 0 -> q = k = v = 0, u = 0)
+    assert np.all(update({2: 1.0, 1: -1.0}) == 0)
+    assert np.abs(update({2: 1.0, 0: -1.0})).max() > 1e-3
+    assert np.all(update({5: 1.0, 4: -1.0}) == 0)
+    assert np.abs(update({5: 1.0, 3: -1.0})).max() > 1e-3
 
 
 def test_block_w3_zero_kills_ffn():
