@@ -13,7 +13,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libzdit.so")
 
-ZDIT_OK, ZDIT_EINVAL, ZDIT_EUNSUPPORTED, ZDIT_EWORKSPACE, ZDIT_EHIP = 0, -1, -2, -3, -4
+ZDIT_OK, ZDIT_EINVAL, ZDIT_EUNSUPPORTED, ZDIT_EWORKSPACE, ZDIT_EHIP, ZDIT_ENONFINITE = 0, -1, -2, -3, -4, -5
+ZDIT_CHECK_FINITE = 1
 ZDIT_BF16, ZDIT_FP32_DEBUG = 0, 1
 ZDIT_SEQ_IMAGE, ZDIT_SEQ_CAPTION, ZDIT_SEQ_JOINT, ZDIT_SEQ_TEXT = 0, 1, 2, 3
 ZDIT_EPI_STORE, ZDIT_EPI_BIAS, ZDIT_EPI_RESID, ZDIT_EPI_SWIGLU = 0, 1, 2, 3
@@ -36,7 +37,7 @@ EXPORTS = [
 class zdit_dims(C.Structure):
     _fields_ = [("dim", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn_hidden", C.c_int32), ("rope_axes", C.c_int32 * 3), ("c_dim", C.c_int32),
-                ("precision", C.c_int32), ("norm_eps", C.c_float)]
+                ("precision", C.c_int32), ("norm_eps", C.c_float), ("flags", C.c_int32)]
 
 
 class zdit_block_w(C.Structure):
@@ -177,19 +178,19 @@ def stream_handle(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-def make_dims(d, precision=ZDIT_BF16) -> zdit_dims:
+def make_dims(d, precision=ZDIT_BF16, flags=0) -> zdit_dims:
     """zdit_dims from any object with dim / n_heads / head_dim / ffn_hidden / rope_axes /
-    c_dim / norm_eps attributes."""
+    c_dim / norm_eps attributes; flags 0 or ZDIT_CHECK_FINITE."""
     out = zdit_dims()
     out.dim, out.n_heads, out.head_dim, out.ffn_hidden = d.dim, d.n_heads, d.head_dim, d.ffn_hidden
     out.rope_axes[:] = list(d.rope_axes)
-    out.c_dim, out.precision, out.norm_eps = d.c_dim, precision, d.norm_eps
+    out.c_dim, out.precision, out.norm_eps, out.flags = d.c_dim, precision, d.norm_eps, flags
     return out
 
 
-def make_cfg(d, precision=ZDIT_BF16) -> zdit_model_cfg:
+def make_cfg(d, precision=ZDIT_BF16, flags=0) -> zdit_model_cfg:
     c = zdit_model_cfg()
-    c.d = make_dims(d, precision)
+    c.d = make_dims(d, precision, flags)
     c.n_noise_ref, c.n_ctx_ref, c.n_main = d.n_noise_ref, d.n_ctx_ref, d.n_main
     c.latent_ch, c.patch, c.cap_dim, c.t_freq = d.latent_ch, d.patch, d.cap_dim, d.t_freq
     c.seq_multiple, c.max_cap_len = d.seq_multiple, d.max_cap_len

@@ -191,6 +191,23 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 // the i-th pair (b, r < len[b]).
 hipError_t launch_valid_rows(int batch, int s_max, const int* len, int* rows, hipStream_t s);
 
+// Opt-in non-finite detection: flag = 1 when any value of the valid rows (r < valid[b]) of a
+// branch-strided fp32 buffer is NaN or +-Inf.  Row r of branch b: p + b * bstride + r * ld,
+// `width` values (a multiple of 4, 16-byte aligned rows).
+struct FiniteArgs {
+  const float* p;
+  int64_t bstride, ld;
+  int rows_per_batch, batch, width;
+  int valid[kMaxBatch];
+  int* flag;
+};
+hipError_t launch_finite_check(const FiniteArgs& a, hipStream_t s);
+// When first[0] < 0 and one of flags[0..n) is set: first = {step, index of the first set flag}.
+// Then every flag is cleared.  One thread, in stream order.
+hipError_t launch_finite_latch(int* flags, int n, int step, int* first, hipStream_t s);
+// p[0..n) = v
+hipError_t launch_fill_i32(int* p, int n, int v, hipStream_t s);
+
 // zero `bytes` (a multiple of 16) at 16-byte aligned p
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
   const __amdgpu_buffer_rsrc_t brs =
       __builtin_amdgcn_make_buffer_rsrc((void*)bb, 0, max(0, a.N - n0) * a.ldb * 2, kSBufFlags);
   const unsigned bvo = (unsigned)(fr * a.ldb * 2 + fh * 16 + k0 * 2);
-  // slabs past the range reload the last one (branch-free); their weights are zeroed below
+  // slabs past the range reload the last one (branch-free); no MFMA uses them
   auto ldb = [&](int t) {
     return __builtin_amdgcn_raw_buffer_load_b128(brs, (int)(bvo + (unsigned)min(t, nk - 1) * (KSL * 2)), 0, 0);
   };
@@ -94,24 +94,28 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
     const unsigned row = m < a.M ? (unsigned)(gather ? a.a_rows[m] : r) * (unsigned)(a.lda * 2) : 0x80000000u;
     avo[j] = row + (unsigned)(c * 16);
   }
+  // The chunk's K offset goes into the per-lane offset, which the hardware checks against the
+  // resource: in the last range's last chunk, columns past K of the last row lie past the end of
+  // A and load as zero instead of reading whatever follows A (the scalar offset is not checked).
+  // An invalid row's 2^31 base plus the offset (< 2^31) stays out of range.
   auto dma_a = [&](int ch, uint4* buf) {
-    const int soff = (k0 + min(ch, nch - 1) * KCH) * 2;
+    const unsigned coff = (unsigned)(k0 + min(ch, nch - 1) * KCH) * 2u;
 #pragma unroll
-    for (int j = 0; j < KCH_DMA; ++j) sdma_16(ars, buf + (KCH_DMA * wave + j) * 64, (int)avo[j], soff);
+    for (int j = 0; j < KCH_DMA; ++j) sdma_16(ars, buf + (KCH_DMA * wave + j) * 64, (int)(avo[j] + coff), 0);
   };
 
   u32x4 bq[KU_B];
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
   // One chunk of A in buffer CUR (every wave's loads landed), the next one's loads go to NXT
   // (every wave finished reading it before the barrier that ended the previous chunk).  Its 8
   // slabs: the weights of slab T from bq, the A fragments from CUR, four MFMAs, then the weight
-  // load of slab T + KU_B.  At the end: this wave's chunk loads (issued before the chunk's 8
-  // weight loads) are complete, then the barrier.  A macro, so that each LDS access names its
-  // own buffer object.
+  // load of slab T + KU_B.  Slabs past the range (in its last chunk) issue no MFMA, so the A
+  // columns there never enter a sum.  At the end: this wave's chunk loads (issued before the
+  // chunk's 8 weight loads) are complete, then the barrier.  A macro, so that each LDS access
+  // names its own buffer object.
 #define ZDIT_SK_CHUNK(CH, CUR, NXT)                                                                    \
   {                                                                                                   \
     const int ch_ = (CH);                                                                             \
@@ -119,12 +123,13 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
     _Pragma("unroll") for (int s = 0; s < KCH_SL; ++s) {                                              \
       const int tt = ch_ * KCH_SL + s;                                                                \
       const int q = (ch_ & 1) * KCH_SL + s; /* ring slot: chunks alternate halves of bq */           \
-      const u32x4 bv = tt < nk ? bq[q] : zero4;                                                       \
-      const bf16x8 bf = __builtin_bit_cast(bf16x8, bv);                                               \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
-        const int r = 16 * i + fr;                                                                    \
-        const bf16x8 af = __builtin_bit_cast(bf16x8, CUR[aslot(r, s * 4 + fh)]);                      \
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i], 0, 0, 0);                    \
+      if (tt < nk) {                                                                                  \
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, bq[q]);                                          \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                               \
+          const int r = 16 * i + fr;                                                                  \
+          const bf16x8 af = __builtin_bit_cast(bf16x8, CUR[aslot(r, s * 4 + fh)]);                    \
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i], 0, 0, 0);                  \
+        }                                                                                             \
       }                                                                                               \
       bq[q] = ldb(tt + KU_B);                                                                         \
     }                                                                                                 \

@@ -38,19 +38,81 @@ zdit_status check_dims(const zdit_dims* d) {
   if (d->c_dim < 64 || d->c_dim % 64 != 0 || d->c_dim > 1024)
     return fail(ZDIT_EUNSUPPORTED, "c_dim %d (multiple of 64, <= 1024)", d->c_dim);
   if (!(d->norm_eps >= 0.f) || !isfinite(d->norm_eps)) return fail(ZDIT_EINVAL, "norm_eps must be finite and >= 0");
+  if (d->flags & ~ZDIT_CHECK_FINITE) return fail(ZDIT_EINVAL, "unknown flag bits 0x%x", (unsigned)d->flags);
+  return ZDIT_OK;
+}
+
+// ------------------------------------------------------------------ non-finite checks
+// ZDIT_CHECK_FINITE: checkpoints of one call raise flags[k]; after each step the latch keeps the
+// first (step, checkpoint) whose flag is set in first[0..1].  The region holds n flags + 2.
+struct Check {
+  int* flags = nullptr;  // nullptr: checking off
+  int* first = nullptr;
+  int n = 0;
+};
+
+size_t check_bytes(int n) { return al256((size_t)(n + 2) * 4); }
+
+Check check_at(const zdit_dims& d, char* region, int n) {
+  Check c;
+  if (d.flags & ZDIT_CHECK_FINITE) {
+    c.flags = (int*)region;
+    c.first = c.flags + n;
+    c.n = n;
+  }
+  return c;
+}
+
+// flags = 0, first = {-1, -1}
+hipError_t check_begin(const Check& c, hipStream_t st) {
+  if (!c.flags) return hipSuccess;
+  if (hipError_t e = launch_fill_i32(c.flags, c.n, 0, st)) return e;
+  return launch_fill_i32(c.first, 2, -1, st);
+}
+
+// flags[k] |= any non-finite value in the valid rows of a branch-strided fp32 buffer
+hipError_t check_rows(const Check& c, int k, const float* p, int64_t bstride, int64_t ld, int rows_per_batch,
+                      int batch, int width, const int* valid, hipStream_t st) {
+  if (!c.flags) return hipSuccess;
+  FiniteArgs a;
+  a.p = p; a.bstride = bstride; a.ld = ld; a.rows_per_batch = rows_per_batch; a.batch = batch; a.width = width;
+  for (int b = 0; b < kMaxBatch; ++b) a.valid[b] = b < batch ? (valid ? valid[b] : rows_per_batch) : 0;
+  a.flag = c.flags + k;
+  return launch_finite_check(a, st);
+}
+
+hipError_t check_latch(const Check& c, int step, hipStream_t st) {
+  if (!c.flags) return hipSuccess;
+  return launch_finite_latch(c.flags, c.n, step, c.first, st);
+}
+
+// Reads the verdict back (synchronising the stream); *step / *where = -1 when every value was
+// finite.
+zdit_status check_read(const Check& c, hipStream_t st, int* step, int* where) {
+  int h[2] = {-1, -1};
+  if (c.flags) {
+    HIP_TRY(hipMemcpyAsync(h, c.first, sizeof h, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+  }
+  *step = h[0];
+  *where = h[1];
   return ZDIT_OK;
 }
 
 // ------------------------------------------------------------------ block workspace plan
 struct BlockPlan {
-  size_t mod, h, qkv, vt, o, u, total;
+  size_t mod, chk, h, qkv, vt, o, u, total;
 };
+
+// checkpoints of zdit_block_fwd: the input rows, the output rows
+constexpr int kBlockChecks = 2;
 
 BlockPlan plan_block(const zdit_dims& d, int B, int s) {
   const size_t M = (size_t)B * s, ab = act_bytes(d.precision);
   BlockPlan p;
   size_t off = 0;
   p.mod = off; off += al256((size_t)B * 6 * d.dim * 4);
+  p.chk = off; off += check_bytes(kBlockChecks);
   p.h = off;   off += al256(M * d.dim * ab);
   const size_t r0 = off;
   p.qkv = off; off += al256(M * 3 * d.dim * ab);
@@ -170,10 +232,29 @@ zdit_status check_block_w(const zdit_block_w* w, bool need_ada) {
 struct StackPlan {
   int nimg, gh, gw, max_nc, s_max;
   int nc[kMaxBatch], S[kMaxBatch];
-  size_t x, c, mod, fmod, tab_img_c, tab_img_s, tab_cap_c, tab_cap_s, tab_j_c, tab_j_s, tok,
+  size_t x, c, mod, fmod, chk, tab_img_c, tab_img_s, tab_cap_c, tab_cap_s, tab_j_c, tab_j_s, tok,
       capa, ftok, blk, total;
   BlockPlan bp;
 };
+
+// Checkpoints of a stack forward: 0 the latents, 1 the caption features, then the residual
+// stream after each noise refiner, context refiner and main block, then the velocity.
+int stack_checks(const zdit_model_cfg& cfg) { return 3 + cfg.n_noise_ref + cfg.n_ctx_ref + cfg.n_main; }
+
+// The place a stack checkpoint names, for zdit_last_error().
+std::string stack_check_name(const zdit_model_cfg& cfg, int k) {
+  char buf[96];
+  const int nr = cfg.n_noise_ref, cr = cfg.n_ctx_ref, nm = cfg.n_main;
+  if (k == 0) return "the input latents";
+  if (k == 1) return "the caption features (valid rows)";
+  k -= 2;
+  if (k < nr) { snprintf(buf, sizeof buf, "the image rows after noise refiner %d", k); return buf; }
+  k -= nr;
+  if (k < cr) { snprintf(buf, sizeof buf, "the caption rows after context refiner %d", k); return buf; }
+  k -= cr;
+  if (k < nm) { snprintf(buf, sizeof buf, "the residual stream after main block %d", k); return buf; }
+  return "the velocity";
+}
 
 // The adaLN modulations of the n blocks of a stage (the same c for all), in launches of up to
 // kMaxAdaJobs blocks: block i's six vectors at mod + i * batch * 6 * dim.
@@ -215,6 +296,8 @@ StackPlan plan_stack(const zdit_model_cfg& cfg, int B, int lat_h, int lat_w, int
   p.s_max = p.nimg + p.max_nc;
   const int F = cfg.patch * cfg.patch * cfg.latent_ch;
   size_t off = 0;
+  // first, so that its offset does not depend on the caption lengths
+  p.chk = off; off += check_bytes(stack_checks(cfg));
   p.x = off; off += al256((size_t)B * p.s_max * D * 4);
   p.c = off; off += al256((size_t)B * d.c_dim * 4);
   // one modulation set per adaLN block of a stage (noise refiners, or main blocks), computed by one launch
@@ -302,10 +385,13 @@ struct CapCache {
   float* out = nullptr;
 };
 
+// chk / step: the ZDIT_CHECK_FINITE checkpoints (off when chk.flags is NULL) and the sampler
+// step they are latched under.
 zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int B, int lat_h, int lat_w,
                           const float* latents, int64_t lat_bstride, const float* cap_feats,
                           int max_cap_len, const int* cap_len, const float* t, float* velocity,
-                          char* ws, hipStream_t st, CapCache cache = CapCache{}) {
+                          char* ws, hipStream_t st, CapCache cache = CapCache{}, Check chk = Check{},
+                          int step = 0) {
   const zdit_dims& d = cfg.d;
   const int P = d.precision, D = d.dim, F = cfg.patch * cfg.patch * cfg.latent_ch;
   const StackPlan p = plan_stack(cfg, B, lat_h, lat_w, max_cap_len, cap_len);
@@ -315,6 +401,13 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   float* fmod = (float*)(ws + p.fmod);
   char* bws = ws + p.blk;
   const int64_t xb = (int64_t)p.s_max * D;
+
+  const int64_t lat_n = (int64_t)cfg.latent_ch * lat_h * lat_w;
+  const int nr = cfg.n_noise_ref, cr = cfg.n_ctx_ref;
+  HIP_TRY(check_rows(chk, 0, latents, lat_bstride, lat_n, 1, lat_bstride == 0 ? 1 : B, (int)lat_n, nullptr, st));
+  if (!cache.in)
+    HIP_TRY(check_rows(chk, 1, cap_feats, (int64_t)max_cap_len * cfg.cap_dim, cfg.cap_dim, max_cap_len, B,
+                       cfg.cap_dim, cap_len, st));
 
   // conditioning
   HIP_TRY(launch_temb(B, t, cfg.t_freq, d.c_dim, cfg.t_scale, w.t_w1, w.t_b1, w.t_w2, w.t_b2, c, st));
@@ -357,6 +450,7 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
     const zdit_block_w& bw = w.noise_ref[i];
     float* mod_i = mod + (size_t)i * Bi * 6 * D;
     if (zdit_status s = block_forward(d, bw, Bi, p.nimg, len, x, xb, mod_i, ti_c, ti_s, 0, bws, st)) return s;
+    HIP_TRY(check_rows(chk, 2 + i, x, xb, D, p.nimg, Bi, D, nullptr, st));
   }
   if (same_img)
     HIP_TRY(launch_copy_rows(x, 0, x + xb, xb, B - 1, (int64_t)p.nimg * D, st));
@@ -380,6 +474,7 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
     for (int i = 0; i < cfg.n_ctx_ref; ++i) {
       if (zdit_status s = block_forward(d, w.ctx_ref[i], B, p.max_nc, len, xcap, xb, nullptr, tc_c, tc_s, 0, bws, st))
         return s;
+      HIP_TRY(check_rows(chk, 2 + nr + i, xcap, xb, D, p.max_nc, B, D, p.nc, st));
     }
     if (cache.out) HIP_TRY(launch_copy_rows(xcap, xb, cache.out, cache_bstride, B, cache_bstride, st));
   }
@@ -391,6 +486,7 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
     const zdit_block_w& bw = w.main[i];
     float* mod_i = mod + (size_t)i * B * 6 * D;
     if (zdit_status s = block_forward(d, bw, B, p.s_max, len, x, xb, mod_i, tj_c, tj_s, 0, bws, st)) return s;
+    HIP_TRY(check_rows(chk, 2 + nr + cr + i, x, xb, D, p.s_max, B, D, p.S, st));
   }
   // final layer on the image rows
   HIP_TRY(launch_adaln(P, B, d.c_dim, 2 * D, c, w.final_ada_w, w.final_ada_b, fmod, st));
@@ -406,6 +502,8 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   g.out = compact_rows(B * p.nimg, F);
   HIP_TRY(gemm(P, EPI_BIAS, g, st));
   HIP_TRY(launch_unpatchify(B, cfg.latent_ch, lat_h, lat_w, (const float*)(ws + p.ftok), velocity, st));
+  HIP_TRY(check_rows(chk, 2 + nr + cr + cfg.n_main, velocity, lat_n, lat_n, 1, B, (int)lat_n, nullptr, st));
+  HIP_TRY(check_latch(chk, step, st));
   return ZDIT_OK;
 }
 
@@ -445,14 +543,24 @@ zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t
   const BlockPlan pl = plan_block(*dims, batch, s_max);
   if (ws_bytes < pl.total) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.total);
   hipStream_t st = (hipStream_t)hip_stream;
+  const int D = dims->dim;
+  const Check chk = check_at(*dims, (char*)ws + pl.chk, kBlockChecks);
+  HIP_TRY(check_begin(chk, st));
+  HIP_TRY(check_rows(chk, 0, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
   float* mod = nullptr;
   if (w->w_ada) {
     mod = (float*)((char*)ws + pl.mod);
-    HIP_TRY(launch_adaln(dims->precision, batch, dims->c_dim, 6 * dims->dim, c, w->w_ada, w->b_ada, mod, st));
+    HIP_TRY(launch_adaln(dims->precision, batch, dims->c_dim, 6 * D, c, w->w_ada, w->b_ada, mod, st));
   }
-  if (zdit_status s = block_forward(*dims, *w, batch, s_max, seq_len, x, (int64_t)s_max * dims->dim, mod,
+  if (zdit_status s = block_forward(*dims, *w, batch, s_max, seq_len, x, (int64_t)s_max * D, mod,
                                     rope_cos, rope_sin, (int64_t)s_max * (dims->head_dim / 2), (char*)ws, st))
     return s;
+  HIP_TRY(check_rows(chk, 1, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
+  HIP_TRY(check_latch(chk, 0, st));
+  int step, where;
+  if (zdit_status s = check_read(chk, st, &step, &where)) return s;
+  if (where == 0) return fail(ZDIT_ENONFINITE, "non-finite value in the valid rows of the input x");
+  if (where == 1) return fail(ZDIT_ENONFINITE, "non-finite value in the block output (residual stream)");
   return ok();
 }
 
@@ -470,11 +578,17 @@ zdit_status zdit_stack_fwd(const zdit_model_cfg* cfg, const zdit_model_w* w, int
     return s;
   if (latent_batch_stride < 0 || latent_batch_stride % 4) return fail(ZDIT_EINVAL, "latent_batch_stride %lld", (long long)latent_batch_stride);
   if (!ws || ((uintptr_t)ws & 255u)) return fail(ZDIT_EINVAL, "workspace NULL or not 256-byte aligned");
-  const size_t need = plan_stack(*cfg, batch, lat_h, lat_w, max_cap_len, nullptr).total;
-  if (ws_bytes < need) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const StackPlan pl = plan_stack(*cfg, batch, lat_h, lat_w, max_cap_len, nullptr);
+  if (ws_bytes < pl.total) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.total);
+  hipStream_t st = (hipStream_t)hip_stream;
+  const Check chk = check_at(cfg->d, (char*)ws + pl.chk, stack_checks(*cfg));
+  HIP_TRY(check_begin(chk, st));
   if (zdit_status s = stack_forward(*cfg, *w, batch, lat_h, lat_w, latents, latent_batch_stride, cap_feats,
-                                    max_cap_len, cap_len, t, velocity, (char*)ws, (hipStream_t)hip_stream))
+                                    max_cap_len, cap_len, t, velocity, (char*)ws, st, CapCache{}, chk, 0))
     return s;
+  int step, where;
+  if (zdit_status s = check_read(chk, st, &step, &where)) return s;
+  if (where >= 0) return fail(ZDIT_ENONFINITE, "non-finite value in %s", stack_check_name(*cfg, where).c_str());
   return ok();
 }
 
@@ -542,6 +656,10 @@ zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_
   char* sws = (char*)cap_cache + sample_cap_cache_bytes(cfg, nb, max_cap_len);
   std::vector<float> sg(num_steps + 1);
   for (int i = 0; i <= num_steps; ++i) sg[i] = (float)sigma_at(i, num_steps, (double)shift);
+  // the stack's own check region inside its workspace; checkpoints latched per step
+  const StackPlan spl = plan_stack(*cfg, nb, lat_h, lat_w, max_cap_len, nullptr);
+  const Check chk = check_at(cfg->d, sws + spl.chk, stack_checks(*cfg));
+  HIP_TRY(check_begin(chk, st));
   for (int i = 0; i < num_steps; ++i) {
     const float ti = 1.0f - sg[i];
     const float tv[2] = {ti, ti};
@@ -549,10 +667,14 @@ zdit_status zdit_sample(const zdit_model_cfg* cfg, const zdit_model_w* w, int32_
     CapCache cc;
     if (i == 0) cc.out = cap_cache; else cc.in = cap_cache;
     if (zdit_status s = stack_forward(*cfg, *w, nb, lat_h, lat_w, x, 0, cap_feats, max_cap_len, cap_len, tv, vel,
-                                      sws, st, cc)) return s;
+                                      sws, st, cc, chk, i)) return s;
     HIP_TRY(launch_euler(x, vel, nb == 2 ? vel + n : nullptr, n, guidance, sg[i], sg[i + 1],
                          i == num_steps - 1 ? decode_out : nullptr, st));
   }
+  int step, where;
+  if (zdit_status s = check_read(chk, st, &step, &where)) return s;
+  if (where >= 0)
+    return fail(ZDIT_ENONFINITE, "sampler step %d: non-finite value in %s", step, stack_check_name(*cfg, where).c_str());
   return ok();
 }
 
@@ -605,6 +727,8 @@ zdit_status zdit_op_rmsnorm_mod(int32_t precision, int32_t rows, int32_t dim, co
   if (precision != ZDIT_BF16 && precision != ZDIT_FP32_DEBUG) return fail(ZDIT_EINVAL, "precision %d", precision);
   if (rows < 0 || dim < 128 || dim % 128 || dim > 4096) return fail(ZDIT_EUNSUPPORTED, "rows %d dim %d", rows, dim);
   if (!x || !gain || !out || (!shift) != (!scale)) return fail(ZDIT_EINVAL, "NULL pointer argument");
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(out) || (shift && (!aligned16(shift) || !aligned16(scale))))
+    return fail(ZDIT_EINVAL, "pointer not 16-byte aligned");
   if (rows == 0) return ok();
   NormArgs na;
   na.x = x; na.x_bstride = 0; na.rows_per_batch = rows; na.batch = 1; na.dim = dim; na.gain = gain;
@@ -619,6 +743,7 @@ zdit_status zdit_op_rope(int32_t precision, int32_t batch, int32_t s_max, int32_
   if (precision != ZDIT_BF16 && precision != ZDIT_FP32_DEBUG) return fail(ZDIT_EINVAL, "precision %d", precision);
   if (batch < 1 || batch > ZDIT_MAX_BATCH || s_max < 1 || n_heads < 1) return fail(ZDIT_EINVAL, "batch/s_max/n_heads");
   if (!seq_len || !qkv || !cos || !sin) return fail(ZDIT_EINVAL, "NULL pointer argument");
+  if (!aligned16(qkv) || !aligned16(cos) || !aligned16(sin)) return fail(ZDIT_EINVAL, "pointer not 16-byte aligned");
   RopeArgs ra;
   ra.qkv = qkv; ra.cos = cos; ra.sin = sin; ra.tab_bstride = (int64_t)s_max * 64;
   ra.batch = batch; ra.s_max = s_max; ra.n_heads = n_heads;
@@ -714,6 +839,8 @@ zdit_status zdit_op_adaln(int32_t precision, int32_t batch, int32_t c_dim, int32
   if (batch < 1 || batch > ZDIT_MAX_BATCH || c_dim < 8 || c_dim % 8 || c_dim > 1024 || n_out < 1)
     return fail(ZDIT_EINVAL, "batch / c_dim / n_out");
   if (!c || !w || !b || !out) return fail(ZDIT_EINVAL, "NULL pointer argument");
+  if (!aligned16(c) || !aligned16(w) || !aligned16(b) || !aligned16(out))
+    return fail(ZDIT_EINVAL, "pointer not 16-byte aligned");
   HIP_TRY(launch_adaln(precision, batch, c_dim, n_out, c, w, b, out, (hipStream_t)hip_stream));
   return ok();
 }

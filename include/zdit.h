@@ -20,7 +20,8 @@
  *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
  *     Nothing synchronises; no host<->device copy is made, except that the text-encoder
  *     calls copy the host token ids into their workspace (the host array may be reused as
- *     soon as the call returns).
+ *     soon as the call returns), and that calls with ZDIT_CHECK_FINITE set read their
+ *     verdict back (see below).
  *   - Arguments are validated before anything is enqueued.  On error nothing runs, outputs
  *     are untouched, the return value is negative and zdit_last_error() says why.  Faults
  *     during execution surface at the caller's next synchronisation, as in any HIP library.
@@ -47,7 +48,8 @@ enum {
   ZDIT_EINVAL = -1,        /* bad argument (null/misaligned pointer, bad size, bad length) */
   ZDIT_EUNSUPPORTED = -2,  /* dimensions the kernels do not implement */
   ZDIT_EWORKSPACE = -3,    /* workspace smaller than the matching *_workspace() query */
-  ZDIT_EHIP = -4           /* a HIP launch failed */
+  ZDIT_EHIP = -4,          /* a HIP launch failed */
+  ZDIT_ENONFINITE = -5     /* ZDIT_CHECK_FINITE found a NaN or an infinity (see below) */
 };
 
 enum { ZDIT_BF16 = 0, ZDIT_FP32_DEBUG = 1 };
@@ -55,8 +57,18 @@ enum { ZDIT_BF16 = 0, ZDIT_FP32_DEBUG = 1 };
 /* Token-sequence layouts for RoPE tables (ZDIT_SEQ_TEXT: the text encoder's tokens). */
 enum { ZDIT_SEQ_IMAGE = 0, ZDIT_SEQ_CAPTION = 1, ZDIT_SEQ_JOINT = 2, ZDIT_SEQ_TEXT = 3 };
 
+/* zdit_dims.flags.  ZDIT_CHECK_FINITE (debug): zdit_block_fwd, zdit_stack_fwd and zdit_sample
+ * scan their inputs, the residual stream after every block and the velocity of every step for
+ * NaN and infinity, and return ZDIT_ENONFINITE naming the first place one appeared (sampler step,
+ * input or block) in zdit_last_error().  The activations of this model outgrow half precision,
+ * and an fp16 run of the DiT turns to NaN by the second sampler step ([CoreAI] "fp16 does not
+ * work. bf16 does.").  With the flag set these calls read the verdict back and synchronise the
+ * stream before returning (so they cannot be captured into a graph); the numeric results are
+ * the same as without it.  Unknown flag bits are ZDIT_EINVAL. */
+#define ZDIT_CHECK_FINITE 1
+
 #define ZDIT_MAX_BATCH 16
-#define ZDIT_ABI_VERSION 1
+#define ZDIT_ABI_VERSION 2
 
 /* Text of the last error on the calling thread; valid until the next zdit_* call on it. */
 const char* zdit_last_error(void);
@@ -64,13 +76,15 @@ int32_t zdit_abi_version(void);
 
 /* Block dimensions.  The kernels implement head_dim 128, rope axes summing to head_dim
  * (each even), dim = n_heads * head_dim with dim % 128 == 0, ffn_hidden % 128 == 0,
- * c_dim % 64 == 0 and c_dim <= 1024.  norm_eps is the RMSNorm epsilon. */
+ * c_dim % 64 == 0 and c_dim <= 1024.  norm_eps is the RMSNorm epsilon.  flags: 0 or
+ * ZDIT_CHECK_FINITE. */
 typedef struct {
   int32_t dim, n_heads, head_dim, ffn_hidden;
   int32_t rope_axes[3];
   int32_t c_dim;
   int32_t precision; /* ZDIT_BF16 or ZDIT_FP32_DEBUG */
   float norm_eps;
+  int32_t flags;
 } zdit_dims;
 
 /* One block's weights (device).  w_qkv [3*dim, dim]: rows 0..dim-1 produce q, dim..2dim-1

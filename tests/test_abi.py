@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     for name in declared:
         assert hasattr(L, name), name
     assert sorted(Z.EXPORTS) == declared
-    assert L.zdit_abi_version() == 1
+    assert L.zdit_abi_version() == 2
 
 
 def test_sigmas_match_oracle_bit_exact():
@@ -102,6 +102,48 @@ def test_block_fwd_rejects_bad_arguments_before_launch():
     d.head_dim = 64
     rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), p, p, p, p, p, 1 << 30, None)
     assert rc == Z.ZDIT_EUNSUPPORTED
+
+
+def test_dims_flags_layout_and_validation():
+    """zdit_dims ends with the flags word (ABI 2); ZDIT_CHECK_FINITE is accepted, any other bit
+    is rejected before anything runs, and the checked workspaces are no larger."""
+    assert C.sizeof(Z.zdit_dims) == 11 * 4 and Z.zdit_dims.flags.offset == 40
+    L = Z.lib()
+    d = Z.make_dims(synth.TINY)
+    plain = Z.zdit_block_workspace(d, 1, 96)
+    d.flags = Z.ZDIT_CHECK_FINITE
+    assert Z.zdit_block_workspace(d, 1, 96) == plain > 0
+    cfg_plain = Z.make_cfg(synth.TINY)
+    cfg_chk = Z.make_cfg(synth.TINY, flags=Z.ZDIT_CHECK_FINITE)
+    assert Z.zdit_stack_workspace(cfg_chk, 2, 16, 16, 45) == Z.zdit_stack_workspace(cfg_plain, 2, 16, 16, 45) > 0
+    assert Z.zdit_sample_workspace(cfg_chk, 16, 16, 45, 1.0) == Z.zdit_sample_workspace(cfg_plain, 16, 16, 45, 1.0)
+    for bad in (2, 4, 1 << 30, -1):
+        d.flags = bad
+        assert Z.zdit_block_workspace(d, 1, 96) == 0
+        w = Z.zdit_block_w()
+        for k in ("w_qkv", "w_out", "w1", "w3", "w2", "norm1", "norm2"):
+            setattr(w, k, 1 << 20)
+        p = _fake()
+        rc = L.zdit_block_fwd(C.byref(d), C.byref(w), 1, 96, Z.i32_array([96]), p, None, p, p, p, 1 << 30, None)
+        assert rc == Z.ZDIT_EINVAL and "flag" in Z.last_error()
+        cfg = Z.make_cfg(synth.TINY, flags=bad)
+        assert Z.zdit_stack_workspace(cfg, 2, 16, 16, 45) == 0
+        assert Z.zdit_sample_workspace(cfg, 16, 16, 45, 1.0) == 0
+
+
+def test_op_entry_points_reject_misaligned_pointers():
+    """The RMSNorm, RoPE and adaLN op entry points make 16-byte accesses: misaligned pointers
+    are rejected before launch."""
+    L = Z.lib()
+    p, q = _fake(), _fake((1 << 20) + 4)
+    rc = L.zdit_op_rmsnorm_mod(Z.ZDIT_BF16, 4, 256, q, p, None, None, 1e-6, p, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
+    rc = L.zdit_op_rmsnorm_mod(Z.ZDIT_BF16, 4, 256, p, p, q, p, 1e-6, p, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
+    rc = L.zdit_op_rope(Z.ZDIT_BF16, 1, 8, 1, Z.i32_array([8]), q, p, p, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
+    rc = L.zdit_op_adaln(Z.ZDIT_BF16, 1, 256, 64, p, q, p, p, None)
+    assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
 
 
 def test_fused_qkv_attn_validates_before_launch():

@@ -89,6 +89,36 @@ def test_gemm_splitk_swiglu(M, N, K):
     assert_bf16_result(host(C), u, 1.1 * e1 * np.abs(a3) + np.abs(silu(a1)) * e3 + 1e-6 * np.abs(u) + e1 * e3)
 
 
+@pytest.mark.parametrize("epi", [Z.ZDIT_EPI_STORE, Z.ZDIT_EPI_RESID])
+@pytest.mark.parametrize("K", [320, 384, 576])
+def test_gemm_splitk_partial_last_chunk_ignores_memory_after_a(epi, K):
+    """K not a multiple of 256: the last K range ends inside a 256-column A chunk.  A sits at the
+    start of a NaN-filled allocation, so the bytes after its last row are NaN; the result must
+    be finite and match the float64 reference (columns past K are neither read nor summed)."""
+    M, N = 70, 264
+    note(f"gemm split-K partial last chunk epi={epi} K={K}, NaN after A")
+    A, B, _ = _sk_inputs(M, N, K, 65)
+    buf = torch.full((M * K + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[:M * K] = dev(A, torch.bfloat16).reshape(-1)
+    Ad = buf[:M * K].view(M, K)
+    ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(epi, M, N, K))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bound = _sk_tol(K) * (np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T)
+    if epi == Z.ZDIT_EPI_STORE:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        Z.zdit_op_gemm_splitk(epi, M, N, K, Ad, dev(B, torch.bfloat16), None, None, C, ws)
+        got = host(C)
+        assert np.isfinite(got).all()
+        assert_bf16_result(got, ref, bound)
+    else:
+        C0 = _rng(66).standard_normal((M, N)).astype(np.float32)
+        C = dev(C0)
+        Z.zdit_op_gemm_splitk(epi, M, N, K, Ad, dev(B, torch.bfloat16), None, None, C, ws)
+        got = host(C)
+        assert np.isfinite(got).all()
+        assert np.all(np.abs(got - (C0 + ref)) <= bound + 1e-6 * np.abs(C0) + 1e-6)
+
+
 def test_gemm_splitk_rows_do_not_depend_on_m():
     """The K ranges depend on N and K only: rows computed with 50 or 256 rows are identical."""
     N, K = 2560, 9728
