@@ -360,6 +360,9 @@ def stack(lat, cap, cap_len, t, W, dims, dtype=F32, record=None):
     for bw in W["ctx_ref"]:
         x_cap = block(x_cap, bw, None, cos_c, sin_c, dims)
     x = np.concatenate([x_img, x_cap], axis=0)
+    if record is not None:
+        record["c"] = c.copy()
+        record["main_in"] = x.copy()
     for i, bw in enumerate(W["main"]):
         x = block(x, bw, block_mod(c, bw, dtype), cos_j, sin_j, dims)
         if record is not None:

@@ -25,6 +25,8 @@ are chosen.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -208,18 +210,25 @@ def embed_weights(dims: Dims, seed: int) -> dict:
     }
 
 
-def model_weights(dims: Dims, seed: int) -> dict:
-    """All weights of a stack: embeds plus noise-refiner, context-refiner and main blocks."""
+def model_weights(dims: Dims, seed: int, threads: int | None = None) -> dict:
+    """All weights of a stack: embeds plus noise-refiner, context-refiner and main blocks.
+
+    Blocks are drawn on `threads` threads (default: the usable cores, at most 16); every tensor
+    has its own generator, so the values do not depend on the thread count."""
     w = embed_weights(dims, seed)
-    idx = 0
-    nr, cr, mb = [], [], []
-    for _ in range(dims.n_noise_ref):
-        nr.append(block_weights(dims, seed, idx, adaln=True)); idx += 1
-    for _ in range(dims.n_ctx_ref):
-        cr.append(block_weights(dims, seed, idx, adaln=False)); idx += 1
-    for _ in range(dims.n_main):
-        mb.append(block_weights(dims, seed, idx, adaln=True)); idx += 1
-    w["noise_ref"], w["ctx_ref"], w["main"] = nr, cr, mb
+    nr_, cr_ = dims.n_noise_ref, dims.n_ctx_ref
+    jobs = [(i, i < nr_ or i >= nr_ + cr_) for i in range(nr_ + cr_ + dims.n_main)]
+    if threads is None:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    make = lambda j: block_weights(dims, seed, j[0], adaln=j[1])
+    if threads > 1 and len(jobs) > 1:
+        with ThreadPoolExecutor(min(threads, len(jobs))) as ex:
+            blocks = list(ex.map(make, jobs))
+    else:
+        blocks = [make(j) for j in jobs]
+    w["noise_ref"] = blocks[:nr_]
+    w["ctx_ref"] = blocks[nr_:nr_ + cr_]
+    w["main"] = blocks[nr_ + cr_:]
     return w
 
 

@@ -70,3 +70,42 @@ def assert_bf16_result(got, ref64, acc_err):
     err = np.abs(np.asarray(got, dtype=np.float64) - ref64)
     bad = err > allow * (1 + 1e-9)
     assert not bad.any(), f"{bad.sum()} elements outside bound; worst excess {(err - allow).max():.3e}"
+
+
+def attention_ref_bound(q, k, v):
+    """Softmax attention of queries q [n, hd] over keys k and values v [m, hd] (all keys
+    visible) in float64, and a per-element bound on a bf16 flash-attention result.
+
+    The kernel rounds each probability to bf16 once and uses that number both in P V and in the
+    row sum, so its output is the weighted mean of the values with every weight w_j scaled by
+    (1 + d_j): o' - o = sum_j w_j (1 + d_j) (v_j - o) / (1 + sum_j w_j d_j), hence
+    |o' - o| <= d / (1 - d) * sum_j w_j |v_j - o| with d = max |d_j|.  d collects the bf16
+    rounding (2^-9), the fp32 score sum over hd products (hd 2^-24 |q| |k| / sqrt(hd)) and the
+    exp2 argument rounding.  Added: the fp32 sums over m keys in P V and in the row sum
+    (2 m 2^-24 sum_j w_j |v_j|); the caller adds half a bf16 ulp for the output rounding."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    hd = q.shape[1]
+    m = k.shape[0]
+    s = q @ k.T / np.sqrt(hd)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    o = w @ v
+    ds = hd * 2.0 ** -24 * (np.abs(q) @ np.abs(k).T) / np.sqrt(hd)
+    d = 2.0 ** -9 + ds.max(axis=1) + 2.0 ** -22 * (1 + np.abs(s).max(axis=1) * 1.4427)
+    spread = np.stack([w[i] @ np.abs(v - o[i]) for i in range(q.shape[0])])
+    bound = (d / (1 - d))[:, None] * spread + 2 * m * 2.0 ** -24 * (w @ np.abs(v))
+    return o, bound
+
+
+def assert_attention_close(got, q, k, v):
+    """got [n, hd] (bf16 values) within attention_ref_bound's bound plus half a bf16 ulp of
+    the output, element by element."""
+    o, bound = attention_ref_bound(q, k, v)
+    err = np.abs(np.asarray(got, np.float64) - o)
+    allow = bound + 0.5 * bf16_ulp(np.abs(o) + bound)
+    bad = err > allow * (1 + 1e-9) + 1e-30
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} elements outside the bound; worst err {err.max():.3e}, "
+                           f"worst excess {(err - allow).max():.3e}")
+    return float((err / np.maximum(allow, 1e-30)).max())

@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import synth
 from diffusion_transformer_text_s3_amd import binding as Z
-from gpu_util import assert_bf16_result, bf16_values, dev, drift, host, note, rel_l2
+from gpu_util import assert_attention_close, assert_bf16_result, bf16_values, dev, drift, host, note, rel_l2
 
 pytestmark = pytest.mark.gpu
 BF, F32P = Z.ZDIT_BF16, Z.ZDIT_FP32_DEBUG
@@ -125,7 +125,11 @@ def test_attention_largest_batch():
         q, k, v = _heads(qkv[b, :n], np.arange(n), nh)
         ref = O.attention(q, k, v).reshape(n, nh * 128)
         assert rel_l2(got[b, :n], ref) < 1e-2, n
-        assert np.abs(got[b, :n] - ref).max() < 0.05, n
+        for h in range(nh):
+            D_ = nh * 128
+            assert_attention_close(got[b][:n, h * 128:(h + 1) * 128], qkv[b][:n, h * 128:(h + 1) * 128],
+                                   qkv[b][:n, D_ + h * 128:D_ + (h + 1) * 128],
+                                   qkv[b][:n, 2 * D_ + h * 128:2 * D_ + (h + 1) * 128])
         assert np.all(got[b, n:] == 0)
 
 
@@ -147,6 +151,8 @@ def test_attention_1536x1024_pair_sampled_queries():
             ref = O.attention(q[:, h:h + 1].astype(np.float64), k[:, h:h + 1].astype(np.float64),
                               v[:, h:h + 1].astype(np.float64))[:, 0]
             assert rel_l2(got[b, qs, h * 128:(h + 1) * 128], ref) < 1e-2
+            worst = assert_attention_close(got[b, qs, h * 128:(h + 1) * 128], q[:, h], k[:, h], v[:, h])
+            print(f"branch {b} head {h}: worst error / element bound {worst:.3f}", flush=True)
         assert np.all(got[b, n:] == 0)
 
 

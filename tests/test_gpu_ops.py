@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import synth
 from diffusion_transformer_text_s3_amd import binding as Z
-from gpu_util import assert_bf16_result, bf16_values, dev, host, note, rel_l2, ulp_diff_bf16
+from gpu_util import assert_attention_close, assert_bf16_result, bf16_values, dev, host, note, rel_l2, ulp_diff_bf16
 
 pytestmark = pytest.mark.gpu
 BF, F32P = Z.ZDIT_BF16, Z.ZDIT_FP32_DEBUG
@@ -238,7 +238,11 @@ def test_attention_ragged(prec):
         ref = _attn_ref(qkv[b], seq[b], nh)
         if prec == BF:
             assert rel_l2(got[b, :seq[b]], ref) < 1e-2
-            assert np.abs(got[b, :seq[b]] - ref).max() < 0.05
+            for h in range(nh):
+                D_ = nh * 128
+                assert_attention_close(got[b][:seq[b], h * 128:(h + 1) * 128], qkv[b][:seq[b], h * 128:(h + 1) * 128],
+                                       qkv[b][:seq[b], D_ + h * 128:D_ + (h + 1) * 128],
+                                       qkv[b][:seq[b], 2 * D_ + h * 128:2 * D_ + (h + 1) * 128])
         else:
             np.testing.assert_allclose(got[b, :seq[b]], ref, rtol=1e-5, atol=1e-5)
         assert np.all(got[b, seq[b]:] == 0)
@@ -259,7 +263,11 @@ def test_attention_key_block_counts():
     for b in range(B):
         ref = _attn_ref(qkv[b], seq[b], nh)
         assert rel_l2(got[b, :seq[b]], ref) < 1e-2, seq[b]
-        assert np.abs(got[b, :seq[b]] - ref).max() < 0.05, seq[b]
+        for h in range(nh):
+            D_ = nh * 128
+            assert_attention_close(got[b][:seq[b], h * 128:(h + 1) * 128], qkv[b][:seq[b], h * 128:(h + 1) * 128],
+                                   qkv[b][:seq[b], D_ + h * 128:D_ + (h + 1) * 128],
+                                   qkv[b][:seq[b], 2 * D_ + h * 128:2 * D_ + (h + 1) * 128])
         assert np.all(got[b, seq[b]:] == 0)
 
 
@@ -282,7 +290,11 @@ def test_attention_rising_scores_rescale():
     for b in range(B):
         ref = _attn_ref(qkv[b], seq[b], nh)
         assert rel_l2(got[b, :seq[b]], ref) < 1e-2
-        assert np.abs(got[b, :seq[b]] - ref).max() < 0.05
+        for h in range(nh):
+            D_ = nh * 128
+            assert_attention_close(got[b][:seq[b], h * 128:(h + 1) * 128], qkv[b][:seq[b], h * 128:(h + 1) * 128],
+                                   qkv[b][:seq[b], D_ + h * 128:D_ + (h + 1) * 128],
+                                   qkv[b][:seq[b], 2 * D_ + h * 128:2 * D_ + (h + 1) * 128])
         assert np.all(got[b, seq[b]:] == 0)
 
 
@@ -327,6 +339,8 @@ def test_attention_full_size_sampled_queries():
             p = np.exp(s - s.max(axis=1, keepdims=True))
             ref = (p / p.sum(axis=1, keepdims=True)) @ v
             assert rel_l2(got[b, qs, h * 128:(h + 1) * 128], ref) < 1e-2
+            worst = assert_attention_close(got[b, qs, h * 128:(h + 1) * 128], q, k, v)
+            print(f"branch {b} head {h}: worst error / element bound {worst:.3f}", flush=True)
         assert np.all(got[b, seq[b]:] == 0)
 
 
