@@ -22,7 +22,7 @@ MAX_BATCH = 16
 
 # every exported symbol of include/zdit.h
 EXPORTS = [
-    "zdit_last_error", "zdit_abi_version", "zdit_block_workspace", "zdit_block_fwd",
+    "zdit_last_error", "zdit_abi_version", "zdit_block_workspace", "zdit_block_fwd", "zdit_block_fwd_noalloc",
     "zdit_stack_workspace", "zdit_stack_fwd", "zdit_sigmas", "zdit_n_cap", "zdit_euler_step",
     "zdit_sample_workspace", "zdit_sample", "zdit_rope_tables", "zdit_op_gemm",
     "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn", "zdit_op_qkv_attn",
@@ -107,6 +107,7 @@ def lib():
             "zdit_abi_version": (i32, []),
             "zdit_block_workspace": (sz, [pd, i32, i32]),
             "zdit_block_fwd": (i32, [pd, pw, i32, i32, pi32, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_block_fwd_noalloc": (i32, [pd, pw, i32, i32, pi32, vp, vp, vp, vp, vp]),
             "zdit_stack_workspace": (sz, [pc, i32, i32, i32, i32]),
             "zdit_stack_fwd": (i32, [pc, pm, i32, i32, i32, vp, i64, vp, i32, pi32, pf32, vp, vp, sz, vp]),
             "zdit_sigmas": (i32, [i32, f32, pf32]),
@@ -319,6 +320,11 @@ def zdit_block_fwd(dims, w: DeviceBlock, batch, s_max, seq_len, x, c, cos, sin, 
     return check(lib().zdit_block_fwd(C.byref(dims), C.byref(w.w), batch, s_max, i32_array(seq_len),
                                       ptr(x), ptr(c), ptr(cos), ptr(sin), ptr(ws), ws.numel(),
                                       stream_handle(stream)))
+
+
+def zdit_block_fwd_noalloc(dims, w: DeviceBlock, batch, s_max, seq_len, x, c, cos, sin, stream=None):
+    return check(lib().zdit_block_fwd_noalloc(C.byref(dims), C.byref(w.w), batch, s_max, i32_array(seq_len),
+                                              ptr(x), ptr(c), ptr(cos), ptr(sin), stream_handle(stream)))
 
 
 def zdit_stack_workspace(cfg, batch, lat_h, lat_w, max_cap_len) -> int:

@@ -8,12 +8,26 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "api_util.h"
 
 using namespace zdit;
+
+// Scratch memory of zdit_block_fwd_noalloc: a file-scope device array, one copy per device (the
+// runtime places it when the code object loads on that device; it stays until the process
+// ends).  Host code never passes the array's name to a kernel: its device address on each
+// device comes from hipGetSymbolAddress with that device current, kept below.
+static constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+}  // namespace
 
 std::string& zdit::api_error_text() {
   thread_local std::string text;
@@ -507,6 +521,50 @@ zdit_status stack_forward(const zdit_model_cfg& cfg, const zdit_model_w& w, int 
   return ZDIT_OK;
 }
 
+// Arguments of a block forward other than the workspace.
+zdit_status check_block_args(const zdit_dims* dims, const zdit_block_w* w, int batch, int s_max, const int* seq_len,
+                             const float* x, const float* c, const float* rope_cos, const float* rope_sin) {
+  if (zdit_status s = check_dims(dims)) return s;
+  if (zdit_status s = check_block_w(w, false)) return s;
+  if (batch < 1 || batch > ZDIT_MAX_BATCH) return fail(ZDIT_EINVAL, "batch %d (1..%d)", batch, ZDIT_MAX_BATCH);
+  if (s_max < 1 || (int64_t)batch * s_max > (1 << 24)) return fail(ZDIT_EINVAL, "s_max %d", s_max);
+  if (!seq_fits(s_max, dims->dim)) return fail(ZDIT_EUNSUPPORTED, "s_max %d too long for dim %d", s_max, dims->dim);
+  if (!seq_len) return fail(ZDIT_EINVAL, "seq_len is NULL");
+  for (int b = 0; b < batch; ++b)
+    if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d outside 1..%d", b, seq_len[b], s_max);
+  if (!x || !rope_cos || !rope_sin) return fail(ZDIT_EINVAL, "NULL pointer argument");
+  if (w->w_ada && !c) return fail(ZDIT_EINVAL, "c is NULL but the block has adaLN weights");
+  if (!aligned16(x) || !aligned16(rope_cos) || !aligned16(rope_sin) || (c && !aligned16(c)))
+    return fail(ZDIT_EINVAL, "device pointer not 16-byte aligned");
+  return ZDIT_OK;
+}
+
+// The launch sequence of zdit_block_fwd on a validated call, with workspace ws (at least
+// plan_block().total bytes, 256-aligned).
+zdit_status run_block(const zdit_dims& d, const zdit_block_w& w, int batch, int s_max, const int* seq_len, float* x,
+                      const float* c, const float* rope_cos, const float* rope_sin, char* ws, hipStream_t st) {
+  const BlockPlan pl = plan_block(d, batch, s_max);
+  const int D = d.dim;
+  const Check chk = check_at(d, ws + pl.chk, kBlockChecks);
+  HIP_TRY(check_begin(chk, st));
+  HIP_TRY(check_rows(chk, 0, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
+  float* mod = nullptr;
+  if (w.w_ada) {
+    mod = (float*)(ws + pl.mod);
+    HIP_TRY(launch_adaln(d.precision, batch, d.c_dim, 6 * D, c, w.w_ada, w.b_ada, mod, st));
+  }
+  if (zdit_status s = block_forward(d, w, batch, s_max, seq_len, x, (int64_t)s_max * D, mod, rope_cos, rope_sin,
+                                    (int64_t)s_max * (d.head_dim / 2), ws, st))
+    return s;
+  HIP_TRY(check_rows(chk, 1, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
+  HIP_TRY(check_latch(chk, 0, st));
+  int step, where;
+  if (zdit_status s = check_read(chk, st, &step, &where)) return s;
+  if (where == 0) return fail(ZDIT_ENONFINITE, "non-finite value in the valid rows of the input x");
+  if (where == 1) return fail(ZDIT_ENONFINITE, "non-finite value in the block output (residual stream)");
+  return ok();
+}
+
 double sigma_at(int i, int n, double shift) {
   const double t = (double)i / (double)n;
   return shift * (1.0 - t) / (shift * (1.0 - t) + t);
@@ -527,41 +585,37 @@ size_t zdit_block_workspace(const zdit_dims* dims, int32_t batch, int32_t s_max)
 zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t batch, int32_t s_max,
                            const int32_t* seq_len, float* x, const float* c, const float* rope_cos,
                            const float* rope_sin, void* ws, size_t ws_bytes, void* hip_stream) {
-  if (zdit_status s = check_dims(dims)) return s;
-  if (zdit_status s = check_block_w(w, false)) return s;
-  if (batch < 1 || batch > ZDIT_MAX_BATCH) return fail(ZDIT_EINVAL, "batch %d (1..%d)", batch, ZDIT_MAX_BATCH);
-  if (s_max < 1 || (int64_t)batch * s_max > (1 << 24)) return fail(ZDIT_EINVAL, "s_max %d", s_max);
-  if (!seq_fits(s_max, dims->dim)) return fail(ZDIT_EUNSUPPORTED, "s_max %d too long for dim %d", s_max, dims->dim);
-  if (!seq_len) return fail(ZDIT_EINVAL, "seq_len is NULL");
-  for (int b = 0; b < batch; ++b)
-    if (seq_len[b] < 1 || seq_len[b] > s_max) return fail(ZDIT_EINVAL, "seq_len[%d] = %d outside 1..%d", b, seq_len[b], s_max);
-  if (!x || !rope_cos || !rope_sin || !ws) return fail(ZDIT_EINVAL, "NULL pointer argument");
-  if (w->w_ada && !c) return fail(ZDIT_EINVAL, "c is NULL but the block has adaLN weights");
-  if (!aligned16(x) || !aligned16(rope_cos) || !aligned16(rope_sin) || (c && !aligned16(c)))
-    return fail(ZDIT_EINVAL, "device pointer not 16-byte aligned");
+  if (zdit_status s = check_block_args(dims, w, batch, s_max, seq_len, x, c, rope_cos, rope_sin)) return s;
+  if (!ws) return fail(ZDIT_EINVAL, "NULL pointer argument");
   if (((uintptr_t)ws & 255u) != 0) return fail(ZDIT_EINVAL, "workspace not 256-byte aligned");
-  const BlockPlan pl = plan_block(*dims, batch, s_max);
-  if (ws_bytes < pl.total) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.total);
-  hipStream_t st = (hipStream_t)hip_stream;
-  const int D = dims->dim;
-  const Check chk = check_at(*dims, (char*)ws + pl.chk, kBlockChecks);
-  HIP_TRY(check_begin(chk, st));
-  HIP_TRY(check_rows(chk, 0, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
-  float* mod = nullptr;
-  if (w->w_ada) {
-    mod = (float*)((char*)ws + pl.mod);
-    HIP_TRY(launch_adaln(dims->precision, batch, dims->c_dim, 6 * D, c, w->w_ada, w->b_ada, mod, st));
+  const size_t need = plan_block(*dims, batch, s_max).total;
+  if (ws_bytes < need) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return run_block(*dims, *w, batch, s_max, seq_len, x, c, rope_cos, rope_sin, (char*)ws, (hipStream_t)hip_stream);
+}
+
+zdit_status zdit_block_fwd_noalloc(const zdit_dims* dims, const zdit_block_w* w, int32_t batch, int32_t s_max,
+                                   const int32_t* seq_len, float* x, const float* c, const float* rope_cos,
+                                   const float* rope_sin, void* hip_stream) {
+  if (zdit_status s = check_block_args(dims, w, batch, s_max, seq_len, x, c, rope_cos, rope_sin)) return s;
+  const size_t need = plan_block(*dims, batch, s_max).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(ZDIT_EUNSUPPORTED, "this shape needs %zu bytes of scratch; zdit_block_fwd_noalloc holds %zu "
+                "(use zdit_block_fwd with a workspace)", need, kNoAllocScratchBytes);
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ZDIT_EUNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      if (!p) return fail(ZDIT_EHIP, "hipGetSymbolAddress returned NULL for the scratch array");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
   }
-  if (zdit_status s = block_forward(*dims, *w, batch, s_max, seq_len, x, (int64_t)s_max * D, mod,
-                                    rope_cos, rope_sin, (int64_t)s_max * (dims->head_dim / 2), (char*)ws, st))
-    return s;
-  HIP_TRY(check_rows(chk, 1, x, (int64_t)s_max * D, D, s_max, batch, D, seq_len, st));
-  HIP_TRY(check_latch(chk, 0, st));
-  int step, where;
-  if (zdit_status s = check_read(chk, st, &step, &where)) return s;
-  if (where == 0) return fail(ZDIT_ENONFINITE, "non-finite value in the valid rows of the input x");
-  if (where == 1) return fail(ZDIT_ENONFINITE, "non-finite value in the block output (residual stream)");
-  return ok();
+  return run_block(*dims, *w, batch, s_max, seq_len, x, c, rope_cos, rope_sin, (char*)ws, (hipStream_t)hip_stream);
 }
 
 size_t zdit_stack_workspace(const zdit_model_cfg* cfg, int32_t batch, int32_t lat_h, int32_t lat_w,

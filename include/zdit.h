@@ -16,7 +16,8 @@
  *   - Device pointers are HIP device addresses; host pointers are ordinary memory.  The
  *     caller owns every buffer (weights, activations, workspace).  Pointers are borrowed for
  *     the call and must stay valid until the enqueued work completes.  The library allocates
- *     no device memory and keeps no pointer after returning.
+ *     no device memory and keeps no pointer after returning (zdit_block_fwd_noalloc works in
+ *     a fixed scratch array the library's code object holds on each device).
  *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
  *     Nothing synchronises; no host<->device copy is made, except that the text-encoder
  *     calls copy the host token ids into their workspace (the host array may be reused as
@@ -123,6 +124,20 @@ zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t
                            int32_t s_max, const int32_t* seq_len, float* x, const float* c,
                            const float* rope_cos, const float* rope_sin, void* ws,
                            size_t ws_bytes, void* hip_stream);
+
+/* zdit_block_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, hosts that forbid allocation): the same computation and results, with
+ * the workspace replaced by a scratch array the library holds on each device (128 MiB, placed
+ * when the library's code loads on that device and kept until the process ends).  Calls
+ * zdit_block_fwd would accept whose zdit_block_workspace() exceeds 128 MiB return
+ * ZDIT_EUNSUPPORTED (the 256 px and 512 px pairs fit; the 1024^2 pair needs a workspace).  All
+ * calls on one device share its scratch: calls that overlap on one device (other streams,
+ * other threads) race and must be ordered by the caller.  No allocation, no free, no host
+ * copy (except the ZDIT_CHECK_FINITE read-back). */
+zdit_status zdit_block_fwd_noalloc(const zdit_dims* dims, const zdit_block_w* w, int32_t batch,
+                                   int32_t s_max, const int32_t* seq_len, float* x,
+                                   const float* c, const float* rope_cos, const float* rope_sin,
+                                   void* hip_stream);
 
 /* Whole-model configuration.  n_noise_ref adaLN blocks on image tokens, n_ctx_ref blocks
  * without adaLN on caption tokens, n_main adaLN blocks on the joint sequence ([CoreAI]
