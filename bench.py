@@ -3,14 +3,22 @@
 A step is one full 8-step negated-CFG FlowMatchEuler pass at 1024x1024 (cond caption 45 ->
 n_cap 64, uncond 10 -> 32): 16 stack forwards of 2 + 2 + 30 blocks at dim 3840 plus the 8
 Euler updates and the decode unscale, through zdit_sample.  Inputs are resident in HBM before
-the timed region.  Prints one JSON line; its value is TFLOP/s over the FLOPs the pass executes
+the timed region.  Prints one JSON line: `value` is TFLOP/s over the FLOPs the pass executes
 (the shared image path and the step-invariant caption path are reused exactly, so those are
-counted once), its ms_per_step the wall time of one pass.
+counted once; the method's own algorithmic count is reported beside it), `ms_per_step` the
+wall time of one pass.  Also reported: the per-pass median and minimum (HIP events), the
+graphics clock and socket power sampled during the timed passes, one main block on the 1024^2
+pair, one full-width block at 256 px (at the MFMA / HBM ridge: both fractions), one stack
+forward at 1024^2 (cond alone and the cond/uncond pair), the roofline of the dominant kernel
+and the oracle's CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder]
 
 --workload encoder times the text encoder instead (its own JSON line): the Qwen3-4B-shaped
 decoder on two right-padded rows of 64 ids (45 and 10 valid) to hidden_states[-2].
+--kernel-only NAME launches one kernel at its main-block shape a few times on operands that
+rotate through more memory than the 256 MB last-level cache holds (as in the pass), for
+rocprofv3 counter runs.
 """
 from __future__ import annotations
 
@@ -78,6 +86,115 @@ def measured_peaks(stream):
     return info
 
 
+class ClockSampler:
+    """The graphics clock (MHz) and socket power (W) sampled on a thread while the work runs,
+    through amdsmi; best effort (empty when the library or the metrics are unavailable)."""
+
+    def __init__(self, period_s=0.02):
+        self.period = period_s
+        self.clk, self.pwr = [], []
+        self._stop = None
+        self._th = None
+        self._h = None
+
+    @staticmethod
+    def _num(v):
+        """A clock or power reading as a float, None when missing (the metrics table marks
+        absent entries with all-ones values); a list (one per XCD) gives its mean."""
+        if isinstance(v, (list, tuple)):
+            vals = [f for f in (ClockSampler._num(x) for x in v) if f is not None]
+            return sum(vals) / len(vals) if vals else None
+        try:
+            f = float(v)
+        except (TypeError, ValueError):
+            return None
+        return f if 0 < f < 65535 else None
+
+    def _sample(self):
+        import amdsmi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        c = None
+        for k in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            if k in m:
+                c = self._num(m[k])
+                if c is not None:
+                    break
+        p = None
+        for k in ("current_socket_power", "average_socket_power"):
+            if k in m:
+                p = self._num(m[k])
+                if p is not None:
+                    break
+        if c is not None:
+            self.clk.append(c)
+        if p is not None:
+            self.pwr.append(p)
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._sample()
+        except Exception:  # noqa: BLE001
+            self._h = None
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.wait(self.period):
+                try:
+                    self._sample()
+                except Exception:  # noqa: BLE001
+                    return
+
+        self._th = threading.Thread(target=run, daemon=True)
+        self._th.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._th:
+            self._stop.set()
+            self._th.join()
+        try:
+            import amdsmi
+            if self._h is not None:
+                amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+        return False
+
+    def summary(self):
+        if not self.clk:
+            return None
+        out = {"gfxclk_mhz_mean": round(sum(self.clk) / len(self.clk), 1), "gfxclk_mhz_min": round(min(self.clk), 1),
+               "gfxclk_mhz_max": round(max(self.clk), 1), "samples": len(self.clk)}
+        if self.pwr:
+            out["socket_power_w_mean"] = round(sum(self.pwr) / len(self.pwr), 1)
+        return out
+
+
+def time_reps(fn, reps, stream):
+    """Per-call durations (ms) of fn() over reps back-to-back calls: HIP events on `stream`
+    between the calls (no synchronisation inside)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        fn()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+
+def stats(ms):
+    s = sorted(ms)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"median_ms": round(med, 4), "min_ms": round(s[0], 4), "mean_ms": round(sum(s) / n, 4), "reps": n}
+
+
 def random_model_on_device(dims, seed):
     """Seeded N(0, 0.02) bf16 weights generated on the device (norm gains 1 + 0.02 N(0,1))."""
     import torch
@@ -123,8 +240,8 @@ def time_op(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
-def measure_block(dims, B, S, seed, stream):
-    """One main block at the 1024^2 pair shape through zdit_block_fwd."""
+def measure_block(dims, B, S, seed, stream, reps=10):
+    """One main block at the 1024^2 pair shape through zdit_block_fwd: per-call durations."""
     import torch
     from diffusion_transformer_text_s3_amd import binding as Z
     g = torch.Generator(device="cuda")
@@ -141,24 +258,204 @@ def measure_block(dims, B, S, seed, stream):
     sin = torch.zeros((B, s_max, 64), device="cuda")
     dd = Z.make_dims(dims)
     ws = Z.workspace(Z.zdit_block_workspace(dd, B, s_max))
-    ms = time_op(lambda: Z.zdit_block_fwd(dd, blk, B, s_max, S, x, c, cos, sin, ws, stream), 10, stream)
+    fn = lambda: Z.zdit_block_fwd(dd, blk, B, s_max, S, x, c, cos, sin, ws, stream)
+    fn()
+    ms = time_reps(fn, reps, stream)
     fl = sum(block_flops(s, d, H) for s in S)
     return ms, fl
 
 
-def measure_dominant_gemm(dims, M, stream):
-    """The SwiGLU w1/w3 GEMM of a main block at the 1024^2 pair shape (M = 2 x 4160)."""
+def block_weight_bytes(dims):
+    """bf16 weight bytes of one adaLN block: W_qkv, W_out, W1, W3, W2 and W_ada."""
+    d, H = dims.dim, dims.ffn_hidden
+    return 2 * (3 * d * d + d * d + 3 * d * H + 6 * d * dims.c_dim)
+
+
+def block_hbm_bytes(dims, S):
+    """HBM bytes of one block on S tokens if every tensor crosses HBM once per use: the bf16
+    weights; the fp32 residual stream read by each RMSNorm and read and written by each gated
+    residual (6 S d floats); the bf16 activations written once and read once (h and h2, q k v,
+    the attention output, the SwiGLU product)."""
+    d, H = dims.dim, dims.ffn_hidden
+    return block_weight_bytes(dims) + 4 * 6 * S * d + 2 * 2 * S * (d + 3 * d + d + d + H)
+
+
+def measure_block_256(dims, seed, stream, reps=10, nblk=8):
+    """One full-width block at 256 px (B = 1, S = 256 image tokens + n_cap 64 = 320): a chain of
+    nblk blocks with distinct weights (2.9 GB, more than the last-level cache holds, as in the
+    stack), timed per chain; per block = chain / nblk."""
     import torch
     from diffusion_transformer_text_s3_amd import binding as Z
-    d, H = dims.dim, dims.ffn_hidden
     g = torch.Generator(device="cuda")
-    g.manual_seed(7)
-    A = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
-    W1 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-    W3 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-    U = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
-    ms = time_op(lambda: Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M, H, d, A, W1, W3, None, U, stream), 20, stream)
-    return ms, 2.0 * M * d * 2 * H
+    g.manual_seed(seed)
+    d, H = dims.dim, dims.ffn_hidden
+    S = 256 + 64
+    mat = lambda r, c: (torch.randn((r, c), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    vec = lambda n, base=0.0: torch.randn(n, generator=g, device="cuda") * 0.02 + base
+    blks = [Z.DeviceBlock({"w_qkv": mat(3 * d, d), "w_out": mat(d, d), "w1": mat(H, d), "w3": mat(H, d),
+                           "w2": mat(d, H), "norm1": vec(d, 1.0), "norm2": vec(d, 1.0), "w_ada": mat(6 * d, dims.c_dim),
+                           "b_ada": vec(6 * d)}) for _ in range(nblk)]
+    x = torch.randn((1, S, d), generator=g, device="cuda")
+    c = torch.randn((1, dims.c_dim), generator=g, device="cuda")
+    cos = torch.ones((1, S, 64), device="cuda")
+    sin = torch.zeros((1, S, 64), device="cuda")
+    dd = Z.make_dims(dims)
+    ws = Z.workspace(Z.zdit_block_workspace(dd, 1, S))
+
+    def chain():
+        for b in blks:
+            Z.zdit_block_fwd(dd, b, 1, S, [S], x, c, cos, sin, ws, stream)
+
+    chain()
+    ms = [t / nblk for t in time_reps(chain, reps, stream)]
+    st = stats(ms)
+    fl, by = block_flops(S, d, H), block_hbm_bytes(dims, S)
+    med = st["median_ms"] * 1e-3
+    return {"shape": f"full-width block at 256 px, B = 1, S = {S}, {nblk} blocks of distinct weights chained",
+            **st, "tflops": round(fl / med / 1e12, 2), "pct_bf16_peak": round(100 * fl / med / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "hbm_bytes_per_block": by, "hbm_gbs": round(by / med / 1e9, 1),
+            "pct_hbm_peak": round(100 * by / med / 1e9 / PEAK_HBM_GBS, 2)}
+
+
+def measure_stack(dims, model, lat, cap, cap_len, stream, reps=10):
+    """One stack forward at 1024^2 (one sampler step): the cond branch alone (B = 1) and the
+    cond/uncond pair sharing the latent (B = 2), per-call durations."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    cfg = Z.make_cfg(dims)
+    lat_h, lat_w = lat.shape[-2:]
+    Lmax = max(cap_len)
+    nimg = (lat_h // 2) * (lat_w // 2)
+    n_cap = lambda L: -(-L // dims.seq_multiple) * dims.seq_multiple
+    out = {}
+    for B in (1, 2):
+        vel = torch.empty((B, dims.latent_ch, lat_h, lat_w), device="cuda")
+        ws = Z.workspace(Z.zdit_stack_workspace(cfg, B, lat_h, lat_w, Lmax))
+        fn = lambda: Z.zdit_stack_fwd(cfg, model, B, lat_h, lat_w, lat, 0, cap[:B], Lmax, cap_len[:B], [0.5] * B,
+                                      vel, ws, stream)
+        fn()
+        st = stats(time_reps(fn, reps, stream))
+        # executed FLOPs: the pair runs the image path once (shared latent, same t)
+        fl = pass_flops(dims, nimg, cap_len[:B], 1, n_cap, reuse=True)
+        alg = pass_flops(dims, nimg, cap_len[:B], 1, n_cap)
+        med = st["median_ms"] * 1e-3
+        out["cond" if B == 1 else "pair"] = {**st, "executed_tflop": round(fl / 1e12, 3),
+                                             "algorithmic_tflop": round(alg / 1e12, 3),
+                                             "tflops": round(fl / med / 1e12, 2),
+                                             "pct_bf16_peak": round(100 * fl / med / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        del ws, vel
+    return out
+
+
+# Kernels timed or counted alone, at their main-block shapes on the 1024^2 pair (M = 2 x 4160
+# rows, of which 4160 + 4128 are valid): name -> (label, algorithmic work per launch on the
+# valid rows, unit).  GEMM FLOPs are 2 M_valid N K; the norm / elementwise kernels count the
+# bytes a single pass over their operands moves.
+M_PAIR, M_VALID = 8320, 8288
+
+
+def kernel_units(dims):
+    d, H = dims.dim, dims.ffn_hidden
+    S = (4160, 4128)
+    n = 16 * 128 * 128
+    return {
+        "qkv": ("gemm_bf16_kernel<EPI_QKV> (q/k/v + RoPE + V^T), M=8320 N=11520 K=3840", 2 * M_VALID * d * 3 * d, "flop"),
+        "attn": ("attn_bf16_kernel, 1024^2 pair (S = 4160 / 4128, 30 heads)", sum(4 * s * s * d for s in S), "flop"),
+        "out": ("gemm_bf16_kernel<EPI_RESID> (out projection + gated residual), M=8320 N=3840 K=3840",
+                2 * M_VALID * d * d, "flop"),
+        "swiglu": ("gemm_bf16_kernel<EPI_SWIGLU> (w1/w3 + SwiGLU), M=8320 N=10240 K=3840", 2 * M_VALID * d * 2 * H,
+                   "flop"),
+        "w2": ("gemm_bf16_kernel<EPI_RESID> (w2 + gated residual), M=8320 N=3840 K=10240", 2 * M_VALID * d * H, "flop"),
+        # x read (fp32), h written (bf16), gain / shift / scale per branch
+        "rmsnorm": ("rmsnorm_mod_kernel, 8320 x 3840 rows", M_VALID * d * (4 + 2), "byte"),
+        # W_ada of 30 main blocks (bf16) + their modulation vectors for two branches (fp32)
+        "adaln": ("adaln_kernel, 30 main blocks x 2 branches (one launch)", 30 * (6 * d * dims.c_dim * 2 + 2 * 6 * d * 4),
+                  "byte"),
+        # x read and written, two velocities read, the decode output written (fp32)
+        "euler": ("euler_kernel, 16 x 128 x 128 fp32 latent, CFG pair + decode", n * 4 * 5, "byte"),
+    }
+
+
+class KernelRunner:
+    """Launches one kernel at its main-block shape on operand sets that rotate through more
+    memory than the 256 MB last-level cache, so the weights and activations come from HBM as
+    they do in the pass."""
+
+    def __init__(self, dims, which, stream, nsets=4):
+        import torch
+        from diffusion_transformer_text_s3_amd import binding as Z
+        self.Z, self.stream, self.which, self.i = Z, stream, which, 0
+        d, H, M = dims.dim, dims.ffn_hidden, M_PAIR
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        bf = torch.bfloat16
+        rnd = lambda *shape, std=1.0: (torch.randn(shape, generator=g, device="cuda") * std)
+        self.sets = []
+        for _ in range(nsets):
+            t = {}
+            if which == "swiglu":
+                t = dict(A=rnd(M, d).to(bf), B=rnd(H, d, std=0.02).to(bf), B2=rnd(H, d, std=0.02).to(bf),
+                         C=torch.empty((M, H), dtype=bf, device="cuda"))
+            elif which in ("out", "w2"):
+                K = d if which == "out" else H
+                t = dict(A=rnd(M, K).to(bf), B=rnd(d, K, std=0.02).to(bf), vec=rnd(d, std=0.02),
+                         C=rnd(M, d))
+            elif which in ("qkv", "attn"):
+                t = dict(h=rnd(M, d).to(bf), w=rnd(3 * d, d, std=0.02).to(bf),
+                         cos=torch.ones((2, 4160, 64), device="cuda"), sin=torch.zeros((2, 4160, 64), device="cuda"),
+                         qkv=torch.empty((M, 3 * d), dtype=bf, device="cuda"),
+                         o=torch.empty((M, d), dtype=bf, device="cuda"),
+                         ws=Z.workspace(Z.zdit_op_attn_workspace(Z.ZDIT_BF16, 2, 4160, dims.n_heads)))
+            elif which == "rmsnorm":
+                t = dict(x=rnd(M, d), gain=rnd(d, std=0.02) + 1, shift=rnd(d, std=0.02), scale=rnd(d, std=0.02),
+                         out=torch.empty((M, d), dtype=bf, device="cuda"))
+            elif which == "adaln":
+                t = dict(c=rnd(2, dims.c_dim), w=rnd(30 * 6 * d, dims.c_dim, std=0.02).to(bf),
+                         b=rnd(30 * 6 * d, std=0.02), out=torch.empty((2, 30 * 6 * d), device="cuda"))
+            elif which == "euler":
+                n = 16 * 128 * 128
+                t = dict(x=rnd(n), vc=rnd(n), vu=rnd(n), dec=torch.empty(n, device="cuda"))
+            elif which == "copy":
+                t = dict(src=rnd(M, H).to(bf), dst=torch.empty((M, H), dtype=bf, device="cuda"))
+            else:
+                raise ValueError(which)
+            self.sets.append(t)
+        self.dims = dims
+
+    def __call__(self):
+        Z, t, d, H = self.Z, self.sets[self.i % len(self.sets)], self.dims.dim, self.dims.ffn_hidden
+        self.i += 1
+        st, w = self.stream, self.which
+        if w == "swiglu":
+            Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M_PAIR, H, d, t["A"], t["B"], t["B2"], None, t["C"], st)
+        elif w == "out":
+            Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_RESID, M_PAIR, d, d, t["A"], t["B"], None, t["vec"], t["C"], st)
+        elif w == "w2":
+            Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_RESID, M_PAIR, d, H, t["A"], t["B"], None, t["vec"], t["C"], st)
+        elif w in ("qkv", "attn"):
+            Z.zdit_op_qkv_attn(2, 4160, self.dims.n_heads, [4160, 4128], t["h"], t["w"], t["cos"], t["sin"],
+                               t["qkv"], t["o"], t["ws"], st)
+        elif w == "rmsnorm":
+            Z.zdit_op_rmsnorm_mod(Z.ZDIT_BF16, M_PAIR, d, t["x"], t["gain"], t["shift"], t["scale"], 1e-6, t["out"], st)
+        elif w == "adaln":
+            Z.zdit_op_adaln(Z.ZDIT_BF16, 2, self.dims.c_dim, 30 * 6 * d, t["c"], t["w"], t["b"], t["out"], st)
+        elif w == "euler":
+            n = t["x"].numel()
+            Z.zdit_euler_step(t["x"], t["vc"], t["vu"], n, 1.0, 0.9, 0.8, t["dec"], st)
+        elif w == "copy":
+            t["dst"].copy_(t["src"])
+
+
+def measure_dominant_gemm(dims, stream, reps=20):
+    """The SwiGLU w1/w3 GEMM of a main block at the 1024^2 pair shape (M = 2 x 4160), operands
+    rotating through four sets (0.9 GB, more than the last-level cache: the weights come from
+    HBM as in the pass).  Average launch duration from HIP events over the timed launches, on
+    the stream they are launched on; FLOPs over the valid rows (2 x 8288 x 3840 x 20480)."""
+    run = KernelRunner(dims, "swiglu", stream)
+    for _ in range(4):
+        run()
+    ms = time_reps(run, reps, stream)
+    return ms, kernel_units(dims)["swiglu"][1]
 
 
 def traffic_from_profiles(kernel_key):
@@ -331,21 +628,17 @@ def encoder_cpu_baseline(ed, lens, nb):
 
 
 def kernel_only(which):
-    """Three launches of the SwiGLU GEMM at the main-block 1024^2 pair shape, three plain
-    device copies of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written), or
-    three of the encoder's split-K down projection (M=128, N=2560, K=9728)."""
+    """Launches of one kernel at its main-block shape on rotating operand sets (KernelRunner):
+    4 warm-up launches, then 12 more, for rocprofv3 counter runs; `copy` is a plain device
+    copy of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written), the counter
+    calibration; `enc_down` the encoder's split-K down projection (M=55, N=2560, K=9728)."""
     import torch
     import synth
     from diffusion_transformer_text_s3_amd import binding as Z
-    d, H, M = synth.FULL.dim, synth.FULL.ffn_hidden, 8320
-    g = torch.Generator(device="cuda")
-    g.manual_seed(7)
-    if which == "copy":
-        src = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-    elif which == "enc_down":
+    stream = torch.cuda.current_stream()
+    if which == "enc_down":
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
         ed = synth.ENC_FULL
         Me, D, I = 55, ed.hidden, ed.inter  # the valid rows of the 45- and 10-token captions
         A = torch.randn((Me, I), generator=g, device="cuda").to(torch.bfloat16)
@@ -355,14 +648,11 @@ def kernel_only(which):
         for _ in range(3):
             Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, Me, D, I, A, Wd, None, None, X, ws)
     else:
-        A = torch.randn((M, d), generator=g, device="cuda").to(torch.bfloat16)
-        W1 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-        W3 = (torch.randn((H, d), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-        U = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
-        for _ in range(3):
-            Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M, H, d, A, W1, W3, None, U)
+        run = KernelRunner(synth.FULL, which, stream)
+        for _ in range(16):
+            run()
     torch.cuda.synchronize()
-    print(f"kernel-only {which}: 3 launches done", flush=True)
+    print(f"kernel-only {which}: launches done", flush=True)
 
 
 def main():
@@ -374,10 +664,11 @@ def main():
                     help="the DiT pass at 1024^2 (default) or 1536x1024, or the text encoder forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
-    ap.add_argument("--kernel-only", choices=["swiglu", "copy", "enc_down"], default=None,
-                    help="launch only the dominant GEMM at its main-block shape (or a plain device copy of "
-                         "170,393,600 bytes, the counter calibration; or the encoder's split-K down projection) "
-                         "three times, for rocprofv3 --pmc runs")
+    ap.add_argument("--kernel-only", default=None,
+                    choices=["qkv", "attn", "out", "swiglu", "w2", "rmsnorm", "adaln", "euler", "copy", "enc_down"],
+                    help="launch only one kernel at its main-block shape on rotating operands (or a plain device "
+                         "copy of 170,393,600 bytes, the counter calibration; or the encoder's split-K down "
+                         "projection), for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
@@ -419,13 +710,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    per_pass = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     out = x.float().cpu().numpy()
     finite = bool(np.isfinite(out).all())
+    del ws
 
     n_cap = lambda L: -(-L // dims.seq_multiple) * dims.seq_multiple
     nimg = (lat_h // 2) * (lat_w // 2)
@@ -436,13 +733,21 @@ def main():
     # one main block at the 1024^2 pair shape
     S_pair = [64 * 64 + n_cap(L) for L in (45, 10)]
     blk_ms, blk_fl = measure_block(dims, 2, S_pair, args.seed + 1, stream)
+    blk = stats(blk_ms)
+    blk_s = blk["median_ms"] * 1e-3
+    # one full-width block at 256 px, and one stack forward at 1024^2 (cond, pair)
+    blk256 = measure_block_256(dims, args.seed + 2, stream)
+    stack = measure_stack(dims, model, x0, cap, cap_len, stream) if args.workload == "1024" else None
+    del model
+    torch.cuda.empty_cache()
     # dominant kernel: the SwiGLU w1/w3 GEMM at the main-block pair shape
-    M = 2 * max(S_pair)
-    g_ms, g_fl = measure_dominant_gemm(dims, M, stream)
-    achieved = g_fl / (g_ms * 1e-3) / 1e12
-    roof = {"kernel": "gemm_bf16_kernel<EPI_SWIGLU> (w1/w3 + SwiGLU), M=8320 N=10240 K=3840",
+    g_ms, g_fl = measure_dominant_gemm(dims, stream)
+    g_avg = sum(g_ms) / len(g_ms)
+    achieved = g_fl / (g_avg * 1e-3) / 1e12
+    roof = {"kernel": kernel_units(dims)["swiglu"][0],
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(g_ms, 4),
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(g_avg, 4),
+            "flop_per_launch": g_fl, "launches": len(g_ms),
             "traffic": traffic_from_profiles("gemm_swiglu")}
 
     dev = measured_peaks(stream)
@@ -461,9 +766,13 @@ def main():
                    "reuse": "shared-latent image path once per step for both branches; caption rows "
                             "after the context refiners computed in step 0 only (bit-identical)"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "block_fwd": {"shape": "main block, 1024^2 cond/uncond pair, S = 4160 / 4128", "ms": round(blk_ms, 3),
-                      "tflops": round(blk_fl / (blk_ms * 1e-3) / 1e12, 2),
-                      "pct_bf16_peak": round(100 * blk_fl / (blk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "algorithmic_tflops": round(flops / dt / 1e12, 2),
+        "pass": {**stats(per_pass), "clock": clock.summary()},
+        "block_fwd": {"shape": "main block, 1024^2 cond/uncond pair, S = 4160 / 4128", **blk,
+                      "tflops": round(blk_fl / blk_s / 1e12, 2),
+                      "pct_bf16_peak": round(100 * blk_fl / blk_s / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        "block_256px": blk256,
+        "stack_fwd_1024": stack,
         "roofline": roof,
         "device": dev,
         "output_finite": finite,

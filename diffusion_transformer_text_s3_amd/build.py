@@ -69,6 +69,57 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, jobs: int
     return LIB
 
 
+SAN_FLAGS = ["-O1", "-g",
+             # host code only: the device code is built as usual
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_DIR = os.path.join(BUILD, "asan")
+SAN_LIB = os.path.join(SAN_DIR, "libzdit_asan.so")
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime (with the UndefinedBehaviorSanitizer handlers) that a
+    process loading the sanitized library must preload."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        lib = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+        for v in sorted(os.listdir(lib)) if os.path.isdir(lib) else []:
+            cand = os.path.join(lib, v, "lib", "linux", "libclang_rt.asan-x86_64.so")
+            if os.path.exists(cand):
+                return cand
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
+def build_sanitized(jobs: int = 8) -> str:
+    """The host code of the library built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (device code unchanged) into _build/asan/libzdit_asan.so, for the host-side tests; not the
+    product library."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = _sources()
+
+    def one(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *[f for f in COMMON_FLAGS if f != "-O3"], *SAN_FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
-    print(path)
+    if "--sanitize" in sys.argv:
+        print(build_sanitized())
+    else:
+        path = build(verbose="-v" in sys.argv)
+        print(path)

@@ -7,6 +7,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# A host-test run against another build of the library (the sanitized one, see
+# test_host_sanitizers.py) names it here.
+if os.environ.get("ZDIT_TEST_LIB"):
+    from diffusion_transformer_text_s3_amd import binding as _binding
+    _binding.LIB_PATH = os.environ["ZDIT_TEST_LIB"]
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
