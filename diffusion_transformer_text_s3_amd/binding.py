@@ -25,6 +25,7 @@ EXPORTS = [
     "zdit_last_error", "zdit_abi_version", "zdit_block_workspace", "zdit_block_fwd", "zdit_block_fwd_noalloc",
     "zdit_stack_workspace", "zdit_stack_fwd", "zdit_sigmas", "zdit_n_cap", "zdit_euler_step",
     "zdit_sample_workspace", "zdit_sample", "zdit_rope_tables", "zdit_op_gemm",
+    "zdit_op_gemm_ksplit_workspace", "zdit_op_gemm_ksplit",
     "zdit_op_rmsnorm_mod", "zdit_op_rope", "zdit_op_attn_workspace", "zdit_op_attn", "zdit_op_qkv_attn",
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
     "zdit_encoder_workspace", "zdit_encoder_fwd", "zdit_op_embed_workspace", "zdit_op_embed",
@@ -117,6 +118,8 @@ def lib():
             "zdit_sample": (i32, [pc, pm, i32, i32, vp, vp, i32, pi32, f32, i32, f32, vp, vp, sz, vp]),
             "zdit_rope_tables": (i32, [i32, pi32, f32, i32, i32, i32, i32, pi32, vp, vp, vp]),
             "zdit_op_gemm": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+            "zdit_op_gemm_ksplit_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_gemm_ksplit": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "zdit_op_rmsnorm_mod": (i32, [i32, i32, i32, vp, vp, vp, vp, f32, vp, vp]),
             "zdit_op_rope": (i32, [i32, i32, i32, i32, pi32, vp, vp, vp, vp]),
             "zdit_op_attn_workspace": (sz, [i32, i32, i32, i32]),
@@ -375,6 +378,15 @@ def zdit_rope_tables(kind, rope_axes, theta, batch, s_max, grid_h, grid_w, n_cap
 def zdit_op_gemm(precision, epilogue, M, N, K, A, B, B2, vec, Cout, stream=None):
     return check(lib().zdit_op_gemm(precision, epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
                                     stream_handle(stream)))
+
+
+def zdit_op_gemm_ksplit_workspace(epilogue, M, N, K) -> int:
+    return lib().zdit_op_gemm_ksplit_workspace(epilogue, M, N, K)
+
+
+def zdit_op_gemm_ksplit(epilogue, M, N, K, A, B, B2, vec, Cout, ws, stream=None):
+    return check(lib().zdit_op_gemm_ksplit(epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
+                                           ptr(ws), ws.numel() if ws is not None else 0, stream_handle(stream)))
 
 
 def zdit_op_rmsnorm_mod(precision, rows, dim, x, gain, shift, scale, eps, out, stream=None):

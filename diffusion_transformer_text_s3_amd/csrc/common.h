@@ -29,7 +29,11 @@ struct RowMap {
 // EPI_QKV: the fused q/k/v projection of a block (bf16 only): q and k columns are rotated by
 // RoPE on rows below seq[b] and stored, v columns are not stored in C but written transposed
 // into vt (see k_attn.hip for its layout), zero on rows at or past seq[b].
-enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+// EPI_PART / EPI_PART_SWIGLU: the K range [k0, k0 + k_split) of split blockIdx.y, its fp32
+// partial product stored to part + split * M * part_ld (row m at m * part_ld; SwiGLU: the W1 sums
+// at columns n, the W3 sums at N + n), for a fixed-order sum by the split-K reduction.
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_RESID = 2, EPI_SWIGLU = 3, EPI_QKV = 4, EPI_PART = 5,
+           EPI_PART_SWIGLU = 6 };
 
 struct GemmArgs {
   const void* A;
@@ -49,10 +53,23 @@ struct GemmArgs {
   void* vt;
   int vt_pad, n_heads;
   int seq[kMaxBatch];
+  // EPI_PART / EPI_PART_SWIGLU only
+  float* part;
+  int k_split, part_ld;
 };
 
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s);
+// The main GEMM split over K for few rows: `splits` ranges of g.k_split columns (a multiple of
+// 32, from N and K only) computed by gemm_bf16_kernel into fp32 partials `part`
+// [splits][M][Nv] (Nv = N, or 2N for SwiGLU), then summed in range order by the split-K
+// reduction with the epilogue (EPI_STORE, EPI_RESID, EPI_SWIGLU) through g.out.
+struct SplitPlan {
+  int splits, k_split, Nv;
+};
+SplitPlan tile_split_plan(int epi, int N, int K);
+size_t tile_split_workspace(int epi, int M, int N, int K);
+hipError_t launch_gemm_bf16_split(int epi, const GemmArgs& g, float* part, hipStream_t s);
 hipError_t launch_gemm_f32(int epi, const GemmArgs& g, hipStream_t s);
 
 // Split-K GEMM for few rows (M <= 256; N % 8 == 0, K % 64 == 0): fp32 partials of
@@ -107,6 +124,9 @@ struct SplitKFuse {
 };
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows = nullptr,
                               int a_phys_rows = 0, const int* c_rows = nullptr, const SplitKFuse* fuse = nullptr);
+// The split-K reduction alone: sums a.splits partial planes [splits][M][Nv] of a.part in order
+// and applies the epilogue (EPI_STORE, EPI_RESID, EPI_SWIGLU) through g.out (a.c_rows NULL).
+hipError_t launch_splitk_reduce(int epi, const SplitKArgs& a, const GemmArgs& g, hipStream_t s);
 
 // q, k, v rows: row r of branch b at qkv + (b * s_max + r) * row_stride elements, query head
 // h at column h * 128, key head j at k_col + j * 128, value head j at v_col + j * 128.  Query

@@ -140,13 +140,19 @@ __device__ __forceinline__ void mma_slab(const Frags& f, AccT (&acc)[4][8]) {
 // 16-byte read-back free of bank conflicts.
 template <int EPI>
 struct EpiFmt {
-  static constexpr bool kF32 = (EPI == EPI_BIAS || EPI == EPI_RESID);
+  static constexpr bool kPart = (EPI == EPI_PART || EPI == EPI_PART_SWIGLU);
+  static constexpr bool kF32 = (EPI == EPI_BIAS || EPI == EPI_RESID || kPart);
   static constexpr int ES = kF32 ? 4 : 2;             // bytes per staged element
   static constexpr int VW = 16 / ES;                  // elements per 16-byte chunk
   static constexpr int CPR = 64 / VW;                 // chunks per 64-wide row
   static constexpr int STRIDE = 64 * ES + 16 * (ES / 2);  // fp32: 288 B, bf16: 144 B
-  static constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;  // 64-column sub-tiles per band
+  // 64-column sub-tiles per band (PART_SWIGLU: the W1 sums, then the W3 sums of 64 outputs)
+  static constexpr int NSUB = (EPI == EPI_SWIGLU) ? 1 : 2;
 };
+
+// The B tile holds W1 and W3 rows in pairs (SwiGLU and its partial form).
+template <int EPI>
+constexpr bool kPaired = (EPI == EPI_SWIGLU || EPI == EPI_PART_SWIGLU);
 
 // RoPE on 4 (x0, x1) pairs of a bf16 q or k chunk: y0 = x0 c - x1 s, y1 = x0 s + x1 c in fp32,
 // each product and sum rounded (no contraction), then rounded to bf16 -- the same arithmetic
@@ -171,15 +177,15 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 v, float4 c4, float4 s4) {
 }
 
 template <int EPI, int NBAND, class Stage>
-__device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int ncol_wave, char* stg, int lane,
-                                             Stage stage) {
+__device__ __forceinline__ void epilogue_out(const GemmArgs& g, void* Cbase, int m_wave, int ncol_wave, char* stg,
+                                             int lane, Stage stage) {
   constexpr bool kF32 = EpiFmt<EPI>::kF32;
   constexpr int VW = EpiFmt<EPI>::VW, CPR = EpiFmt<EPI>::CPR, STRIDE = EpiFmt<EPI>::STRIDE;
   constexpr int NSUB = EpiFmt<EPI>::NSUB;
   const int rpb = g.out.rows_per_batch;
   const float rinv = 1.0f / (float)rpb;
   // 16-byte row chunks need 16-byte aligned rows
-  const bool vec_ok = ((g.out.ld | g.out.batch_stride) % VW == 0) && (((uintptr_t)g.C & 15) == 0) &&
+  const bool vec_ok = ((g.out.ld | g.out.batch_stride) % VW == 0) && (((uintptr_t)Cbase & 15) == 0) &&
                       (EPI != EPI_RESID || g.vec == nullptr || (g.vec_bstride % VW == 0 && ((uintptr_t)g.vec & 15) == 0)) &&
                       (EPI != EPI_BIAS || ((uintptr_t)g.vec & 15) == 0);
 #pragma unroll
@@ -187,7 +193,8 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
 #pragma unroll
     for (int p = 0; p < NSUB; ++p) {
       stage(mt, p, stg);
-      const int ncol0 = ncol_wave + p * 64;
+      // PART_SWIGLU's two sub-tiles are the W1 and W3 sums of the same 64 outputs
+      const int ncol0 = ncol_wave + (EPI == EPI_PART_SWIGLU ? 0 : p * 64);
       if constexpr (EPI == EPI_QKV) {
         // v columns: the 32 rows of the sub-tile are 32 consecutive tokens of one branch
         // (rows per branch are a multiple of 32); write them transposed into V^T, 8 keys per
@@ -218,6 +225,8 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
         }
       }
       constexpr int NIT = 32 * CPR / 64;
+      // PART_SWIGLU: the second sub-tile holds W3 sums, stored N columns further on
+      const int64_t cadd = (EPI == EPI_PART_SWIGLU && p == 1) ? (int64_t)g.N : 0;
       // addresses of this lane's chunks; all global loads are issued before any is used
       int64_t off[NIT];
       int nn[NIT], bq[NIT], rq[NIT];
@@ -232,7 +241,7 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
         const int rr = mm - bq[it] * rpb;
         rq[it] = rr;
         ok[it] = m < g.M && nn[it] < g.N && rr < g.out.valid[bq[it]];
-        off[it] = bq[it] * g.out.batch_stride + (int64_t)rr * g.out.ld + nn[it];
+        off[it] = bq[it] * g.out.batch_stride + (int64_t)rr * g.out.ld + nn[it] + cadd;
         full[it] = vec_ok && nn[it] + VW <= g.N;
       }
       if constexpr (EPI == EPI_RESID) {
@@ -244,7 +253,7 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (ok[it] && full[it]) x[it] = *(const float4*)((const float*)g.C + off[it]);
+          if (ok[it] && full[it]) x[it] = *(const float4*)((const float*)Cbase + off[it]);
         }
         const bool two = g.vec && rpb >= 32 && full[0];
         float4 g_lo = make_float4(1.f, 1.f, 1.f, 1.f), g_hi = g_lo;
@@ -258,7 +267,7 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
           const int c = it * 64 + lane, row = c / CPR, ch = c % CPR;
           const uint4 v = *(const uint4*)(stg + row * STRIDE + ch * 16);
           const float* vf = (const float*)&v;
-          float* C = (float*)g.C + off[it];
+          float* C = (float*)Cbase + off[it];
           if (full[it]) {
             float4 gv = bq[it] == bq[0] ? g_lo : g_hi;
             if (g.vec && !two) gv = *(const float4*)(g.vec + bq[it] * g.vec_bstride + nn[it]);
@@ -278,12 +287,20 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
           const int n = nn[it];
           if constexpr (EPI == EPI_BIAS) {
             const float* vf = (const float*)&v;
-            float* C = (float*)g.C + off[it];
+            float* C = (float*)Cbase + off[it];
             if (full[it]) {
               const float4 bi = *(const float4*)(g.vec + n);
               *(float4*)C = make_float4(vf[0] + bi.x, vf[1] + bi.y, vf[2] + bi.z, vf[3] + bi.w);
             } else {
               for (int e = 0; e < VW && n + e < g.N; ++e) C[e] = vf[e] + g.vec[n + e];
+            }
+          } else if constexpr (EpiFmt<EPI>::kPart) {
+            const float* vf = (const float*)&v;
+            float* C = (float*)Cbase + off[it];
+            if (full[it]) {
+              *(uint4*)C = v;
+            } else {
+              for (int e = 0; e < VW && n + e < g.N; ++e) C[e] = vf[e];
             }
           } else if constexpr (EPI == EPI_QKV) {
             // q / k columns (rows per branch, head dim and N are multiples of 8: always full)
@@ -293,9 +310,9 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
               const int64_t toff = b * g.rope_bstride + (int64_t)rr * 64 + ((n & 127) >> 1);
               y = rope_chunk(v, *(const float4*)(g.rope_cos + toff), *(const float4*)(g.rope_sin + toff));
             }
-            *(uint4*)((bf16*)g.C + off[it]) = y;
+            *(uint4*)((bf16*)Cbase + off[it]) = y;
           } else {
-            bf16* C = (bf16*)g.C + off[it];
+            bf16* C = (bf16*)Cbase + off[it];
             if (full[it]) {
               *(uint4*)C = v;
             } else {
@@ -314,11 +331,11 @@ __device__ __forceinline__ void epilogue_out(const GemmArgs& g, int m_wave, int 
 // this lane is C[4 (lane / 16) + r][lane % 16] within the tile.  For SwiGLU, B tiles j and j + 2
 // (j % 4 < 2) are the W1 and W3 rows of the same 16 outputs.
 template <int EPI, int NI>
-__device__ __forceinline__ void epilogue16(const GemmArgs& g, const f32x4 (&acc)[NI][8], int m_wave, int ncol_wave,
-                                           char* stg, int lane) {
+__device__ __forceinline__ void epilogue16(const GemmArgs& g, void* Cbase, const f32x4 (&acc)[NI][8], int m_wave,
+                                           int ncol_wave, char* stg, int lane) {
   const int c16 = lane & 15, q4 = lane >> 4;
   constexpr int ES = EpiFmt<EPI>::ES, STRIDE = EpiFmt<EPI>::STRIDE;
-  epilogue_out<EPI, NI / 2>(g, m_wave, ncol_wave, stg, lane, [&](int mt, int p, char* st) {
+  epilogue_out<EPI, NI / 2>(g, Cbase, m_wave, ncol_wave, stg, lane, [&](int mt, int p, char* st) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
 #pragma unroll
@@ -331,6 +348,10 @@ __device__ __forceinline__ void epilogue16(const GemmArgs& g, const f32x4 (&acc)
           if constexpr (EPI == EPI_SWIGLU) {
             const int j1 = (jj >> 1) * 4 + (jj & 1);
             *(bf16*)dst = (bf16)(silu_fast(acc[i][j1][r]) * acc[i][j1 + 2][r]);
+          } else if constexpr (EPI == EPI_PART_SWIGLU) {
+            // sub-tile 0: the W1 tiles (0, 1, 4, 5), sub-tile 1: the W3 tiles (2, 3, 6, 7)
+            const int j1 = (jj >> 1) * 4 + (jj & 1) + 2 * p;
+            *(float*)dst = acc[i][j1][r];
           } else if constexpr (EPI == EPI_STORE || EPI == EPI_QKV) {
             *(bf16*)dst = (bf16)acc[i][4 * p + jj][r];
           } else {
@@ -356,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, sw = wave & 3;   // group; the group's wave on SIMD sw
   const int wm = grp * 2 + (sw >> 1), wn = sw & 1;  // 64-row band, 128-column half
-  const int nout_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int nout_tile = kPaired<EPI> ? BN / 2 : BN;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + nout_tile - 1) / nout_tile;
   int tm, tn;
@@ -372,14 +393,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int brec = (int)min((int64_t)(g.N - n0) * g.ldb * 2, (int64_t)0x7fffffff);
   const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc((void*)B0, 0, brec, kBufFlags);
   __amdgpu_buffer_rsrc_t rb2_rs = rb_rs;
-  if constexpr (EPI == EPI_SWIGLU)
+  if constexpr (kPaired<EPI>)
     rb2_rs = __builtin_amdgcn_make_buffer_rsrc((void*)((const bf16*)g.B2 + (int64_t)n0 * g.ldb), 0, brec, kBufFlags);
 
   // Direct-to-LDS loads: group 0 fetches the A rows of a slab, group 1 the B rows, each wave
   // four 16-row blocks (1 KB each).  One instruction writes lane L at slot L of the block (row
   // L / 4, slot L % 4), so lane L fetches logical chunk (L % 4) ^ ((L / 16) % 4) of its row.
   // The row offset is in the per-lane (bounds-checked) offset; the K offset is scalar.
-  const int nk = g.K / BK;
+  // K range: the whole of K, or split blockIdx.y's range for the partial forms
+  const int k_begin = EpiFmt<EPI>::kPart ? (int)blockIdx.y * g.k_split : 0;
+  const int nk = (EpiFmt<EPI>::kPart ? min(g.K, k_begin + g.k_split) - k_begin : g.K) / BK;
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const int64_t ld = grp == 0 ? g.lda : g.ldb;
   int voff[DMA_PER_WAVE];
@@ -389,7 +412,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
     const int blk = sw * DMA_PER_WAVE + i;  // tile rows blk*16 .. blk*16+15
     int row = blk * 16;
     drs[i] = grp == 0 ? ra_rs : rb_rs;
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (kPaired<EPI>) {
       if (grp == 1) {
         // tile row t: wave column t / 128, MFMA tile (t % 128) / 32 (even: W1, odd: W3),
         // output column (t / 128) * 64 + (tile / 2) * 32 + t % 32
@@ -403,7 +426,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   const int dma_dst = (grp * BM + sw * DMA_PER_WAVE * 16) * 4;  // first chunk of this wave's blocks
 
   auto issue = [&](int kt, uint4* stage) {
-    const int kb = min(kt, nk - 1) * BK * 2;  // past the end: reload the last slab into a dead stage
+    // past the end: reload the last slab into a dead stage
+    const int kb = (k_begin + min(kt, nk - 1) * BK) * 2;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) lds_dma_16(drs[i], stage + dma_dst + i * 64, voff[i], kb);
   };
@@ -433,13 +457,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   // them), barrier.  Group 0's loads of slab kt+1 are complete after its compute phase of slab
   // kt, group 1's after its memory phase of slab kt; both before the barrier that precedes
   // group 0's reads of slab kt+1.
-#define ZDIT_SLAB(CUR, FREE, KT)                                   \
+#define ZDIT_SLAB(CUR, FREE, KT, MMA)                              \
   {                                                                \
     read_frags(CUR, arow, brow, fh, f);                            \
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                         \
     if (grp == 1) __builtin_amdgcn_s_waitcnt(kVmcntG1);            \
     barrier_fenced();                                              \
-    mma_slab(f, acc);                                              \
+    if (MMA) mma_slab(f, acc);                                     \
     issue((KT) + NST - 1, FREE);                                   \
     for (int q = 0; q < DMA_PER_WAVE; ++q) {                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);           \
@@ -450,17 +474,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
   }
 
   // Whole turns of the ring, then the remaining slabs.  (The loop body is branch-free, so the
-  // compiler sees every stage's last load exactly.)
-  int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    ZDIT_SLAB(st0, st3, kt)
-    ZDIT_SLAB(st1, st0, kt + 1)
-    ZDIT_SLAB(st2, st1, kt + 2)
-    ZDIT_SLAB(st3, st2, kt + 3)
+  // compiler sees every stage's last load exactly.)  Rows past M load as zero and are summed
+  // like the others: skipping the MFMAs of waves whose rows all lie past M (a separate loop
+  // copy for them) made the block's GEMMs 4-5 % slower on the same box, so they run as well.
+#define ZDIT_LOOP(MMA)                                             \
+  {                                                                \
+    int kt = 0;                                                    \
+    for (; kt + 4 <= nk; kt += 4) {                                \
+      ZDIT_SLAB(st0, st3, kt, MMA)                                 \
+      ZDIT_SLAB(st1, st0, kt + 1, MMA)                             \
+      ZDIT_SLAB(st2, st1, kt + 2, MMA)                             \
+      ZDIT_SLAB(st3, st2, kt + 3, MMA)                             \
+    }                                                              \
+    if (kt < nk) ZDIT_SLAB(st0, st3, kt, MMA)                      \
+    if (kt + 1 < nk) ZDIT_SLAB(st1, st0, kt + 1, MMA)              \
+    if (kt + 2 < nk) ZDIT_SLAB(st2, st1, kt + 2, MMA)              \
   }
-  if (kt < nk) ZDIT_SLAB(st0, st3, kt)
-  if (kt + 1 < nk) ZDIT_SLAB(st1, st0, kt + 1)
-  if (kt + 2 < nk) ZDIT_SLAB(st2, st1, kt + 2)
+  ZDIT_LOOP(true)
+#undef ZDIT_LOOP
 #undef ZDIT_SLAB
   // Loads of the slabs past the end are still landing in dead stages.  Once every wave has
   // drained its loads and passed this barrier, the LDS stages are free for the epilogue.
@@ -469,7 +500,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs g) {
 
   const int sidx = wave >> 1;
   char* const stg = (char*)(sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3) + (wave & 1) * 16384;
-  epilogue16<EPI, 4>(g, acc, m0 + wm * 64, n0 + wn * ((EPI == EPI_SWIGLU) ? 64 : 128), stg, lane);
+  // the partial forms write split blockIdx.y's plane [M][part_ld]
+  void* Cbase = EpiFmt<EPI>::kPart ? (void*)(g.part + (int64_t)blockIdx.y * g.M * g.part_ld) : g.C;
+  epilogue16<EPI, 4>(g, Cbase, acc, m0 + wm * 64, n0 + wn * (kPaired<EPI> ? 64 : 128), stg, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -555,6 +588,57 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+SplitPlan tile_split_plan(int epi, int N, int K) {
+  // About 160 workgroups per 256-row panel, at most 8 ranges and ranges of at least 16 slabs:
+  // more ranges spread a short branch's first (full) row panel over more CUs but write and read
+  // one more fp32 partial plane each (on the 256 px block, 256 workgroups per panel was slower
+  // than 128).  From N and K only, so a row's sums do not depend on M.
+  SplitPlan p;
+  const bool paired = epi == EPI_SWIGLU;
+  const int n_tiles = (N + (paired ? BN / 2 : BN) - 1) / (paired ? BN / 2 : BN);
+  const int max_splits = std::max(1, std::min(8, K / 512));
+  const int splits = std::min(max_splits, std::max(1, (160 + n_tiles / 2) / n_tiles));
+  p.k_split = ((K + splits - 1) / splits + BK - 1) / BK * BK;
+  p.splits = (K + p.k_split - 1) / p.k_split;
+  p.Nv = paired ? 2 * N : N;
+  return p;
+}
+
+size_t tile_split_workspace(int epi, int M, int N, int K) {
+  const SplitPlan p = tile_split_plan(epi, N, K);
+  return (size_t)p.splits * M * p.Nv * sizeof(float);
+}
+
+hipError_t launch_gemm_bf16_split(int epi, const GemmArgs& g, float* part, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SWIGLU) return hipErrorInvalidValue;
+  const SplitPlan p = tile_split_plan(epi, g.N, g.K);
+  GemmArgs pg = g;
+  pg.C = part;
+  pg.part = part;
+  pg.k_split = p.k_split;
+  pg.part_ld = p.Nv;
+  pg.out.rows_per_batch = g.M;
+  pg.out.batch_stride = 0;
+  pg.out.ld = p.Nv;
+  for (int b = 0; b < kMaxBatch; ++b) pg.out.valid[b] = g.M;
+  const bool paired = epi == EPI_SWIGLU;
+  const int nout_tile = paired ? BN / 2 : BN;
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + nout_tile - 1) / nout_tile);
+  dim3 grid(tiles, p.splits), block(512);
+  // one partial plane per split: the kernel offsets C by split * M * Nv itself
+  if (paired) hipLaunchKernelGGL(gemm_bf16_kernel<EPI_PART_SWIGLU>, grid, block, 0, s, pg);
+  else hipLaunchKernelGGL(gemm_bf16_kernel<EPI_PART>, grid, block, 0, s, pg);
+  if (hipError_t e = hipGetLastError()) return e;
+  SplitKArgs a{};
+  a.part = part;
+  a.M = g.M;
+  a.N = g.N;
+  a.Nv = p.Nv;
+  a.splits = p.splits;
+  return launch_splitk_reduce(epi, a, g, s);
 }
 
 hipError_t launch_gemm_f32(int epi, const GemmArgs& g, hipStream_t s) {

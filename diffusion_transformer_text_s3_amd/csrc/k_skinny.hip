@@ -399,6 +399,18 @@ size_t splitk_workspace(int epi, int M, int N, int K) {
   return (size_t)a.splits * M * a.Nv * sizeof(float);
 }
 
+hipError_t launch_splitk_reduce(int epi, const SplitKArgs& a, const GemmArgs& g, hipStream_t s) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  const unsigned rb = (unsigned)(((int64_t)a.M * (a.N / 4) + 255) / 256);
+  switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(rb), dim3(256), 0, s, a, g); break;
+    case EPI_RESID: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID>, dim3(rb), dim3(256), 0, s, a, g); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SWIGLU>, dim3(rb), dim3(256), 0, s, a, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows,
                               int a_phys_rows, const int* c_rows, const SplitKFuse* fuse) {
   if (g.M == 0 || g.N == 0) return hipSuccess;

@@ -114,9 +114,35 @@ zdit_status check_read(const Check& c, hipStream_t st, int* step, int* where) {
 }
 
 // ------------------------------------------------------------------ block workspace plan
+// Rows per branch up to which the block's four GEMMs split K into fp32 partials summed in a
+// fixed order (tile_split_plan): with a few hundred rows the 256 x 256 tiles would occupy a
+// small part of the chip (the 256 px and 512 px images, the caption refiners).  The choice
+// depends on the rows per branch and the split on N and K only, so a branch computed alone and
+// the same branch in a batch (or the shared image path and its per-branch copies) agree to the
+// bit.
+constexpr int kSplitRows = 512;
+
+bool use_split(const zdit_dims& d, int s) { return d.precision == ZDIT_BF16 && s <= kSplitRows; }
+
+// fp32 partial planes of the largest of the block's four split GEMMs at M rows
+size_t split_part_bytes(const zdit_dims& d, int M) {
+  const int D = d.dim, H = d.ffn_hidden;
+  size_t m = tile_split_workspace(EPI_STORE, M, 3 * D, D);
+  m = std::max(m, tile_split_workspace(EPI_RESID, M, D, D));
+  m = std::max(m, tile_split_workspace(EPI_SWIGLU, M, H, D));
+  m = std::max(m, tile_split_workspace(EPI_RESID, M, D, H));
+  return m;
+}
+
 struct BlockPlan {
-  size_t mod, chk, h, qkv, vt, o, u, total;
+  size_t mod, chk, part, h, qkv, vt, o, u, total;
 };
+
+// A GEMM of the block: the whole-K kernel, or the K-split one with partials in `part`.
+hipError_t block_gemm(const zdit_dims& d, bool split, int epi, const GemmArgs& g, void* part, hipStream_t st) {
+  if (split) return launch_gemm_bf16_split(epi, g, (float*)part, st);
+  return gemm(d.precision, epi, g, st);
+}
 
 // checkpoints of zdit_block_fwd: the input rows, the output rows
 constexpr int kBlockChecks = 2;
@@ -127,6 +153,7 @@ BlockPlan plan_block(const zdit_dims& d, int B, int s) {
   size_t off = 0;
   p.mod = off; off += al256((size_t)B * 6 * d.dim * 4);
   p.chk = off; off += check_bytes(kBlockChecks);
+  p.part = off; off += use_split(d, s) ? al256(split_part_bytes(d, (int)M)) : 0;
   p.h = off;   off += al256(M * d.dim * ab);
   const size_t r0 = off;
   p.qkv = off; off += al256(M * 3 * d.dim * ab);
@@ -145,7 +172,7 @@ BlockPlan plan_block(const zdit_dims& d, int B, int s) {
 // stores q, k, v and separate kernels rotate and transpose.  The results are bit-identical.
 zdit_status qkv_attention(int P, int nh, int B, int s, const int* seq_len, const void* h, const void* w_qkv,
                           void* qkv, void* vt, void* o, const float* cosT, const float* sinT,
-                          int64_t tab_bstride, hipStream_t st) {
+                          int64_t tab_bstride, hipStream_t st, void* part = nullptr) {
   const int D = nh * kHeadDim, M = B * s;
   AttnArgs aa{};
   aa.qkv = qkv; aa.vt = vt; aa.out = o; aa.batch = B; aa.s_max = s; aa.s_pad = round_up(s, 64);
@@ -154,7 +181,7 @@ zdit_status qkv_attention(int P, int nh, int B, int s, const int* seq_len, const
 
   GemmArgs g{};
   g.A = h; g.B = w_qkv; g.C = qkv; g.M = M; g.N = 3 * D; g.K = D; g.lda = D; g.ldb = D;
-  if (P == ZDIT_BF16 && s % 32 == 0) {
+  if (P == ZDIT_BF16 && s % 32 == 0 && !part) {
     g.out.rows_per_batch = s; g.out.batch_stride = (int64_t)s * 3 * D; g.out.ld = 3 * D;
     for (int b = 0; b < kMaxBatch; ++b) { g.out.valid[b] = b < B ? s : 0; g.seq[b] = b < B ? seq_len[b] : 0; }
     g.rope_cos = cosT; g.rope_sin = sinT; g.rope_bstride = tab_bstride;
@@ -164,7 +191,8 @@ zdit_status qkv_attention(int P, int nh, int B, int s, const int* seq_len, const
     aa.vt_ready = 1;
   } else {
     g.out = compact_rows(M, 3LL * D);
-    HIP_TRY(gemm(P, EPI_STORE, g, st));
+    if (part) HIP_TRY(launch_gemm_bf16_split(EPI_STORE, g, (float*)part, st));
+    else HIP_TRY(gemm(P, EPI_STORE, g, st));
     RopeArgs ra;
     ra.qkv = qkv; ra.cos = cosT; ra.sin = sinT; ra.tab_bstride = tab_bstride;
     ra.batch = B; ra.s_max = s; ra.n_heads = nh;
@@ -183,6 +211,8 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
                           hipStream_t st) {
   const int P = d.precision, D = d.dim, H = d.ffn_hidden, M = B * s;
   const BlockPlan pl = plan_block(d, B, s);
+  const bool split = use_split(d, s);
+  void* part = split ? ws + pl.part : nullptr;
   void* h = ws + pl.h;
   void* qkv = ws + pl.qkv;
   void* vt = ws + pl.vt;
@@ -199,7 +229,7 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
 
   {
     const zdit_status rc = qkv_attention(P, d.n_heads, B, s, seq_len, h, w.w_qkv, qkv, vt, o, cosT, sinT,
-                                         tab_bstride, st);
+                                         tab_bstride, st, part);
     if (rc != ZDIT_OK) return rc;
   }
 
@@ -210,7 +240,7 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
   GemmArgs g{};
   g.A = o; g.B = w.w_out; g.C = x; g.M = M; g.N = D; g.K = D; g.lda = D; g.ldb = D;
   g.vec = mod ? mod + 2LL * D : nullptr; g.vec_bstride = 6LL * D; g.out = xr;
-  HIP_TRY(gemm(P, EPI_RESID, g, st));
+  HIP_TRY(block_gemm(d, split, EPI_RESID, g, part, st));
 
   na.gain = w.norm2;
   na.shift = mod ? mod + 3LL * D : nullptr; na.scale = mod ? mod + 4LL * D : nullptr;
@@ -219,12 +249,12 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
   g = GemmArgs{};
   g.A = h; g.B = w.w1; g.B2 = w.w3; g.C = u; g.M = M; g.N = H; g.K = D; g.lda = D; g.ldb = D;
   g.out = compact_rows(M, H);
-  HIP_TRY(gemm(P, EPI_SWIGLU, g, st));
+  HIP_TRY(block_gemm(d, split, EPI_SWIGLU, g, part, st));
 
   g = GemmArgs{};
   g.A = u; g.B = w.w2; g.C = x; g.M = M; g.N = D; g.K = H; g.lda = H; g.ldb = H;
   g.vec = mod ? mod + 5LL * D : nullptr; g.vec_bstride = 6LL * D; g.out = xr;
-  HIP_TRY(gemm(P, EPI_RESID, g, st));
+  HIP_TRY(block_gemm(d, split, EPI_RESID, g, part, st));
   return ZDIT_OK;
 }
 
@@ -773,6 +803,34 @@ zdit_status zdit_op_gemm(int32_t precision, int32_t epilogue, int32_t M, int32_t
   g.M = M; g.N = N; g.K = K; g.lda = K; g.ldb = K;
   g.out = compact_rows(M, N);
   HIP_TRY(gemm(precision, epilogue, g, (hipStream_t)hip_stream));
+  return ok();
+}
+
+size_t zdit_op_gemm_ksplit_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K) {
+  if ((epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU) || M < 1 ||
+      M > (1 << 24) || N < 8 || N % 8 || K < 64 || K % 64)
+    return 0;
+  return al256(tile_split_workspace(epilogue, M, N, K));
+}
+
+zdit_status zdit_op_gemm_ksplit(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                                const void* B2, const float* vec, void* C, void* ws, size_t ws_bytes,
+                                void* hip_stream) {
+  if (epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU)
+    return fail(ZDIT_EUNSUPPORTED, "epilogue %d (STORE, RESID or SWIGLU)", epilogue);
+  if (M < 0 || N < 1 || K < 1) return fail(ZDIT_EINVAL, "M %d N %d K %d", M, N, K);
+  if (M > (1 << 24) || N % 8 || K % 64) return fail(ZDIT_EUNSUPPORTED, "M %d / N %d / K %d", M, N, K);
+  if (!A || !B || !C || (epilogue == ZDIT_EPI_SWIGLU && !B2)) return fail(ZDIT_EINVAL, "NULL operand");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (B2 && !aligned16(B2)) || (vec && !aligned16(vec)))
+    return fail(ZDIT_EINVAL, "operand not 16-byte aligned");
+  if (M == 0) return ok();
+  if (!ws || !aligned16(ws) || ws_bytes < zdit_op_gemm_ksplit_workspace(epilogue, M, N, K))
+    return fail(ZDIT_EWORKSPACE, "workspace too small");
+  GemmArgs g{};
+  g.A = A; g.B = B; g.B2 = B2; g.C = C; g.vec = vec; g.vec_bstride = 0;
+  g.M = M; g.N = N; g.K = K; g.lda = K; g.ldb = K;
+  g.out = compact_rows(M, N);
+  HIP_TRY(launch_gemm_bf16_split(epilogue, g, (float*)ws, (hipStream_t)hip_stream));
   return ok();
 }
 

@@ -130,7 +130,8 @@ zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t
  * the workspace replaced by a scratch array the library holds on each device (128 MiB, placed
  * when the library's code loads on that device and kept until the process ends).  Calls
  * zdit_block_fwd would accept whose zdit_block_workspace() exceeds 128 MiB return
- * ZDIT_EUNSUPPORTED (the 256 px and 512 px pairs fit; the 1024^2 pair needs a workspace).  All
+ * ZDIT_EUNSUPPORTED (a 256 px branch and the 512 px pair fit; the 256 px pair, whose K-split
+ * GEMMs keep ~105 MB of partial products, and the 1024^2 pair need a workspace).  All
  * calls on one device share its scratch: calls that overlap on one device (other streams,
  * other threads) race and must be ordered by the caller.  No allocation, no free, no host
  * copy (except the ZDIT_CHECK_FINITE read-back). */
@@ -283,6 +284,17 @@ enum { ZDIT_EPI_STORE = 0, ZDIT_EPI_BIAS = 1, ZDIT_EPI_RESID = 2, ZDIT_EPI_SWIGL
 zdit_status zdit_op_gemm(int32_t precision, int32_t epilogue, int32_t M, int32_t N, int32_t K,
                          const void* A, const void* B, const void* B2, const float* vec,
                          void* C, void* hip_stream);
+
+/* The same contraction split over K, as the block runs its GEMMs for branches of at most 512
+ * rows (bf16 only; epilogues ZDIT_EPI_STORE, ZDIT_EPI_RESID, ZDIT_EPI_SWIGLU): K is cut into
+ * ranges chosen from N and K alone, the 256 x 256-tile kernel writes each range's fp32 partial
+ * product to the workspace, and a second kernel sums the ranges in order and applies the
+ * epilogue, so a row's result does not depend on M.  K % 64 == 0, N % 8 == 0; ws:
+ * zdit_op_gemm_ksplit_workspace() bytes (0 for a shape or epilogue this form rejects). */
+size_t zdit_op_gemm_ksplit_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K);
+zdit_status zdit_op_gemm_ksplit(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
+                                const void* B, const void* B2, const float* vec, void* C, void* ws,
+                                size_t ws_bytes, void* hip_stream);
 
 /* RMSNorm + modulation: out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * gain * (1 + scale) +
  * shift over `rows` rows of `dim`; x fp32, gain/shift/scale fp32 [dim] (shift/scale NULL:

@@ -146,6 +146,24 @@ def test_op_entry_points_reject_misaligned_pointers():
     assert rc == Z.ZDIT_EINVAL and "aligned" in Z.last_error()
 
 
+def test_ksplit_gemm_validates_before_launch():
+    L = Z.lib()
+    p = _fake()
+    assert Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_BIAS, 10, 64, 64) == 0
+    assert Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_STORE, 10, 60, 64) == 0
+    assert Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_STORE, 10, 64, 96) == 0
+    w1 = Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_STORE, 10, 3840, 10240)
+    w2 = Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_STORE, 20, 3840, 10240)
+    assert w1 > 0 and w2 >= 2 * w1 - 256  # partial planes grow with M, the split does not
+    assert Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_SWIGLU, 10, 3840, 10240) > 0
+    rc = L.zdit_op_gemm_ksplit(Z.ZDIT_EPI_BIAS, 4, 64, 64, p, p, None, p, p, p, 1 << 20, None)
+    assert rc == Z.ZDIT_EUNSUPPORTED
+    rc = L.zdit_op_gemm_ksplit(Z.ZDIT_EPI_SWIGLU, 4, 64, 64, p, p, None, None, p, p, 1 << 20, None)
+    assert rc == Z.ZDIT_EINVAL
+    rc = L.zdit_op_gemm_ksplit(Z.ZDIT_EPI_STORE, 4, 64, 64, p, p, None, None, p, p, 16, None)
+    assert rc == Z.ZDIT_EWORKSPACE
+
+
 def test_fused_qkv_attn_validates_before_launch():
     L = Z.lib()
     p = _fake()

@@ -91,6 +91,73 @@ def _check_swiglu(got, A, B, B2):
     assert_bf16_result(got, u, err)
 
 
+def _ksplit(epi, M, N, K, A, B, B2, vec, C):
+    ws = Z.workspace(Z.zdit_op_gemm_ksplit_workspace(epi, M, N, K))
+    Z.zdit_op_gemm_ksplit(epi, M, N, K, dev(A, torch.bfloat16), dev(B, torch.bfloat16),
+                          None if B2 is None else dev(B2, torch.bfloat16), None if vec is None else dev(vec), C, ws)
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 520, 192), (320, 3840, 3840), (640, 1032, 1280), (300, 11520, 3840)])
+def test_gemm_ksplit_store_and_resid(M, N, K):
+    """The K-split form of the block GEMMs (branches of <= 512 rows): fp32 partial products over
+    K ranges summed in order, then the epilogue; within the same fp32 accumulation bound."""
+    note(f"gemm K-split STORE / RESID M={M} N={N} K={K}")
+    A, B, _ = _gemm_inputs(M, N, K, 30)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bound = np.abs(A).astype(np.float64) @ np.abs(B).astype(np.float64).T
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _ksplit(Z.ZDIT_EPI_STORE, M, N, K, A, B, None, None, C)
+    assert_bf16_result(host(C), ref, 2e-6 * bound)
+    g = _rng(31)
+    C0 = (100 * g.standard_normal((M, N))).astype(np.float32)
+    gate = g.standard_normal(N).astype(np.float32)
+    C = dev(C0)
+    _ksplit(Z.ZDIT_EPI_RESID, M, N, K, A, B, None, gate, C)
+    r = C0 + gate * ref
+    assert np.all(np.abs(host(C) - r) <= 2e-6 * np.abs(gate) * bound + 1e-6 * np.abs(C0) + 1e-6)
+
+
+@pytest.mark.parametrize("M,N,K", [(77, 384, 256), (320, 10240, 3840)])
+def test_gemm_ksplit_swiglu(M, N, K):
+    note(f"gemm K-split SWIGLU M={M} N={N} K={K}")
+    A, B, B2 = _gemm_inputs(M, N, K, 32, two_b=True)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _ksplit(Z.ZDIT_EPI_SWIGLU, M, N, K, A, B, B2, None, C)
+    _check_swiglu(host(C), A.astype(np.float64), B.astype(np.float64), B2.astype(np.float64))
+
+
+def test_gemm_ksplit_rows_do_not_depend_on_m():
+    """The K ranges depend on N and K only: rows computed among 40 or 600 rows are identical,
+    and rows past the first 256-row panel (where the last panel's empty row groups skip their
+    MFMAs) too."""
+    N, K = 3840, 10240
+    note("gemm K-split rows independent of M")
+    A, B, _ = _gemm_inputs(600, N, K, 33)
+    outs = {}
+    for M in (600, 40, 300):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        _ksplit(Z.ZDIT_EPI_STORE, M, N, K, A[:M], B, None, None, C)
+        outs[M] = host(C)
+    np.testing.assert_array_equal(outs[600][:40], outs[40])
+    np.testing.assert_array_equal(outs[600][:300], outs[300])
+
+
+def test_gemm_whole_k_rows_do_not_depend_on_m():
+    """The whole-K kernel: rows in a last panel whose lower row groups are empty (and skip their
+    MFMAs) equal the same rows computed in a full panel."""
+    N, K = 1024, 768
+    note("gemm whole-K rows independent of M (empty row groups)")
+    A, B, _ = _gemm_inputs(512, N, K, 34)
+    outs = {}
+    for M in (512, 300, 257, 100):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        Z.zdit_op_gemm(BF, Z.ZDIT_EPI_STORE, M, N, K, dev(A[:M], torch.bfloat16), dev(B, torch.bfloat16), None,
+                       None, C)
+        outs[M] = host(C)
+    for M in (300, 257, 100):
+        np.testing.assert_array_equal(outs[512][:M], outs[M])
+
+
 @pytest.mark.parametrize("epi", [Z.ZDIT_EPI_STORE, Z.ZDIT_EPI_BIAS, Z.ZDIT_EPI_RESID, Z.ZDIT_EPI_SWIGLU])
 def test_gemm_fp32_debug(epi):
     M, N, K = 100, 130, 72

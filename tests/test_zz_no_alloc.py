@@ -1,7 +1,8 @@
 """zdit_block_fwd_noalloc (the block forward in the library's own per-device scratch, for callers
 that cannot allocate) against zdit_block_fwd with a caller workspace: bit-identical outputs on
-two calls in a row, the second on a smaller input, so stale scratch contents from the first call
-must not matter; a shape whose workspace exceeds the scratch is rejected before anything runs."""
+calls in a row, each on a smaller input than the one before, so stale scratch contents from the
+previous call must not matter; a shape whose workspace exceeds the scratch is rejected before
+anything runs."""
 import numpy as np
 import pytest
 import torch
@@ -41,20 +42,26 @@ def _both(case, flags=0):
     return host(xa), host(xb)
 
 
-def test_noalloc_matches_workspace_entry_two_calls_second_smaller():
-    # call 1: full width, 256 px cond/uncond pair (S = 320 / 288), residual outliers at 6.7e3
-    note("noalloc block: full-width 256 px pair, then a tiny block")
-    big = _case(synth.FULL, 2, 16, 16, [45, 10], 98, outliers=0.001)
-    a, b = _both(big)
-    np.testing.assert_array_equal(b, a)
-    for br in range(2):
-        n = big["S"][br]
-        cs, sn = O.rope_tables(O.position_ids("joint", 16, 16, big["ncs"][br]))
-        ref = O.block(big["x"][br, :n], big["w"], O.block_mod(big["c"][br], big["w"]), cs, sn, big["dims"])
-        assert rel_l2(b[br, :n] - big["x"][br, :n], ref - big["x"][br, :n]) <= 1e-2
-        np.testing.assert_array_equal(b[br, n:], big["x"][br, n:])
-    # call 2: a smaller input on the scratch the first call left behind
-    small = _case(synth.TINY, 1, 8, 8, [20], 99)
+def _oracle_update(case, br):
+    n = case["S"][br]
+    cs, sn = O.rope_tables(O.position_ids("joint", case["gh"], case["gw"], case["ncs"][br]))
+    ref = O.block(case["x"][br, :n], case["w"], O.block_mod(case["c"][br], case["w"]), cs, sn, case["dims"])
+    return ref - case["x"][br, :n]
+
+
+def test_noalloc_matches_workspace_entry_calls_getting_smaller():
+    """Three calls in a row, each smaller than the one before, on the scratch the previous one
+    left behind: a full-width 512 px branch (S = 1088, whole-K GEMMs), a full-width 256 px branch
+    (S = 320, K-split GEMMs) and a tiny block."""
+    note("noalloc block: full-width 512 px, then 256 px, then a tiny block")
+    for case in (_case(synth.FULL, 1, 32, 32, [45], 98, outliers=0.001),
+                 _case(synth.FULL, 1, 16, 16, [45], 99, outliers=0.001)):
+        a, b = _both(case)
+        np.testing.assert_array_equal(b, a)
+        n = case["S"][0]
+        assert rel_l2(b[0, :n] - case["x"][0, :n], _oracle_update(case, 0)) <= 1e-2
+        np.testing.assert_array_equal(b[0, n:], case["x"][0, n:])
+    small = _case(synth.TINY, 1, 8, 8, [20], 97)
     a, b = _both(small)
     np.testing.assert_array_equal(b, a)
     # and with the non-finite check on
@@ -63,7 +70,8 @@ def test_noalloc_matches_workspace_entry_two_calls_second_smaller():
 
 
 def test_noalloc_rejects_shapes_beyond_its_scratch():
-    """The 1024^2 pair needs ~390 MB of workspace: rejected, x untouched."""
+    """The 1024^2 pair needs ~390 MB of workspace: rejected, x untouched (so is the 256 px pair,
+    whose K-split GEMMs keep ~105 MB of fp32 partial products)."""
     note("noalloc block: 1024^2 pair rejected")
     dims = synth.FULL
     d = Z.make_dims(dims)
@@ -77,3 +85,4 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
         Z.zdit_block_fwd_noalloc(d, blk, 2, 4160, [4160, 4128], x, c, cos, sin)
     assert e.value.code == Z.ZDIT_EUNSUPPORTED and "scratch" in str(e.value)
     assert bool((x == 3.0).all())
+    assert Z.zdit_block_workspace(d, 2, 320) > (128 << 20)
