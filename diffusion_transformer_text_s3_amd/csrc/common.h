@@ -198,12 +198,17 @@ hipError_t launch_qknorm_rope(const QkNormRopeArgs& a, hipStream_t s);
 
 // out[b][r][:] = table[ids[b * s_max + r]][:] (bf16 table, fp32 out) for r < len[b], 0 for
 // r >= len[b] (ids there are not read).  dim a multiple of 8.
+// Ids of at most kInlineIds tokens (batch * s_max) travel in the kernel arguments (n_inline > 0),
+// so the call makes no host-to-device copy; otherwise they are read from `ids` (device).
+constexpr int kInlineIds = 512;
 struct EmbedArgs {
   const int* ids;
   const void* table;
   float* out;
   int batch, s_max, dim;
   int len[kMaxBatch];
+  int n_inline;
+  int inline_ids[kInlineIds];
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 

@@ -208,12 +208,25 @@ zdit_status enc_block(const zdit_enc_cfg& c, const zdit_enc_layer_w& w, int B, i
   return ZDIT_OK;
 }
 
-// ids (host) -> workspace, then the embedding gather into out
+// The embedding gather of the host ids into out: up to kInlineIds tokens the ids ride in the
+// kernel arguments (no copy, so the call can be captured into a graph), more are copied into
+// the workspace first.
 zdit_status embed_rows(int B, int L, int dim, const int32_t* ids, const int32_t* len, const void* table,
                        float* out, int* ids_dev, hipStream_t st) {
-  HIP_TRY(hipMemcpyAsync(ids_dev, ids, (size_t)B * L * sizeof(int32_t), hipMemcpyHostToDevice, st));
   EmbedArgs ea;
-  ea.ids = ids_dev; ea.table = table; ea.out = out; ea.batch = B; ea.s_max = L; ea.dim = dim;
+  const int64_t n = (int64_t)B * L;
+  ea.n_inline = n <= kInlineIds ? (int)n : 0;
+  if (ea.n_inline) {
+    for (int64_t i = 0; i < n; ++i) {
+      const int r = (int)(i % L);
+      ea.inline_ids[i] = r < len[i / L] ? ids[i] : 0;  // only valid rows' ids are read
+    }
+    ea.ids = nullptr;
+  } else {
+    HIP_TRY(hipMemcpyAsync(ids_dev, ids, (size_t)n * sizeof(int32_t), hipMemcpyHostToDevice, st));
+    ea.ids = ids_dev;
+  }
+  ea.table = table; ea.out = out; ea.batch = B; ea.s_max = L; ea.dim = dim;
   for (int b = 0; b < kMaxBatch; ++b) ea.len[b] = b < B ? len[b] : 0;
   HIP_TRY(launch_embed(ea, st));
   return ZDIT_OK;

@@ -20,7 +20,8 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   float* o = a.out + ((int64_t)b * a.s_max + r) * a.dim + c * 8;
   float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
   if (r < a.len[b]) {
-    const int id = a.ids[(int64_t)b * a.s_max + r];
+    const int64_t k = (int64_t)b * a.s_max + r;
+    const int id = a.n_inline ? a.inline_ids[k] : a.ids[k];
     const uint4 v = *(const uint4*)((const bf16*)a.table + (int64_t)id * a.dim + c * 8);
     // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 pattern
     lo = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),

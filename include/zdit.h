@@ -20,9 +20,10 @@
  *     a fixed scratch array the library's code object holds on each device).
  *   - All device work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream).
  *     Nothing synchronises; no host<->device copy is made, except that the text-encoder
- *     calls copy the host token ids into their workspace (the host array may be reused as
- *     soon as the call returns), and that calls with ZDIT_CHECK_FINITE set read their
- *     verdict back (see below).
+ *     calls with more than 512 tokens (batch * max_len) copy the host token ids into their
+ *     workspace (up to 512 they travel in the kernel arguments; either way the host array may
+ *     be reused as soon as the call returns), and that calls with ZDIT_CHECK_FINITE set read
+ *     their verdict back (see below).
  *   - Arguments are validated before anything is enqueued.  On error nothing runs, outputs
  *     are untouched, the return value is negative and zdit_last_error() says why.  Faults
  *     during execution surface at the caller's next synchronisation, as in any HIP library.

@@ -347,6 +347,22 @@ def test_encoder_valid_rows_do_not_depend_on_padding_length():
     assert np.all(b[:, 33:] == 0)
 
 
+def test_encoder_ids_inline_and_copied_paths_agree():
+    """Up to 512 tokens (batch x max_len) the ids travel in the kernel arguments, beyond that they
+    are copied into the workspace: the valid rows are bit-identical either way (both shapes run
+    the main-GEMM projections) and match the oracle."""
+    ed = synth.ENC_TINY
+    lens = [250, 31]
+    note("encoder ids inline (2 x 256) vs copied (2 x 300)")
+    W = synth.encoder_weights(ed, 17, ed.n_layers - 1)
+    ids = synth.token_ids(2, 256, lens, ed.vocab, 18)
+    a = _encoder_run(ed, W, ids, lens)                # 512 tokens: inline
+    b = _encoder_run(ed, W, ids, lens, max_len=300)   # 600 tokens: copied
+    for i, L in enumerate(lens):
+        np.testing.assert_array_equal(a[i, :L], b[i, :L])
+    _check_vs_oracle(a, E.encoder_penultimate(ids, lens, W, ed), lens)
+
+
 def test_encoder_is_causal_bit_exact():
     ed = synth.ENC_TINY
     note("encoder causality")
