@@ -325,3 +325,93 @@ def token_ids(batch: int, max_len: int, lengths, vocab: int, seed: int) -> np.nd
     for b, L in enumerate(lengths):
         ids[b, L:] = 0
     return ids.astype(np.int32)
+
+
+# ----------------------------------------------------------------------------- VAE decoder
+_T_VAE = 9
+
+
+@dataclass(frozen=True)
+class VaeDims:
+    """The 16-channel AutoencoderKL decoder.  Core AI model zoo, "Z-Image-Turbo port", table
+    "Architecture -> export mapping", row VAE, gives the latent width, fp32 and the unscale
+    constants; the stage widths (given in encoder order, the decoder walks them reversed),
+    three ResNet blocks per decoder stage and 32 norm groups are the published configuration
+    of the 16-channel autoencoder with those constants (a reading, not on the pages)."""
+    latent_ch: int = 16
+    out_ch: int = 3
+    widths: tuple = (128, 256, 512, 512)
+    resnets: int = 3
+    groups: int = 32
+    eps: float = 1e-6
+    scale: float = 0.3611
+    shift: float = 0.1159
+
+    def replace(self, **kw) -> "VaeDims":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def stages(self):
+        """Decoder stages in order: (input width, output width, upsample after)."""
+        rev = list(reversed(self.widths))
+        out, cin = [], rev[0]
+        for i, c in enumerate(rev):
+            out.append((cin, c, i < len(rev) - 1))
+            cin = c
+        return out
+
+
+VAE_FULL = VaeDims()
+VAE_TINY = VaeDims(widths=(32, 32, 64, 64))
+
+
+def vae_weights(vd: VaeDims, seed: int) -> dict:
+    """Weights of the decoder as fp32 arrays, convolutions [out, in, kh, kw], linear maps
+    [out, in].  Convolutions draw N(0, 1/fan_in) (the second conv of each ResNet block
+    N(0, 0.25/fan_in), so the residual stream grows slowly); norm gains 1 + 0.1 N(0,1),
+    norm shifts and biases 0.05 N(0,1).  Keys: conv_in, mid.res0, mid.attn, mid.res1,
+    up{i}.res{j}, up{i}.upconv (stages 0..2), norm_out, conv_out."""
+    idx = [0]
+
+    def nxt():
+        idx[0] += 1
+        return rng(seed, _T_VAE, idx[0])
+
+    def conv(o, i, k, gain=1.0):
+        return _normal(nxt(), (o, i, k, k), float(np.sqrt(gain / (i * k * k))))
+
+    def vec(n, base=0.0, std=0.05):
+        return (np.float32(base) + _normal(nxt(), (n,), std)).astype(np.float32)
+
+    W = {}
+
+    def resnet(p, cin, cout):
+        W[p + ".gn1.g"], W[p + ".gn1.b"] = vec(cin, 1.0, 0.1), vec(cin)
+        W[p + ".conv1.w"], W[p + ".conv1.b"] = conv(cout, cin, 3), vec(cout)
+        W[p + ".gn2.g"], W[p + ".gn2.b"] = vec(cout, 1.0, 0.1), vec(cout)
+        W[p + ".conv2.w"], W[p + ".conv2.b"] = conv(cout, cout, 3, 0.25), vec(cout)
+        if cin != cout:
+            W[p + ".short.w"], W[p + ".short.b"] = conv(cout, cin, 1), vec(cout)
+
+    c0 = vd.widths[-1]
+    W["conv_in.w"], W["conv_in.b"] = conv(c0, vd.latent_ch, 3), vec(c0)
+    resnet("mid.res0", c0, c0)
+    W["mid.attn.gn.g"], W["mid.attn.gn.b"] = vec(c0, 1.0, 0.1), vec(c0)
+    for n in "qkvo":
+        W[f"mid.attn.{n}.w"] = _normal(nxt(), (c0, c0), float(np.sqrt(1.0 / c0)))
+        W[f"mid.attn.{n}.b"] = vec(c0)
+    resnet("mid.res1", c0, c0)
+    for i, (cin, c, up) in enumerate(vd.stages):
+        for j in range(vd.resnets):
+            resnet(f"up{i}.res{j}", cin if j == 0 else c, c)
+        if up:
+            W[f"up{i}.upconv.w"], W[f"up{i}.upconv.b"] = conv(c, c, 3), vec(c)
+    cl = vd.widths[0]
+    W["norm_out.g"], W["norm_out.b"] = vec(cl, 1.0, 0.1), vec(cl)
+    W["conv_out.w"], W["conv_out.b"] = conv(vd.out_ch, cl, 3), vec(vd.out_ch)
+    return W
+
+
+def vae_activations(shape, seed: int, index: int = 0, std: float = 1.0) -> np.ndarray:
+    """A seeded N(0, std^2) fp32 activation tensor (inputs of single-layer tests)."""
+    return _normal(rng(seed, _T_VAE, 100000 + index), shape, std)

@@ -66,6 +66,37 @@ ENC_MUTATIONS = {
 }
 
 
+# planted in oracle/vae_oracle.py, caught by tests/test_vae_oracle_pins.py
+VAE_MUTATIONS = {
+    "convolution instead of correlation": ("tap = w[:, :, i, j].astype(x.dtype)", "tap = w[:, :, k - 1 - i, k - 1 - j].astype(x.dtype)"),
+    "no zero padding (wrap around)": ("win = xp[:, :, i:i + H, j:j + Wd]",
+                                      "win = np.roll(np.roll(x, p - i, axis=2), p - j, axis=3)"),
+    "conv bias dropped": ("return out + b.astype(x.dtype)[None, :, None, None]", "return out"),
+    "GroupNorm groups strided": ("xg = x.reshape(B, groups, C // groups, H, Wd)",
+                                 "xg = x.reshape(B, C // groups, groups, H, Wd).transpose(0, 2, 1, 3, 4)"),
+    "GroupNorm statistics over the batch": ("mean = xg.mean(axis=(2, 3, 4), keepdims=True)",
+                                            "mean = xg.mean(axis=(0, 2, 3, 4), keepdims=True)"),
+    "GroupNorm eps outside the root": ("np.sqrt(var + x.dtype.type(eps))", "(np.sqrt(var) + x.dtype.type(eps))"),
+    "SiLU dropped before conv1": ('h = conv2d(silu(group_norm(x, W[p + ".gn1.g"]', 'h = conv2d((group_norm(x, W[p + ".gn1.g"]'),
+    "ResNet norms swapped": ('group_norm(h, W[p + ".gn2.g"], W[p + ".gn2.b"]', 'group_norm(h, W[p + ".gn1.g"], W[p + ".gn1.b"]'),
+    "no shortcut": ("    return s + h\n", "    return h\n"),
+    "upsample by interleaving channels": ("return np.repeat(np.repeat(x, 2, axis=2), 2, axis=3)",
+                                          "return np.tile(x, (1, 1, 2, 2))"),
+    "upsample after the conv": ("x = conv2d(upsample_nearest(x), W[f\"up{i}.upconv.w\"], W[f\"up{i}.upconv.b\"])",
+                                "x = upsample_nearest(conv2d(x, W[f\"up{i}.upconv.w\"], W[f\"up{i}.upconv.b\"]))"),
+    "attention without 1/sqrt(C)": ("s = (q[n] @ k[n].T) / dt.type(math.sqrt(C))", "s = (q[n] @ k[n].T)"),
+    "attention q and k swapped with v": ('q, k, v = lin(t, "q"), lin(t, "k"), lin(t, "v")',
+                                         'q, k, v = lin(t, "q"), lin(t, "v"), lin(t, "k")'),
+    "attention softmax over queries": ("out[n] = (e / e.sum(axis=1, keepdims=True)) @ v[n]",
+                                       "out[n] = (e / e.sum(axis=0, keepdims=True)) @ v[n]"),
+    "attention residual dropped": ("return x + o.transpose(0, 2, 1).reshape(B, C, H, Wd)",
+                                   "return o.transpose(0, 2, 1).reshape(B, C, H, Wd)"),
+    "unscale inverted": ("return z / z.dtype.type(scale) + z.dtype.type(shift)",
+                         "return (z - z.dtype.type(shift)) * z.dtype.type(scale)"),
+    "no SiLU before conv_out": ('x = silu(group_norm(x, W["norm_out.g"]', 'x = (group_norm(x, W["norm_out.g"]'),
+}
+
+
 @pytest.fixture(scope="module")
 def sandbox(tmp_path_factory):
     d = tmp_path_factory.mktemp("oracle_mut")
@@ -74,7 +105,7 @@ def sandbox(tmp_path_factory):
                         ignore=shutil.ignore_patterns("__pycache__"))
     os.makedirs(os.path.join(d, "tests"))
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(d, "tests", "golden"))
-    for f in ("conftest.py", "test_oracle_pins.py", "test_encoder_oracle_pins.py"):
+    for f in ("conftest.py", "test_oracle_pins.py", "test_encoder_oracle_pins.py", "test_vae_oracle_pins.py"):
         shutil.copy(os.path.join(ROOT, "tests", f), os.path.join(d, "tests", f))
     return str(d)
 
@@ -100,7 +131,7 @@ def test_pins_catch_planted_mistake(sandbox, name):
 
 def test_sandbox_copy_passes_unmutated(sandbox):
     """The unmutated sandbox passes both pin files, so a failure below is the mutation's."""
-    for f in ("tests/test_oracle_pins.py", "tests/test_encoder_oracle_pins.py"):
+    for f in ("tests/test_oracle_pins.py", "tests/test_encoder_oracle_pins.py", "tests/test_vae_oracle_pins.py"):
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", f],
                            cwd=sandbox, capture_output=True, text=True, timeout=300)
         assert r.returncode == 0, r.stdout[-2000:]
@@ -118,6 +149,25 @@ def test_encoder_pins_catch_planted_mistake(sandbox, name):
             f.write(src.replace(a, b, 1))
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                             "tests/test_encoder_oracle_pins.py"], cwd=sandbox, capture_output=True,
+                           text=True, timeout=300)
+    finally:
+        with open(dst, "w") as f:
+            f.write(src)
+    assert r.returncode != 0, f"pins did not catch: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(VAE_MUTATIONS))
+def test_vae_pins_catch_planted_mistake(sandbox, name):
+    src_path = os.path.join(ROOT, "oracle", "vae_oracle.py")
+    src = open(src_path).read()
+    a, b = VAE_MUTATIONS[name]
+    assert src.count(a) >= 1, f"mutation anchor not found: {name}"
+    dst = os.path.join(sandbox, "oracle", "vae_oracle.py")
+    try:
+        with open(dst, "w") as f:
+            f.write(src.replace(a, b, 1))
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            "tests/test_vae_oracle_pins.py"], cwd=sandbox, capture_output=True,
                            text=True, timeout=300)
     finally:
         with open(dst, "w") as f:
