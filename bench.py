@@ -12,10 +12,11 @@ pair, one full-width block at 256 px (at the MFMA / HBM ridge: both fractions), 
 forward at 1024^2 (cond alone and the cond/uncond pair), the roofline of the dominant kernel
 and the oracle's CPU baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder|vae]
 
 --workload encoder times the text encoder instead (its own JSON line): the Qwen3-4B-shaped
 decoder on two right-padded rows of 64 ids (45 and 10 valid) to hidden_states[-2].
+--workload vae times the fp32 VAE decode of one 1024x1024 image (latent 16 x 128 x 128).
 --kernel-only NAME launches one kernel at its main-block shape a few times on operands that
 rotate through more memory than the 256 MB last-level cache holds (as in the pass), for
 rocprofv3 counter runs.
@@ -647,6 +648,10 @@ def kernel_only(which):
         ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, Me, D, I))
         for _ in range(3):
             Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, Me, D, I, A, Wd, None, None, X, ws)
+    elif which in ("vae_conv", "vae_upconv"):
+        conv = vae_conv_runner(which == "vae_upconv", stream)
+        for _ in range(16):
+            conv()
     else:
         run = KernelRunner(synth.FULL, which, stream)
         for _ in range(16):
@@ -655,20 +660,157 @@ def kernel_only(which):
     print(f"kernel-only {which}: launches done", flush=True)
 
 
+def vae_conv_runner(upsample, stream):
+    """One VAE conv at its decode shape: the 3x3 conv 512 -> 512 at 256 x 256 with the
+    GroupNorm affine + SiLU fused (upsample False; the stage-1 ResNet convs), or the upsample
+    conv 512 -> 512 from 256 x 256 to 512 x 512 (upsample True).  Returns (launch, flops)."""
+    import torch
+    from diffusion_transformer_text_s3_amd import binding as Z
+    C = 512
+    Hc = 512 if upsample else 256
+    Hi = Hc // 2 if upsample else Hc
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn((1, Hi, Hi, C), generator=g, device="cuda")
+    wt = torch.randn((C, 3, 3, C), generator=g, device="cuda") * (1.0 / (3 * C ** 0.5))
+    bias = torch.zeros(C, device="cuda")
+    aff = None if upsample else torch.stack([torch.ones(C, device="cuda"), torch.zeros(C, device="cuda")],
+                                            dim=-1)[None].contiguous()
+    out = torch.empty((1, Hc, Hc, C), device="cuda")
+    up = 1 if upsample else 0
+    act = 0 if upsample else 1
+
+    def launch():
+        Z.zdit_op_vae_conv(1, Hc, Hc, C, C, 3, up, x, aff, act, wt, bias, None, out, stream)
+
+    launch.flops = 2 * 9 * C * C * Hc * Hc
+    launch.keep = (x, wt, bias, aff, out)
+    return launch
+
+
+# ------------------------------------------------------------------------------ VAE decoder
+PEAK_FP32_TFLOPS = 157.3      # dense fp32 MFMA
+VAE_METRIC = "VAE decodes/s of one 1024x1024 image (16-channel AutoencoderKL decoder, fp32)"
+
+
+def vae_flops(vd, B, h, w):
+    """Multiply-adds x 2 of the decoder: every convolution (2 k^2 cin cout per output pixel),
+    the attention's four position-wise linear maps (2 C^2 each per position) and its two
+    products over all position pairs (2 C per pair each)."""
+    conv = lambda cin, cout, k, px: 2 * k * k * cin * cout * px
+    px = h * w
+    c = list(reversed(vd.widths))
+    f = conv(vd.latent_ch, c[0], 3, px)
+    res = lambda cin, cout, p: conv(cin, cout, 3, p) + conv(cout, cout, 3, p) + (conv(cin, cout, 1, p) if cin != cout else 0)
+    f += 2 * res(c[0], c[0], px) + 4 * 2 * c[0] * c[0] * px + 2 * 2 * px * px * c[0]
+    cin = c[0]
+    for i, co in enumerate(c):
+        f += res(cin, co, px) + (vd.resnets - 1) * res(co, co, px)
+        if i < 3:
+            px *= 4
+            f += conv(co, co, 3, px)
+        cin = co
+    f += conv(c[-1], vd.out_ch, 3, px)
+    return B * f
+
+
+def vae_bench(args):
+    """The decoder on one 1024x1024 image (latent 16 x 128 x 128), seeded full-width weights."""
+    import numpy as np
+    import torch
+    import synth
+    from diffusion_transformer_text_s3_amd import binding as Z
+    vd = synth.VAE_FULL
+    B, h, w = 1, 128, 128
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    m = Z.upload_vae(synth.vae_weights(vd, args.seed), vd)
+    z = torch.from_numpy(synth.latents((B, vd.latent_ch, h, w), args.seed)).cuda()
+    cfg = Z.make_vae_cfg(vd)
+    img = torch.empty((B, vd.out_ch, 8 * h, 8 * w), device="cuda")
+    ws = Z.workspace(Z.zdit_vae_workspace(cfg, B, h, w))
+    step = lambda: Z.zdit_vae_decode(cfg, m, B, h, w, z, img, ws, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_reps(step, args.steps, stream)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    finite = bool(np.isfinite(img.cpu().numpy()).all())
+    fl = vae_flops(vd, B, h, w)
+    del ws
+    torch.cuda.empty_cache()
+
+    # dominant kernel: the 3x3 conv 512 -> 512 at 256 x 256 with the GroupNorm affine and SiLU
+    # fused (the six stage-1 ResNet convs of a decode)
+    Hc = Wc = 256
+    C = 512
+    conv = vae_conv_runner(False, stream)
+    for _ in range(3):
+        conv()
+    c_ms = time_reps(conv, 20, stream)
+    c_avg = sum(c_ms) / len(c_ms)
+    c_fl = conv.flops
+    achieved = c_fl / (c_avg * 1e-3) / 1e12
+    st = stats(ms)
+    rec = {
+        "metric": VAE_METRIC, "value": round(1e3 / st["median_ms"], 3), "unit": "decodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) latent, random-init fp32 decoder weights)",
+        "config": {"workload": "VAE decode, latent 16 x 128 x 128 -> image 3 x 1024 x 1024, batch 1",
+                   "widths": list(vd.widths), "resnets_per_stage": vd.resnets, "tflop_per_step": round(fl / 1e12, 3)},
+        "decode": {**st, "tflops": round(fl / (st["median_ms"] * 1e-3) / 1e12, 2),
+                   "pct_fp32_peak": round(100 * fl / (st["median_ms"] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 2)},
+        "roofline": {"kernel": f"vconv_kernel (3x3 conv {C} -> {C} at {Hc}x{Wc}, GroupNorm affine + SiLU fused)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "avg_launch_ms": round(c_avg, 4),
+                     "flop_per_launch": c_fl, "launches": len(c_ms), "traffic": None},
+        "output_finite": finite,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = vae_cpu_baseline(vd, args.seed)
+    print(json.dumps(rec), flush=True)
+
+
+def vae_cpu_baseline(vd, seed):
+    """The decoder oracle (as it stands, fp32 NumPy) on a bounded sample: one decode of a
+    32 x 32 latent (a 256 x 256 image), timed on this host's cores, in TFLOP/s."""
+    import numpy as np
+    import synth
+    from oracle import vae_oracle as V
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    W = synth.vae_weights(vd, seed)
+    z = synth.latents((1, vd.latent_ch, 32, 32), seed)
+    t0 = time.perf_counter()
+    V.decoder(z, W, vd, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    fl = vae_flops(vd, 1, 32, 32)
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one decode of a 32 x 32 latent (256 x 256 image), fp32 NumPy oracle", "seconds": round(dt, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", choices=["1024", "1536", "encoder"], default="1024",
-                    help="the DiT pass at 1024^2 (default) or 1536x1024, or the text encoder forward")
+    ap.add_argument("--workload", choices=["1024", "1536", "encoder", "vae"], default="1024",
+                    help="the DiT pass at 1024^2 (default) or 1536x1024, the text encoder forward, or the VAE "
+                         "decode of a 1024x1024 image")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--kernel-only", default=None,
-                    choices=["qkv", "attn", "out", "swiglu", "w2", "rmsnorm", "adaln", "euler", "copy", "enc_down"],
+                    choices=["qkv", "attn", "out", "swiglu", "w2", "rmsnorm", "adaln", "euler", "copy", "enc_down",
+                             "vae_conv", "vae_upconv"],
                     help="launch only one kernel at its main-block shape on rotating operands (or a plain device "
                          "copy of 170,393,600 bytes, the counter calibration; or the encoder's split-K down "
-                         "projection), for rocprofv3 --pmc runs")
+                         "projection; or a VAE conv at its decode shape), for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU "
@@ -685,6 +827,9 @@ def main():
         return
     if args.workload == "encoder":
         encoder_bench(args)
+        return
+    if args.workload == "vae":
+        vae_bench(args)
         return
 
     wl = synth.CFG5 if args.workload == "1024" else synth.CFG5_WIDE

@@ -32,7 +32,10 @@ EXPORTS = [
     "zdit_op_qknorm_rope", "zdit_op_attn_gqa_workspace", "zdit_op_attn_gqa",
     "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk", "zdit_op_mfma_peak",
     "zdit_device_info",
+    "zdit_vae_workspace", "zdit_vae_decode", "zdit_op_vae_groupnorm_workspace", "zdit_op_vae_groupnorm",
+    "zdit_op_vae_conv", "zdit_op_vae_conv_out", "zdit_op_vae_attention_workspace", "zdit_op_vae_attention",
 ]
+ZDIT_VAE_INPUT_UNSCALED = 1
 
 
 class zdit_dims(C.Structure):
@@ -80,6 +83,35 @@ class zdit_enc_w(C.Structure):
     _fields_ = [("embed", C.c_void_p), ("layers", C.POINTER(zdit_enc_layer_w))]
 
 
+class zdit_vae_cfg(C.Structure):
+    _fields_ = [("latent_ch", C.c_int32), ("out_ch", C.c_int32), ("widths", C.c_int32 * 4), ("resnets", C.c_int32),
+                ("groups", C.c_int32), ("eps", C.c_float), ("scale", C.c_float), ("shift", C.c_float),
+                ("flags", C.c_int32)]
+
+
+class zdit_vae_conv(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("b", C.c_void_p)]
+
+
+class zdit_vae_norm(C.Structure):
+    _fields_ = [("gamma", C.c_void_p), ("beta", C.c_void_p)]
+
+
+class zdit_vae_resnet(C.Structure):
+    _fields_ = [("gn1", zdit_vae_norm), ("conv1", zdit_vae_conv), ("gn2", zdit_vae_norm), ("conv2", zdit_vae_conv),
+                ("shortcut", zdit_vae_conv)]
+
+
+class zdit_vae_attn(C.Structure):
+    _fields_ = [("gn", zdit_vae_norm), ("qkv", zdit_vae_conv), ("out", zdit_vae_conv)]
+
+
+class zdit_vae_w(C.Structure):
+    _fields_ = [("conv_in", zdit_vae_conv), ("mid", zdit_vae_resnet * 2), ("attn", zdit_vae_attn),
+                ("stages", C.POINTER(zdit_vae_resnet) * 4), ("upconv", zdit_vae_conv * 3),
+                ("norm_out", zdit_vae_norm), ("conv_out", zdit_vae_conv)]
+
+
 class ZditError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"zdit error {code}: {msg}")
@@ -103,6 +135,7 @@ def lib():
         pd, pw = C.POINTER(zdit_dims), C.POINTER(zdit_block_w)
         pc, pm = C.POINTER(zdit_model_cfg), C.POINTER(zdit_model_w)
         pe, pew = C.POINTER(zdit_enc_cfg), C.POINTER(zdit_enc_w)
+        pv, pvw, pva = C.POINTER(zdit_vae_cfg), C.POINTER(zdit_vae_w), C.POINTER(zdit_vae_attn)
         sig = {
             "zdit_last_error": (C.c_char_p, []),
             "zdit_abi_version": (i32, []),
@@ -141,6 +174,14 @@ def lib():
             "zdit_op_gemm_splitk": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
             "zdit_op_mfma_peak": (i32, [i32, i32, vp, vp]),
             "zdit_device_info": (i32, [i32, pi32, pi32, pi32]),
+            "zdit_vae_workspace": (sz, [pv, i32, i32, i32]),
+            "zdit_vae_decode": (i32, [pv, pvw, i32, i32, i32, vp, vp, vp, sz, vp]),
+            "zdit_op_vae_groupnorm_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_vae_groupnorm": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_op_vae_conv": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp]),
+            "zdit_op_vae_conv_out": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+            "zdit_op_vae_attention_workspace": (sz, [i32, i32, i32, i32]),
+            "zdit_op_vae_attention": (i32, [i32, i32, i32, i32, i32, f32, pva, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -497,3 +538,119 @@ def zdit_device_info(device=0) -> dict:
     cu, clk, l2 = C.c_int32(), C.c_int32(), C.c_int32()
     check(lib().zdit_device_info(device, C.byref(cu), C.byref(clk), C.byref(l2)))
     return {"cu_count": cu.value, "max_sclk_mhz": clk.value / 1000.0, "l2_bytes": l2.value}
+
+
+# ----------------------------------------------------------------------------- VAE decoder
+def make_vae_cfg(vd, flags=0) -> zdit_vae_cfg:
+    """zdit_vae_cfg from any object with latent_ch / out_ch / widths / resnets / groups / eps /
+    scale / shift attributes; flags 0 or ZDIT_VAE_INPUT_UNSCALED."""
+    c = zdit_vae_cfg()
+    c.latent_ch, c.out_ch, c.resnets, c.groups = vd.latent_ch, vd.out_ch, vd.resnets, vd.groups
+    c.widths[:] = list(vd.widths)
+    c.eps, c.scale, c.shift, c.flags = vd.eps, vd.scale, vd.shift, flags
+    return c
+
+
+def vae_conv_weight(w, device="cuda"):
+    """A conv weight [out, in, k, k] (or a linear map [out, in]) as the library's
+    [out][k][k][in] fp32 device tensor."""
+    import numpy as np
+    import torch
+    w = np.asarray(w, dtype=np.float32)
+    if w.ndim == 2:
+        w = w[:, :, None, None]
+    return torch.from_numpy(np.ascontiguousarray(w.transpose(0, 2, 3, 1))).to(device)
+
+
+class DeviceVae:
+    """Device copies of the decoder weights and the zdit_vae_w view (keeps them alive)."""
+
+    def __init__(self, W: dict, vd, device="cuda"):
+        import numpy as np
+        import torch
+        self.t = {}
+
+        def vec(k):
+            self.t[k] = torch.from_numpy(np.ascontiguousarray(W[k], dtype=np.float32)).to(device)
+            return self.t[k].data_ptr()
+
+        def conv(dst, p):
+            self.t[p + ".w"] = vae_conv_weight(W[p + ".w"], device)
+            dst.w, dst.b = self.t[p + ".w"].data_ptr(), vec(p + ".b")
+
+        def norm(dst, p):
+            dst.gamma, dst.beta = vec(p + ".g"), vec(p + ".b")
+
+        def resnet(dst, p):
+            norm(dst.gn1, p + ".gn1")
+            conv(dst.conv1, p + ".conv1")
+            norm(dst.gn2, p + ".gn2")
+            conv(dst.conv2, p + ".conv2")
+            if (p + ".short.w") in W:
+                conv(dst.shortcut, p + ".short")
+
+        w = zdit_vae_w()
+        conv(w.conv_in, "conv_in")
+        resnet(w.mid[0], "mid.res0")
+        resnet(w.mid[1], "mid.res1")
+        norm(w.attn.gn, "mid.attn.gn")
+        qkv = np.concatenate([W["mid.attn.q.w"], W["mid.attn.k.w"], W["mid.attn.v.w"]], axis=0)
+        self.t["qkv.w"] = vae_conv_weight(qkv, device)
+        self.t["qkv.b"] = torch.from_numpy(np.concatenate(
+            [W["mid.attn.q.b"], W["mid.attn.k.b"], W["mid.attn.v.b"]]).astype(np.float32)).to(device)
+        w.attn.qkv.w, w.attn.qkv.b = self.t["qkv.w"].data_ptr(), self.t["qkv.b"].data_ptr()
+        conv(w.attn.out, "mid.attn.o")
+        self.stages = []
+        for i in range(4):
+            arr = (zdit_vae_resnet * vd.resnets)()
+            for j in range(vd.resnets):
+                resnet(arr[j], f"up{i}.res{j}")
+            self.stages.append(arr)
+            w.stages[i] = C.cast(arr, C.POINTER(zdit_vae_resnet))
+            if i < 3:
+                conv(w.upconv[i], f"up{i}.upconv")
+        norm(w.norm_out, "norm_out")
+        conv(w.conv_out, "conv_out")
+        self.w = w
+        self.attn = w.attn
+
+
+def upload_vae(W: dict, vd, device="cuda") -> DeviceVae:
+    return DeviceVae(W, vd, device)
+
+
+def zdit_vae_workspace(cfg, batch, lat_h, lat_w) -> int:
+    return lib().zdit_vae_workspace(C.byref(cfg), batch, lat_h, lat_w)
+
+
+def zdit_vae_decode(cfg, m: DeviceVae, batch, lat_h, lat_w, latent, image, ws, stream=None):
+    return check(lib().zdit_vae_decode(C.byref(cfg), C.byref(m.w), batch, lat_h, lat_w, ptr(latent), ptr(image),
+                                       ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_vae_groupnorm_workspace(batch, hw, C_, groups) -> int:
+    return lib().zdit_op_vae_groupnorm_workspace(batch, hw, C_, groups)
+
+
+def zdit_op_vae_groupnorm(batch, hw, C_, groups, eps, x, gamma, beta, affine, ws, stream=None):
+    return check(lib().zdit_op_vae_groupnorm(batch, hw, C_, groups, eps, ptr(x), ptr(gamma), ptr(beta), ptr(affine),
+                                             ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_vae_conv(batch, H, W, cin, cout, ksize, upsample, x, affine, silu, w, b, res, out, stream=None):
+    return check(lib().zdit_op_vae_conv(batch, H, W, cin, cout, ksize, upsample, ptr(x), ptr(affine), silu, ptr(w),
+                                        ptr(b), ptr(res), ptr(out), stream_handle(stream)))
+
+
+def zdit_op_vae_conv_out(batch, H, W, cin, cout, x, affine, w, b, image, stream=None):
+    return check(lib().zdit_op_vae_conv_out(batch, H, W, cin, cout, ptr(x), ptr(affine), ptr(w), ptr(b), ptr(image),
+                                            stream_handle(stream)))
+
+
+def zdit_op_vae_attention_workspace(batch, hw, C_, groups) -> int:
+    return lib().zdit_op_vae_attention_workspace(batch, hw, C_, groups)
+
+
+def zdit_op_vae_attention(batch, H, W, C_, groups, eps, m: DeviceVae, x, ws, stream=None):
+    return check(lib().zdit_op_vae_attention(batch, H, W, C_, groups, eps, C.byref(m.attn), ptr(x), ptr(ws),
+                                             ws.numel(), stream_handle(stream)))

@@ -1,0 +1,385 @@
+// fp32 kernels of the 16-channel AutoencoderKL decoder (Core AI model zoo, "Z-Image-Turbo
+// port", table "Architecture -> export mapping", row VAE: the decoder runs in fp32 and
+// upsamples by nearest neighbour).  Activations are NHWC fp32 so that a pixel's channels are
+// contiguous: the 3x3 convolutions run as implicit GEMMs on the fp32 MFMA (v_mfma_f32_16x16x4
+// _f32), reading each (pixel, tap) as a 64-byte channel slice, with the GroupNorm affine,
+// SiLU and the 2x nearest upsample applied while the input tile is staged in LDS.
+#include <math.h>
+
+#include <algorithm>
+
+#include "vae.h"
+
+namespace zdit {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kVM = 128;     // output pixels per tile
+constexpr int kVN = 128;     // output channels per tile
+constexpr int kVK = 16;      // channels of one tap per K step
+constexpr int kVLd = 16;     // LDS row: the 16 channels of a K step, 64 bytes
+
+// 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 2) & 3): a wave's fragment reads (16
+// rows x one chunk) and the loaders' writes (8 rows x two chunks) then hit distinct banks.
+__device__ inline int vlds(int r, int c) { return r * kVLd + ((c ^ ((r >> 2) & 3)) << 2); }
+
+// SiLU with the hardware exp2 and reciprocal (each within a few ulp): t / (1 + e^-t)
+__device__ inline float silu_f(float t) { return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
+
+// 256 threads = 4 wavefronts, each owning 64 rows x (BN / (4 / (BM / 64))) columns of the
+// BM x BN output tile as 16 x 16 MFMA tiles: BM = BN = 128 (a 2 x 2 wave grid, 64 x 64 per
+// wave, 64 fp32 accumulators per lane) for the convolutions and GEMMs, BM = 256, BN = 16 (4 x 1,
+// 64 x 16 per wave) for the output conv to 3 channels.  One K step = 16 channels of one tap:
+// the A tile (BM pixels x 16) and the B tile (BN output channels x 16) are loaded into
+// registers one step ahead, transformed, and written to the other half of a double-buffered
+// LDS ring; one barrier per step.  A lane reads its fragment as one 16-byte row chunk: lane l
+// feeds k = 4 * (l / 16) + kk of the step in the kk-th MFMA, for A and B alike.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
+  constexpr int TA = 256 / BM;          // loader threads per A row
+  constexpr int FA = 4 / TA;            // float4 of one A row per loader thread
+  constexpr int WGM = BM / 64;          // wave grid rows
+  constexpr int WGN = 4 / WGM;          // wave grid columns
+  constexpr int RJ = BN / WGN / 16;     // 16-wide column tiles per wave
+  constexpr int FB = 4 * BN >= 256 ? 4 * BN / 256 : 1;  // float4 of B per loader thread
+  constexpr int TB = 4 / FB;            // loader threads per B row
+  __shared__ __attribute__((aligned(16))) float sA[2][BM * kVLd];
+  __shared__ __attribute__((aligned(16))) float sB[2][BN * kVLd];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int z = blockIdx.z;
+  const float* A = a.A + (int64_t)z * a.a_bstride;
+  const float* B = a.B + (int64_t)z * a.b_bstride;
+  float* C = a.C + (int64_t)z * a.c_bstride;
+  const float* R = a.res ? a.res + (int64_t)z * a.c_bstride : nullptr;
+  const int hw = a.H * a.W;
+
+  // A loader: tile row lr, channels 4 FA lh .. of the step; B loader: row br, part bh
+  const int lr = tid / TA, lh = tid % TA;
+  const int am = m0 + lr;
+  const bool arow = am < a.M;
+  int img = 0, py = 0, px = 0;
+  if (arow) {
+    img = am / hw;
+    const int rem = am - img * hw;
+    py = rem / a.W;
+    px = rem - py * a.W;
+  }
+  const int br = tid / TB, bh = tid % TB;
+  const bool bload = br < BN;
+  const int bn = n0 + br;
+  const bool brow = bload && bn < a.N;
+  const float* Brow = B + (int64_t)(brow ? bn : 0) * a.ldb;
+  const int rad = a.ksize >> 1;
+  const int Hs = a.upsample ? a.H >> 1 : a.H, Ws = a.upsample ? a.W >> 1 : a.W;
+  const int csteps = (a.K + kVK - 1) / kVK;
+  const int nsteps = a.ksize * a.ksize * csteps;
+  const float* aff = a.affine ? a.affine + (int64_t)img * a.K * 2 : nullptr;
+
+  f4 ra[FA], rb[FB], rf[2 * FA];  // rf: (a, d) pairs of the A channels
+  bool aval = false;
+  int ac = 0;
+  // position of the next step to load: tap (ky, kx) and channel step cst, advanced in order
+  int ky = 0, kx = 0, tap = 0, cst = 0;
+  auto load = [&]() {
+    const int cs = cst * kVK;
+    const int c0 = cs + 4 * FA * lh;
+    const int yy = py + ky - rad, xx = px + kx - rad;
+    aval = arow && yy >= 0 && yy < a.H && xx >= 0 && xx < a.W;
+    ac = c0;
+    const float* src = A;
+    if (aval) {
+      const int ys = a.upsample ? yy >> 1 : yy, xs = a.upsample ? xx >> 1 : xx;
+      src = A + ((int64_t)(img * Hs + ys) * Ws + xs) * a.lda + c0;
+    }
+#pragma unroll
+    for (int j = 0; j < FA; ++j) {
+      const bool cin = c0 + 4 * j < a.K;  // K % 4 == 0: a 4-channel group is all in or all out
+      ra[j] = (aval && cin) ? *(const f4*)(src + 4 * j) : f4{0.f, 0.f, 0.f, 0.f};
+      if (aff) {
+        rf[2 * j] = cin ? *(const f4*)(aff + 2 * (c0 + 4 * j)) : f4{0.f, 0.f, 0.f, 0.f};
+        rf[2 * j + 1] = cin ? *(const f4*)(aff + 2 * (c0 + 4 * j) + 4) : f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const int cb = cs + 4 * FB * bh;
+    const float* wsrc = Brow + (int64_t)tap * a.K + cb;
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+      rb[j] = (brow && cb + 4 * j < a.K) ? *(const f4*)(wsrc + 4 * j) : f4{0.f, 0.f, 0.f, 0.f};
+    if (++cst == csteps) {
+      cst = 0;
+      ++tap;
+      if (++kx == a.ksize) {
+        kx = 0;
+        ++ky;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < FA; ++j) {
+      f4 v = ra[j];
+      if (aff && aval && ac + 4 * j < a.K) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f4 ad = rf[2 * j + (e >> 1)];
+          const float t = fmaf(ad[2 * (e & 1)], v[e], ad[2 * (e & 1) + 1]);
+          v[e] = a.silu ? silu_f(t) : t;
+        }
+      }
+      *(f4*)&sA[buf][vlds(lr, FA * lh + j)] = v;
+    }
+    if (bload) {
+#pragma unroll
+      for (int j = 0; j < FB; ++j) *(f4*)&sB[buf][vlds(br, FB * bh + j)] = rb[j];
+    }
+  };
+
+  const int wm0 = (wave % WGM) * 64, wn0 = (wave / WGM) * (BN / WGN);
+  const int fr = lane & 15, fk = 4 * (lane >> 4), fc = lane >> 4;
+  f4 acc[4][RJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  load();
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nsteps) load();
+    f4 af[4], bf[RJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *(const f4*)&sA[buf][vlds(wm0 + 16 * i + fr, fc)];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) bf[j] = *(const f4*)&sB[buf][vlds(wn0 + 16 * j + fr, fc)];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < RJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
+    if (s + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane l holds rows 4 * (l / 16) + e, column l % 16 of each 16 x 16 result tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int n = n0 + wn0 + 16 * j + fr;
+      if (n >= a.N) continue;
+      const float bv = a.bias ? a.bias[n] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm0 + 16 * i + fk + e;
+        if (m >= a.M) continue;
+        int64_t o;
+        if (a.out_nchw) {
+          const int im = m / hw;
+          o = ((int64_t)im * a.N + n) * hw + (m - im * hw);
+        } else {
+          o = (int64_t)m * a.ldc + n;
+        }
+        float v = a.alpha * acc[i][j][e] + bv;
+        if (R) v = R[o] + v;
+        C[o] = v;
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------ GroupNorm
+// Partial sums over one chunk of pixels of one image: pass 0 sums x, pass 1 sums (x - mean)^2
+// with the group's mean from the first pass.  256 threads: C / 4 channel quads across, 256 /
+// (C / 4) pixels down; the per-thread sums are added per channel in a fixed order.
+__global__ __launch_bounds__(256) void vgn_partial_kernel(VGnArgs a, int pass) {
+  __shared__ f4 red[256];
+  const int tid = threadIdx.x;
+  const int img = blockIdx.y, chunk = blockIdx.x;
+  const int Q = a.C >> 2, rows = 256 / Q;
+  const int q = tid % Q, r = tid / Q;
+  const int p0 = chunk * a.chunk, p1 = min(p0 + a.chunk, a.HW);
+  const int cpg = a.C / a.groups;
+  f4 m = f4{0.f, 0.f, 0.f, 0.f};
+  if (pass) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m[e] = (float)a.stat[((int64_t)img * a.groups + (4 * q + e) / cpg) * 2];
+  }
+  f4 s = f4{0.f, 0.f, 0.f, 0.f};
+  const float* x = a.x + (int64_t)img * a.HW * a.C + 4 * q;
+  for (int p = p0 + r; p < p1; p += rows) {
+    const f4 v = *(const f4*)(x + (int64_t)p * a.C);
+    if (pass) {
+      const f4 d = v - m;
+      s += d * d;
+    } else {
+      s += v;
+    }
+  }
+  red[tid] = s;
+  __syncthreads();
+  const int nch = gridDim.x;
+  for (int c = tid; c < a.C; c += 256) {
+    float t = 0.f;
+    for (int rr = 0; rr < rows; ++rr) t += red[rr * Q + (c >> 2)][c & 3];
+    a.part[((int64_t)img * nch + chunk) * a.C + c] = t;
+  }
+}
+
+// One workgroup per (group, image): the chunk partials of the group's channels summed in
+// float64 in a fixed order; pass 0 stores the mean, pass 1 1/sqrt(var + eps) and the
+// per-channel affine (a, d) = (gamma rstd, beta - mean gamma rstd).
+__global__ __launch_bounds__(256) void vgn_finalize_kernel(VGnArgs a, int nch, int pass) {
+  __shared__ double red[256];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x, img = blockIdx.y;
+  const int cpg = a.C / a.groups;
+  const int n = nch * cpg;
+  double t = 0.0;
+  for (int i = tid; i < n; i += 256) {
+    const int ch = i / cpg, cc = i - ch * cpg;
+    t += (double)a.part[((int64_t)img * nch + ch) * a.C + g * cpg + cc];
+  }
+  red[tid] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const double cnt = (double)a.HW * cpg;
+  double* st = a.stat + ((int64_t)img * a.groups + g) * 2;
+  if (pass == 0) {
+    if (tid == 0) st[0] = red[0] / cnt;
+    return;
+  }
+  const double mean = st[0];
+  const double rstd = 1.0 / sqrt(red[0] / cnt + (double)a.eps);
+  if (tid == 0) st[1] = rstd;
+  for (int cc = tid; cc < cpg; cc += 256) {
+    const int c = g * cpg + cc;
+    const double ga = (double)a.gamma[c] * rstd;
+    a.affine[((int64_t)img * a.C + c) * 2] = (float)ga;
+    a.affine[((int64_t)img * a.C + c) * 2 + 1] = (float)((double)a.beta[c] - mean * ga);
+  }
+}
+
+// ------------------------------------------------------------------------------ small kernels
+__global__ void vlatent_in_kernel(const float* z, float* out, int images, int ch, int h, int w, int unscale,
+                                  float scale, float shift) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)images * ch * h * w;
+  if (i >= n) return;
+  // i indexes the NHWC output: ((img * h + y) * w + x) * ch + c
+  const int c = (int)(i % ch);
+  const int64_t pix = i / ch;
+  const int x = (int)(pix % w);
+  const int64_t t = pix / w;
+  const int y = (int)(t % h);
+  const int img = (int)(t / h);
+  const float v = z[(((int64_t)img * ch + c) * h + y) * w + x];
+  out[i] = unscale ? v / scale + shift : v;
+}
+
+// one workgroup per row: max, then the sum of exp(s - max), then exp(s - max) / sum
+__global__ __launch_bounds__(256) void vsoftmax_kernel(float* S, int n) {
+  __shared__ float red[256];
+  float* row = S + (int64_t)blockIdx.x * n;
+  const int tid = threadIdx.x;
+  float mx = -INFINITY;
+  for (int j = tid; j < n; j += 256) mx = fmaxf(mx, row[j]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sm = 0.f;
+  for (int j = tid; j < n; j += 256) sm += expf(row[j] - mx);
+  red[tid] = sm;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  sm = red[0];
+  for (int j = tid; j < n; j += 256) row[j] = expf(row[j] - mx) / sm;
+}
+
+__global__ void vtranspose_kernel(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int n, int C) {
+  __shared__ float t[32][33];
+  const int b = blockIdx.z;
+  const int j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const float* src = in + (int64_t)b * in_bstride + c0;
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int j = j0 + r, c = k0 + threadIdx.x;
+    t[r][threadIdx.x] = (j < n && c < C) ? src[(int64_t)j * ld + c] : 0.f;
+  }
+  __syncthreads();
+  float* dst = out + (int64_t)b * C * n;
+  for (int r = threadIdx.y; r < 32; r += 8) {
+    const int c = k0 + r, j = j0 + threadIdx.x;
+    if (c < C && j < n) dst[(int64_t)c * n + j] = t[threadIdx.x][r];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_vconv(const VConvArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.N <= 16) {  // the output conv (3 channels): 256 x 16 tiles
+    dim3 grid((a.M + 255) / 256, 1, a.batch);
+    hipLaunchKernelGGL((vconv_kernel<256, 16>), grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((a.M + kVM - 1) / kVM, (a.N + kVN - 1) / kVN, a.batch);
+    hipLaunchKernelGGL((vconv_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+int vgn_chunks(int HW, int C) {
+  const int chunk = std::max(256 / (C / 4), 65536 / C);
+  return (HW + chunk - 1) / chunk;
+}
+
+size_t vgn_part_floats(int images, int HW, int C) { return (size_t)images * vgn_chunks(HW, C) * C; }
+
+hipError_t launch_vgn(VGnArgs a, hipStream_t s) {
+  a.chunk = std::max(256 / (a.C / 4), 65536 / a.C);
+  const int nch = vgn_chunks(a.HW, a.C);
+  for (int pass = 0; pass < 2; ++pass) {
+    hipLaunchKernelGGL(vgn_partial_kernel, dim3(nch, a.images), dim3(256), 0, s, a, pass);
+    hipLaunchKernelGGL(vgn_finalize_kernel, dim3(a.groups, a.images), dim3(256), 0, s, a, nch, pass);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_vlatent_in(const float* z, float* out, int images, int ch, int h, int w, int unscale,
+                             float scale, float shift, hipStream_t s) {
+  const int64_t n = (int64_t)images * ch * h * w;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(vlatent_in_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, z, out, images, ch, h, w,
+                     unscale, scale, shift);
+  return hipGetLastError();
+}
+
+hipError_t launch_vsoftmax(float* S, int64_t rows, int n, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(vsoftmax_kernel, dim3((unsigned)rows), dim3(256), 0, s, S, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_vtranspose(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int batch, int n,
+                             int C, hipStream_t s) {
+  dim3 grid((n + 31) / 32, (C + 31) / 32, batch);
+  hipLaunchKernelGGL(vtranspose_kernel, grid, dim3(32, 8), 0, s, in, ld, in_bstride, c0, out, n, C);
+  return hipGetLastError();
+}
+
+}  // namespace zdit

@@ -1,0 +1,71 @@
+// Internal types and launchers of the fp32 VAE-decoder kernels (k_vae.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zdit {
+
+// Implicit-GEMM convolution / batched GEMM on fp32 MFMA:
+//   C[z][m][n] = res[z][m][n] + alpha * sum_k A'[z][m][k] B[z][n][k] + bias[n]
+// Convolution mode (ksize 3 or 1, batch folded into M): row m is output pixel (img, y, x) of
+// an H x W image, k runs over (tap, channel) with channels innermost, A' is the input pixel
+// at (y + ky - r, x + kx - r) (zero outside the image; with `upsample` the input has H/2 x W/2
+// pixels and is read at half the coordinates), rows of `lda` floats; if `affine` is set each
+// input value becomes a * x + d with (a, d) = affine[img][c] (then SiLU if `silu`) before the
+// product, padding staying zero.  B holds weights [N][ksize * ksize * K] (ldb floats per row).
+// GEMM mode (ksize 1, H = 1, W = M, grid z = batch): plain row-major operands with batch
+// strides.  res may alias C (each element is read before it is written by the same thread).
+// N <= 16 runs 256 x 16 tiles (the output conv), else 128 x 128.
+struct VConvArgs {
+  const float* A;
+  int64_t a_bstride;
+  int64_t lda;
+  const float* B;
+  int64_t b_bstride;
+  int64_t ldb;
+  float* C;
+  int64_t c_bstride;
+  int64_t ldc;
+  const float* res;
+  const float* bias;
+  const float* affine;  // [images][K][2]
+  int silu;
+  int M, N, K;          // K = channels per tap
+  int H, W;             // output image size (conv mode)
+  int ksize, upsample;
+  int batch;            // grid z (GEMM mode), 1 in conv mode
+  int out_nchw;         // conv mode: C is [images][N][H][W] (ldc unused)
+  float alpha;
+};
+
+// GroupNorm statistics over NHWC activations x [images][HW][C], groups of C / groups
+// consecutive channels; partial sums per (image, chunk of pixels, channel), then per group.
+struct VGnArgs {
+  const float* x;
+  int images, HW, C, groups;
+  int chunk;            // pixels per workgroup
+  float* part;          // [images][n_chunks][C]
+  double* stat;         // [images][groups][2]: mean, then 1/sqrt(var + eps)
+  const float* gamma;
+  const float* beta;
+  float* affine;        // [images][C][2]
+  float eps;
+};
+
+int vgn_chunks(int HW, int C);
+size_t vgn_part_floats(int images, int HW, int C);
+
+hipError_t launch_vconv(const VConvArgs& a, hipStream_t s);
+hipError_t launch_vgn(VGnArgs a, hipStream_t s);   // stats + affine (two passes over x)
+// latent [images][ch][h][w] -> NHWC [images][h][w][ch], each value z / scale + shift (unscale
+// != 0) or copied
+hipError_t launch_vlatent_in(const float* z, float* out, int images, int ch, int h, int w, int unscale,
+                             float scale, float shift, hipStream_t s);
+// rows of S [rows][n] in place: exp(s - max) / sum
+hipError_t launch_vsoftmax(float* S, int64_t rows, int n, hipStream_t s);
+// out[b][c][j] = in[b][j][c0 + c] (in rows of ld floats), c < C, j < n
+hipError_t launch_vtranspose(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int batch, int n,
+                             int C, hipStream_t s);
+
+}  // namespace zdit

@@ -469,6 +469,111 @@ zdit_status zdit_op_attn_gqa(int32_t precision, int32_t batch, int32_t s_max, in
                              void* hip_stream);
 
 /* ---------------------------------------------------------------------------------------
+ * VAE decoder: the 16-channel AutoencoderKL decoder that turns the sampler's final latent
+ * into the image ([CoreAI] "Architecture -> export mapping", row VAE: fp32, nearest-neighbour
+ * upsampling, the unscale z / 0.3611 + 0.1159 built into the decoder, which is fed the raw
+ * latent; [Status] component matrix, row VAE: the raw decode is the component boundary).
+ * Architecture (the published 16-channel autoencoder with those constants; not spelled out
+ * on the pages), widths in decoder order c0..c3 = widths[3], widths[2], widths[1], widths[0]:
+ *   x = conv_in(z / scale + shift)                      3x3, latent_ch -> c0
+ *   x = resnet(x); x = attention(x); x = resnet(x)      c0
+ *   stage i = 0..3: `resnets` ResNet blocks to width ci (the first from c(i-1), c0 for
+ *   stage 0); for i < 3 then x = conv(upsample2x_nearest(x)), 3x3, ci -> ci
+ *   image = conv_out(SiLU(GroupNorm(x)))                3x3, c3 -> out_ch
+ *   ResNet: h = conv1(SiLU(GN1(x))); h = conv2(SiLU(GN2(h))); out = s(x) + h with s the
+ *     identity, or a 1x1 conv when the width changes.
+ *   Attention: h = GN(x); [q | k | v] = per-position linear maps of h; out = x + (softmax(
+ *     q k^T / sqrt(C)) v) W_o^T + b_o, one head over all positions of an image.
+ *   GroupNorm: `groups` groups of consecutive channels, statistics over the group and all
+ *     positions of one image, biased variance, eps; then a per-channel gain and shift.
+ *   Convolutions: cross-correlation, zero padding (k - 1) / 2, stride 1, with biases.
+ * All arithmetic fp32 (GroupNorm statistics accumulated in float64).  Activations inside
+ * are NHWC; the latent is NCHW [batch, latent_ch, lat_h, lat_w], the image NCHW [batch,
+ * out_ch, 8 lat_h, 8 lat_w].
+ * ------------------------------------------------------------------------------------- */
+#define ZDIT_VAE_INPUT_UNSCALED 1 /* cfg.flags: the latent is already unscaled (the sampler's
+                                     decode_out); the decoder then skips z / scale + shift */
+
+typedef struct {
+  int32_t latent_ch; /* 16; a multiple of 4 */
+  int32_t out_ch;    /* 3; 1..4 */
+  int32_t widths[4]; /* encoder-order widths (128, 256, 512, 512): powers of two in 32..1024,
+                        each a multiple of groups */
+  int32_t resnets;   /* ResNet blocks per decoder stage (3); 1..8 */
+  int32_t groups;    /* 32 */
+  float eps;         /* 1e-6 */
+  float scale;       /* 0.3611 */
+  float shift;       /* 0.1159 */
+  int32_t flags;     /* 0 or ZDIT_VAE_INPUT_UNSCALED */
+} zdit_vae_cfg;
+
+/* conv weights fp32 [cout][k][k][cin] (input channels innermost, 16-byte aligned), bias fp32
+ * [cout]; norm gain and shift fp32 [C] */
+typedef struct { const float* w; const float* b; } zdit_vae_conv;
+typedef struct { const float* gamma; const float* beta; } zdit_vae_norm;
+typedef struct {
+  zdit_vae_norm gn1;
+  zdit_vae_conv conv1;    /* 3x3, cin -> cout */
+  zdit_vae_norm gn2;
+  zdit_vae_conv conv2;    /* 3x3, cout -> cout */
+  zdit_vae_conv shortcut; /* 1x1, cin -> cout; w NULL exactly when cin == cout */
+} zdit_vae_resnet;
+typedef struct {
+  zdit_vae_norm gn;
+  zdit_vae_conv qkv; /* w [3C][1][1][C]: the q rows, then k, then v; b [3C] */
+  zdit_vae_conv out; /* w [C][1][1][C] */
+} zdit_vae_attn;
+typedef struct {
+  zdit_vae_conv conv_in;
+  zdit_vae_resnet mid[2];
+  zdit_vae_attn attn;
+  const zdit_vae_resnet* stages[4]; /* host arrays of cfg.resnets blocks each, decoder order */
+  zdit_vae_conv upconv[3];
+  zdit_vae_norm norm_out;
+  zdit_vae_conv conv_out;
+} zdit_vae_w;
+
+/* Decode `batch` latents.  latent device fp32 [batch, latent_ch, lat_h, lat_w] (raw: the
+ * sampler's final x, unless cfg.flags has ZDIT_VAE_INPUT_UNSCALED), image device fp32
+ * [batch, out_ch, 8 lat_h, 8 lat_w], written.  batch 1..ZDIT_MAX_BATCH; lat_h, lat_w even,
+ * 2..256; ws: zdit_vae_workspace() bytes (1024^2: ~4.3 GB for one image, the attention
+ * scores of the 128 x 128 latent taking 1 GiB of it).  Images are independent. */
+size_t zdit_vae_workspace(const zdit_vae_cfg* cfg, int32_t batch, int32_t lat_h, int32_t lat_w);
+zdit_status zdit_vae_decode(const zdit_vae_cfg* cfg, const zdit_vae_w* w, int32_t batch,
+                            int32_t lat_h, int32_t lat_w, const float* latent, float* image,
+                            void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Decoder steps alone (tests and measurement); activations NHWC fp32 [batch, H, W, C]. */
+/* GroupNorm of x [batch, hw, C] as a per-image, per-channel affine: affine [batch, C, 2] =
+ * (gamma_c r, beta_c - mean gamma_c r), r = 1 / sqrt(var + eps) of the channel's group.
+ * C a power of two in 32..1024, groups divides C; ws: zdit_op_vae_groupnorm_workspace(). */
+size_t zdit_op_vae_groupnorm_workspace(int32_t batch, int32_t hw, int32_t C, int32_t groups);
+zdit_status zdit_op_vae_groupnorm(int32_t batch, int32_t hw, int32_t C, int32_t groups, float eps,
+                                  const float* x, const float* gamma, const float* beta,
+                                  float* affine, void* ws, size_t ws_bytes, void* hip_stream);
+/* out [batch, H, W, cout] = res + conv(t(x)) + b, ksize 1 or 3: x [batch, H, W, cin], or
+ * [batch, H/2, W/2, cin] read at half the coordinates with upsample != 0 (2x nearest
+ * upsampling before the conv); t(v) = a v + d with (a, d) = affine[img][c] if affine is
+ * set (then SiLU if silu != 0), else v; zero padding after t.  res NULL or [batch, H, W,
+ * cout] (may equal out).  w [cout][ksize][ksize][cin]; cin a multiple of 4. */
+zdit_status zdit_op_vae_conv(int32_t batch, int32_t H, int32_t W, int32_t cin, int32_t cout,
+                             int32_t ksize, int32_t upsample, const float* x, const float* affine,
+                             int32_t silu, const float* w, const float* b, const float* res,
+                             float* out, void* hip_stream);
+/* image NCHW [batch, cout, H, W] = conv3x3(SiLU(a x + d)) + b with x NHWC [batch, H, W, cin],
+ * (a, d) = affine[img][c] (16-byte aligned), w [cout][3][3][cin]; cout 1..4, cin a multiple
+ * of 4. */
+zdit_status zdit_op_vae_conv_out(int32_t batch, int32_t H, int32_t W, int32_t cin, int32_t cout,
+                                 const float* x, const float* affine, const float* w,
+                                 const float* b, float* image, void* hip_stream);
+/* The middle attention block in place on x [batch, H, W, C]; H * W a multiple of 4 and at
+ * most 65536; ws: zdit_op_vae_attention_workspace(batch, H * W, C, groups) bytes. */
+size_t zdit_op_vae_attention_workspace(int32_t batch, int32_t hw, int32_t C, int32_t groups);
+zdit_status zdit_op_vae_attention(int32_t batch, int32_t H, int32_t W, int32_t C, int32_t groups,
+                                  float eps, const zdit_vae_attn* w, float* x, void* ws,
+                                  size_t ws_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------------------
  * Measurement: the sustained bf16 MFMA rate, for roofline fractions against a measured
  * ceiling.  `workgroups` x 256 threads; every wavefront issues 4 x iters
  * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands, with no memory traffic

@@ -332,3 +332,114 @@ def test_splitk_workspace_depends_on_rows_only_through_m():
     assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_STORE, 257, 2560, 9728) == 0
     assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_STORE, 64, 2560, 9700) == 0
     assert Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_BIAS, 64, 2560, 9728) == 0
+
+
+# ------------------------------------------------------------------------------ VAE decoder
+_FAKE = 0x10000   # an aligned address; argument checks never dereference it
+
+
+def _fake_vae_w(vd, drop_shortcut=False, extra_shortcut=False):
+    """zdit_vae_w with every pointer set to a dummy aligned address (validation only)."""
+    def conv(c):
+        c.w, c.b = _FAKE, _FAKE
+
+    def norm(n):
+        n.gamma, n.beta = _FAKE, _FAKE
+
+    def resnet(r, cin, cout):
+        norm(r.gn1), conv(r.conv1), norm(r.gn2), conv(r.conv2)
+        if cin != cout and not drop_shortcut:
+            conv(r.shortcut)
+
+    w = Z.zdit_vae_w()
+    conv(w.conv_in)
+    c0 = vd.widths[-1]
+    resnet(w.mid[0], c0, c0)
+    resnet(w.mid[1], c0, c0)
+    norm(w.attn.gn), conv(w.attn.qkv), conv(w.attn.out)
+    keep = []
+    for i, (cin, c, up) in enumerate(vd.stages):
+        arr = (Z.zdit_vae_resnet * vd.resnets)()
+        for j in range(vd.resnets):
+            resnet(arr[j], cin if j == 0 else c, c)
+        if extra_shortcut and i == 0:
+            conv(arr[1].shortcut)
+        keep.append(arr)
+        w.stages[i] = C.cast(arr, C.POINTER(Z.zdit_vae_resnet))
+        if up:
+            conv(w.upconv[i])
+    norm(w.norm_out), conv(w.conv_out)
+    return w, keep
+
+
+def _vae_call(cfg, w, B, h, wd, ws_bytes=None, latent=_FAKE, image=_FAKE, ws=_FAKE):
+    L = Z.lib()
+    n = ws_bytes if ws_bytes is not None else max(L.zdit_vae_workspace(C.byref(cfg), B, h, wd), 1)
+    return L.zdit_vae_decode(C.byref(cfg), C.byref(w), B, h, wd, latent, image, ws, n, None)
+
+
+def test_vae_workspace_query():
+    cfg = Z.make_vae_cfg(synth.VAE_FULL)
+    n1 = Z.zdit_vae_workspace(cfg, 1, 128, 128)
+    # three activation buffers of the largest stage (1024^2 x 256 channels) and the 1 GiB of scores
+    assert n1 >= 3 * 1024 * 1024 * 256 * 4 + 16384 * 16384 * 4
+    assert Z.zdit_vae_workspace(cfg, 2, 128, 128) > n1
+    for bad in ((1, 7, 8), (1, 8, 0), (0, 8, 8), (17, 8, 8), (1, 258, 8)):
+        assert Z.zdit_vae_workspace(cfg, *bad) == 0
+    assert Z.zdit_vae_workspace(Z.make_vae_cfg(synth.VAE_FULL.replace(widths=(128, 256, 384, 512))), 1, 8, 8) == 0
+    assert Z.zdit_vae_workspace(Z.make_vae_cfg(synth.VAE_FULL, flags=4), 1, 8, 8) == 0
+
+
+def test_vae_decode_rejects_bad_arguments_before_launch():
+    vd = synth.VAE_TINY
+    cfg = Z.make_vae_cfg(vd)
+    w, keep = _fake_vae_w(vd)
+    L = Z.lib()
+    assert L.zdit_vae_decode(None, C.byref(w), 1, 8, 8, _FAKE, _FAKE, _FAKE, 1 << 30, None) == Z.ZDIT_EINVAL
+    assert _vae_call(cfg, w, 1, 8, 8, ws_bytes=1024) == Z.ZDIT_EWORKSPACE
+    assert _vae_call(cfg, w, 1, 8, 8, ws=_FAKE + 4) == Z.ZDIT_EINVAL
+    assert _vae_call(cfg, w, 1, 8, 8, latent=None) == Z.ZDIT_EINVAL
+    assert _vae_call(cfg, w, 1, 9, 8, ws_bytes=1 << 30) == Z.ZDIT_EUNSUPPORTED
+    w2, keep2 = _fake_vae_w(vd, drop_shortcut=True)
+    assert _vae_call(cfg, w2, 1, 8, 8) == Z.ZDIT_EINVAL and "shortcut" in Z.last_error()
+    w3, keep3 = _fake_vae_w(vd, extra_shortcut=True)
+    assert _vae_call(cfg, w3, 1, 8, 8) == Z.ZDIT_EINVAL and "shortcut" in Z.last_error()
+    w4, keep4 = _fake_vae_w(vd)
+    w4.stages[2] = None
+    assert _vae_call(cfg, w4, 1, 8, 8) == Z.ZDIT_EINVAL and "stages[2]" in Z.last_error()
+    w5, keep5 = _fake_vae_w(vd)
+    w5.conv_out.w = _FAKE + 4
+    assert _vae_call(cfg, w5, 1, 8, 8) == Z.ZDIT_EINVAL and "conv_out" in Z.last_error()
+    bad = Z.make_vae_cfg(vd.replace(groups=3))
+    assert _vae_call(bad, w, 1, 8, 8, ws_bytes=1 << 30) == Z.ZDIT_EINVAL
+    bad = Z.make_vae_cfg(vd.replace(out_ch=5))
+    assert _vae_call(bad, w, 1, 8, 8, ws_bytes=1 << 30) == Z.ZDIT_EUNSUPPORTED
+
+
+def test_vae_ops_reject_bad_arguments_before_launch():
+    L = Z.lib()
+    conv = lambda **k: L.zdit_op_vae_conv(k.get("B", 1), k.get("H", 8), k.get("W", 8), k.get("cin", 32),
+                                          k.get("cout", 32), k.get("ks", 3), k.get("up", 0), k.get("x", _FAKE),
+                                          None, 0, k.get("w", _FAKE), _FAKE, None, _FAKE, None)
+    assert conv(ks=2) == Z.ZDIT_EUNSUPPORTED
+    assert conv(cin=30) == Z.ZDIT_EUNSUPPORTED
+    assert conv(up=1, H=7) == Z.ZDIT_EINVAL
+    assert conv(x=_FAKE + 8) == Z.ZDIT_EINVAL
+    assert conv(w=None) == Z.ZDIT_EINVAL
+    assert conv(B=0) == Z.ZDIT_EINVAL
+    out = lambda **k: L.zdit_op_vae_conv_out(k.get("B", 1), 8, 8, k.get("cin", 128), k.get("cout", 3), _FAKE, _FAKE,
+                                             _FAKE, _FAKE, _FAKE, None)
+    assert out(cout=5) == Z.ZDIT_EUNSUPPORTED
+    assert out(cin=130) == Z.ZDIT_EUNSUPPORTED
+    gn = lambda **k: L.zdit_op_vae_groupnorm(1, 64, k.get("C", 64), k.get("g", 32), k.get("eps", 1e-6), _FAKE, _FAKE,
+                                             _FAKE, _FAKE, _FAKE, k.get("ws", 1 << 20), None)
+    assert gn(C=48) == Z.ZDIT_EUNSUPPORTED
+    assert gn(g=3) == Z.ZDIT_EINVAL
+    assert gn(eps=float("nan")) == Z.ZDIT_EINVAL
+    assert gn(ws=16) == Z.ZDIT_EWORKSPACE
+    assert L.zdit_op_vae_groupnorm_workspace(1, 64, 48, 32) == 0
+    at = Z.zdit_vae_attn()
+    assert L.zdit_op_vae_attention(1, 3, 5, 64, 32, 1e-6, C.byref(at), _FAKE, _FAKE, 1 << 30, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_vae_attention(1, 4, 4, 64, 32, 1e-6, C.byref(at), _FAKE, _FAKE, 1 << 30, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_vae_attention_workspace(1, 15, 64, 32) == 0
+    assert L.zdit_op_vae_attention_workspace(1, 16, 64, 32) >= 16 * 16 * 4 + 16 * 3 * 64 * 4

@@ -84,3 +84,14 @@ def test_graph_text_encoder():
     out = torch.empty((2, 40, ed.hidden), device="cuda")
     ws = Z.workspace(Z.zdit_encoder_workspace(cfg, 2, 40))
     _replays(lambda: Z.zdit_encoder_fwd(cfg, m, 2, 40, ids, lens, out, ws), lambda: None, out)
+
+
+def test_graph_vae_decode():
+    note("graph capture: tiny VAE decode")
+    vd = synth.VAE_TINY
+    m = Z.upload_vae(synth.vae_weights(vd, 84), vd)
+    z = dev(synth.latents((2, vd.latent_ch, 6, 4), 84))
+    cfg = Z.make_vae_cfg(vd)
+    img = torch.empty((2, vd.out_ch, 48, 32), device="cuda")
+    ws = Z.workspace(Z.zdit_vae_workspace(cfg, 2, 6, 4))
+    _replays(lambda: Z.zdit_vae_decode(cfg, m, 2, 6, 4, z, img, ws), lambda: None, img)
