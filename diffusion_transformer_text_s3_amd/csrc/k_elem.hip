@@ -27,20 +27,25 @@ template <> __device__ __forceinline__ float from_act<bf16>(bf16 v) { return (fl
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------------------------------
-// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift.  A workgroup of 4 wavefronts takes 16
+// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift.  A workgroup of 8 wavefronts takes 8
 // rows of one branch; gain, shift and scale of that branch are staged in LDS once, then each
-// wavefront normalises 4 rows, one at a time, keeping the row in registers (dim <= 4096: at
-// most 16 float4 per lane).
+// wavefront normalises one row, keeping it in registers (dim <= 4096: at most 16 float4 per
+// lane).  One row per wavefront keeps more rows in flight than a wavefront looping over rows
+// (55 against 61 us at 8320 x 3840 with 4 rows per wavefront, same box).
 // ---------------------------------------------------------------------------------------
 constexpr int kNormMaxChunks = 16;
-constexpr int kNormRowsPerBlock = 16;
+constexpr int kNormRowsPerBlock = 8;
 
-// STAGED: 16 rows per workgroup with gain / shift / scale staged in LDS (many rows).  Else one
+// STAGED: 8 rows per workgroup with gain / shift / scale staged in LDS (many rows).  Else one
 // row per wavefront, 4 per workgroup, the vectors read from global memory where they stay in
 // L2 (few rows: more workgroups, no staging to amortise).
+constexpr int kNormWaves = 8;
+
 template <typename TO, bool STAGED>
-__global__ __launch_bounds__(256) void rmsnorm_mod_kernel(NormArgs a) {
+__global__ __launch_bounds__(STAGED ? 64 * kNormWaves : 256) void rmsnorm_mod_kernel(NormArgs a) {
   constexpr int kRows = STAGED ? kNormRowsPerBlock : 4;
+  constexpr int kW = STAGED ? kNormWaves : 4;
+  constexpr int kT = 64 * kW;
   __shared__ float4 vg_[STAGED ? 1024 : 1], vsh_[STAGED ? 1024 : 1], vsc_[STAGED ? 1024 : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.y;
@@ -50,15 +55,15 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(NormArgs a) {
   const float4* vsh = mod ? (const float4*)(a.shift + b * a.mod_bstride) : nullptr;
   const float4* vsc = mod ? (const float4*)(a.scale + b * a.mod_bstride) : nullptr;
   if constexpr (STAGED) {
-    for (int c = threadIdx.x; c < nchunk; c += 256) {
+    for (int c = threadIdx.x; c < nchunk; c += kT) {
       vg_[c] = vg[c];
       if (mod) { vsh_[c] = vsh[c]; vsc_[c] = vsc[c]; }
     }
     __syncthreads();
     vg = vg_; vsh = vsh_; vsc = vsc_;
   }
-  for (int i = 0; i < kRows / 4; ++i) {
-    const int r = blockIdx.x * kRows + i * 4 + wave;
+  for (int i = 0; i < kRows / kW; ++i) {
+    const int r = blockIdx.x * kRows + i * kW + wave;
     if (r >= a.rows_per_batch) break;
     const int64_t m = (int64_t)b * a.rows_per_batch + r;
     TO* out = (TO*)a.out + m * a.dim;
@@ -411,8 +416,8 @@ hipError_t launch_rmsnorm_mod(int precision, const NormArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (rows >= 2048) {
     dim3 grid((a.rows_per_batch + kNormRowsPerBlock - 1) / kNormRowsPerBlock, a.batch);
-    if (precision == 0) hipLaunchKernelGGL((rmsnorm_mod_kernel<bf16, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((rmsnorm_mod_kernel<float, true>), grid, dim3(256), 0, s, a);
+    if (precision == 0) hipLaunchKernelGGL((rmsnorm_mod_kernel<bf16, true>), grid, dim3(64 * kNormWaves), 0, s, a);
+    else hipLaunchKernelGGL((rmsnorm_mod_kernel<float, true>), grid, dim3(64 * kNormWaves), 0, s, a);
   } else {
     dim3 grid((a.rows_per_batch + 3) / 4, a.batch);
     if (precision == 0) hipLaunchKernelGGL((rmsnorm_mod_kernel<bf16, false>), grid, dim3(256), 0, s, a);
