@@ -502,9 +502,47 @@ def cpu_baseline(dims):
         O.block(x, w, O.block_mod(c, w), cos, sin, dims)
         flops += block_flops(S, dims.dim, dims.ffn_hidden)
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    rate = flops / dt
+    # the other workloads: the tiny block and the full-width 256 px block timed, the stack step
+    # and the 8-step pass extrapolated from this block's rate (their oracle cost is minutes)
+    per = {"pair_block_1024": {"seconds": round(dt, 2), "tflop": round(flops / 1e12, 3), "measured": True}}
+    for name, wd, S in (("tiny_block", synth.TINY, 96), ("block_256px", dims, 320)):
+        wt = synth.block_weights(wd, 2, 0)
+        c = O.t_condition(np.array([0.5], np.float32), synth.embed_weights(wd, 2), wd)[0]
+        nc = 32 if S == 96 else 64
+        g2 = 8 if S == 96 else 16
+        cos, sin = O.rope_tables(O.position_ids("joint", g2, g2, nc))
+        x = synth.residual_input((S, wd.dim), 2)
+        t1 = time.perf_counter()
+        O.block(x, wt, O.block_mod(c, wt), cos, sin, wd)
+        per[name] = {"seconds": round(time.perf_counter() - t1, 3),
+                     "tflop": round(block_flops(S, wd.dim, wd.ffn_hidden) / 1e12, 5), "measured": True}
+    for name, tf in (("stack_step_1024_cond", 55.61), ("pass_8step_1024", 885.8)):
+        per[name] = {"seconds": round(tf * 1e12 / rate, 1), "tflop": tf, "measured": False,
+                     "note": "extrapolated from the pair block's rate"}
+    return {"value": round(rate / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": "one main block (fp32 NumPy oracle) on the 1024^2 cond/uncond pair, S = 4160 and 4128",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": _cpu_model(), "blas": _blas_name(), "configs": per}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_name():
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in libs) or None
+    except Exception:  # noqa: BLE001
+        return None
 
 
 ENC_METRIC = "text-encoder forwards/s to hidden_states[-2] (35 of 36 Qwen3-4B-shaped blocks, B=2, L_max 64)"
