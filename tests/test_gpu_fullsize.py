@@ -15,7 +15,7 @@
   with the oracle's (Core AI model zoo, "Z-Image-Turbo port", section "Gates": each stage is
   checked against a captured fp32 run, step by step, for both branches).
 
-Gates (the benchmark spec, and the Status page's distribution tolerances): rel-L2 <= 1e-2 and
+Gates (the bf16 path's tolerance, modelled on the Status page's distribution gates): rel-L2 <= 1e-2 and
 mean |gpu - oracle| <= 0.025 RMS(oracle).  The oracle runs here on the host's cores (about a
 minute and a half for the full stack), so these tests are slow.
 """
