@@ -227,3 +227,42 @@ def test_vae_decode_full_size_against_golden(name, h, w):
     img = got[0].astype(np.float64)
     np.testing.assert_allclose(img.mean(axis=(1, 2)), gold["ch_mean"], rtol=0, atol=1e-4 * gold["ch_rms"].max())
     np.testing.assert_allclose(np.sqrt((img ** 2).mean(axis=(1, 2))), gold["ch_rms"], rtol=1e-4)
+
+
+def test_vae_decode_edges_max_batch_and_longest_side():
+    """ZDIT_MAX_BATCH images of a 2 x 2 latent, and the longest supported side (a 256 x 2 latent,
+    a 2048 x 16 image) at full width, both against the oracle."""
+    vd = synth.VAE_TINY
+    note("vae decode: 16 images of a 2 x 2 latent (tiny widths)")
+    W = synth.vae_weights(vd, 30)
+    z = synth.latents((Z.MAX_BATCH, vd.latent_ch, 2, 2), 30)
+    got, _ = _decode(vd, W, z)
+    e = rel_l2(got, V.decoder(z, W, vd))
+    print(f"16 images: rel-L2 {e:.2e}", flush=True)
+    assert e <= 1e-4
+    vd = synth.VAE_FULL
+    note("vae decode: 256 x 2 latent at full width")
+    W = synth.vae_weights(vd, 31)
+    z = synth.latents((1, vd.latent_ch, 256, 2), 31)
+    got, _ = _decode(vd, W, z)
+    assert got.shape == (1, 3, 2048, 16)
+    e = rel_l2(got, V.decoder(z, W, vd, dtype=np.float32))
+    print(f"256 x 2 latent: rel-L2 {e:.2e}", flush=True)
+    assert e <= 1e-4
+
+
+def test_vae_groupnorm_widest_channels():
+    """C = 1024 (one loader thread per channel quad, one pixel row per pass) against the oracle."""
+    B, H, W, C, groups = 2, 8, 8, 1024, 32
+    note("vae groupnorm C=1024")
+    g = _g(32)
+    x = (1.0 + g.standard_normal((B, C, H, W))).astype(np.float32)
+    gam = (1 + 0.1 * g.standard_normal(C)).astype(np.float32)
+    bet = (0.1 * g.standard_normal(C)).astype(np.float32)
+    aff = torch.empty((B, C, 2), device="cuda")
+    ws = Z.workspace(Z.zdit_op_vae_groupnorm_workspace(B, H * W, C, groups))
+    Z.zdit_op_vae_groupnorm(B, H * W, C, groups, 1e-6, dev(nhwc(x)), dev(gam), dev(bet), aff, ws)
+    a = host(aff).astype(np.float64)
+    got = a[:, :, 0, None, None] * x + a[:, :, 1, None, None]
+    ref = V.group_norm(x.astype(np.float64), gam.astype(np.float64), bet.astype(np.float64), groups, 1e-6)
+    assert np.abs(got - ref).max() <= 2e-6 * (np.abs(x).max() * np.abs(a[:, :, 0]).max() + np.abs(a[:, :, 1]).max()) + 1e-7
