@@ -1,9 +1,9 @@
 """zdit_stack_fwd and zdit_sample against the oracle stack and sampler.
 
 The full 2 + 2 + 30 depth is checked at the tiny width (dim 384); full width (dim 3840) is
-checked at reduced depth at 256 px and at 1024^2.  Full width at full depth is covered by the
-bench's properties (finite output, run-to-run bit identity), since the oracle would need
-~55 TFLOP of fp32 CPU work per branch there."""
+checked at reduced depth at 256 px and at 1024^2 here, and at full depth in
+tests/test_gpu_fullsize.py.  Also: two runs of the sampler are bit-identical, and the loop
+resumes exactly from its state (x, step)."""
 import numpy as np
 import pytest
 import torch
@@ -213,3 +213,35 @@ def test_sample_base_recipe_50_steps_cfg4():
     print(f"sample 50 steps g=4: final latent rel-L2 {e:.2e}", flush=True)
     assert e <= 1e-2
     np.testing.assert_array_equal(host(dec), O.unscale(host(x)))
+
+
+def test_sampler_deterministic_and_resumable_from_its_state():
+    """Two zdit_sample runs give the same bits; and the loop's state is (x, step): running
+    steps 0-3 as per-step calls, taking x to the host and back, then steps 4-7 gives the
+    uninterrupted run's final latent bit for bit."""
+    note("sample determinism and resume")
+    dims = synth.TINY
+    case = stack_case(dims, 16, 16, (45, 10), seed=80)
+    cfg = Z.make_cfg(dims)
+    model = Z.upload_model(case["W"])
+    ws = Z.workspace(Z.zdit_sample_workspace(cfg, 16, 16, case["Lmax"], 1.0))
+    runs = []
+    for _ in range(2):
+        x = dev(case["lat"])
+        dec = torch.empty_like(x)
+        Z.zdit_sample(cfg, model, 16, 16, x, dev(case["cap"]), case["Lmax"], case["cap_len"], 1.0, 8, 3.0, dec, ws)
+        runs.append((host(x), host(dec)))
+    np.testing.assert_array_equal(runs[0][0], runs[1][0])
+    np.testing.assert_array_equal(runs[0][1], runs[1][1])
+    sg = Z.zdit_sigmas(8, 3.0)
+    sws = Z.workspace(Z.zdit_stack_workspace(cfg, 2, 16, 16, case["Lmax"]))
+    y = dev(case["lat"])
+    vel = torch.empty((2,) + tuple(y.shape), device="cuda")
+    for i in range(8):
+        if i == 4:
+            y = dev(host(y))   # the saved state: the fp32 latent and the step index
+        ti = float(np.float32(1.0) - np.float32(sg[i]))
+        Z.zdit_stack_fwd(cfg, model, 2, 16, 16, y, 0, dev(case["cap"]), case["Lmax"], case["cap_len"], [ti, ti],
+                         vel, sws)
+        Z.zdit_euler_step(y, vel[0], vel[1], y.numel(), 1.0, sg[i], sg[i + 1])
+    np.testing.assert_array_equal(host(y), runs[0][0])
