@@ -20,8 +20,8 @@ constexpr int kVN = 128;     // output channels per tile
 constexpr int kVK = 16;      // channels of one tap per K step
 constexpr int kVLd = 16;     // LDS row: the 16 channels of a K step, 64 bytes
 
-// 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 2) & 3): a wave's fragment reads (16
-// rows x one chunk) and the loaders' writes (8 rows x two chunks) then hit distinct banks.
+// 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 2) & 3), as in the bf16 GEMM: a wave's
+// fragment reads (16 consecutive rows, one chunk each) cover all banks.
 __device__ inline int vlds(int r, int c) { return r * kVLd + ((c ^ ((r >> 2) & 3)) << 2); }
 
 // SiLU with the hardware exp2 and reciprocal (each within a few ulp): t / (1 + e^-t)

@@ -45,10 +45,10 @@ zdit_status check_shape(int batch, int lat_h, int lat_w) {
 
 bool ok_ptr(const void* p) { return p && aligned16(p); }
 
-// Stage widths in decoder order and the shapes each step runs at.
+// Workspace regions (byte offsets): the NHWC latent, three activation buffers of the largest
+// stage, GroupNorm partials, statistics and affines, and the attention's q/k/v, v^T and scores.
 struct VaePlan {
   size_t lat, X, H, T, part, stat, aff, qkv, vt, S, total;
-  size_t act_floats, part_floats;
 };
 
 int dec_width(const zdit_vae_cfg& c, int i) { return c.widths[3 - i]; }
@@ -73,8 +73,6 @@ VaePlan plan_vae(const zdit_vae_cfg& c, int B, int h, int w) {
   }
   part = std::max(part, vgn_part_floats(B, (int)res, cin));
   const int C = dec_width(c, 0);
-  p.act_floats = (size_t)act;
-  p.part_floats = part;
   size_t off = 0;
   p.lat = off; off += al256((size_t)B * n0 * c.latent_ch * 4);
   p.X = off; off += al256((size_t)act * 4);
