@@ -309,13 +309,19 @@ def encoder_layer_weights(ed: EncDims, seed: int, index: int) -> dict:
     }
 
 
-def encoder_weights(ed: EncDims, seed: int, n_layers: int | None = None) -> dict:
-    """Embedding table (bf16-representable N(0,1) rows) and the first n_layers blocks."""
+def encoder_weights(ed: EncDims, seed: int, n_layers: int | None = None, threads: int | None = None) -> dict:
+    """Embedding table (bf16-representable N(0,1) rows) and the first n_layers blocks (drawn on
+    `threads` threads; each block has its own generators, so the result does not depend on it)."""
     n = ed.n_layers if n_layers is None else n_layers
-    return {
-        "embed": bf16_truncate(_normal(rng(seed, _T_ENC, 1 << 20), (ed.vocab, ed.hidden))),
-        "layers": [encoder_layer_weights(ed, seed, i) for i in range(n)],
-    }
+    embed = bf16_truncate(_normal(rng(seed, _T_ENC, 1 << 20), (ed.vocab, ed.hidden)))
+    if threads is None:
+        threads = min(16, len(os.sched_getaffinity(0))) if n > 4 else 1
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            layers = list(ex.map(lambda i: encoder_layer_weights(ed, seed, i), range(n)))
+    else:
+        layers = [encoder_layer_weights(ed, seed, i) for i in range(n)]
+    return {"embed": embed, "layers": layers}
 
 
 def token_ids(batch: int, max_len: int, lengths, vocab: int, seed: int) -> np.ndarray:

@@ -256,3 +256,46 @@ def test_sampler_teacher_forced_per_step_256px():
         Z.zdit_op_adaln(Z.ZDIT_BF16, 1, dims.c_dim, 6 * dims.dim, dev(c_ref), dev(blk0["w_ada"], torch.bfloat16),
                         dev(blk0["b_ada"]), mod_gpu)
         np.testing.assert_allclose(host(mod_gpu)[0], O.block_mod(c_ref[0], blk0).reshape(-1), rtol=1e-5, atol=1e-5)
+
+
+def test_encoder_full_depth_full_width_per_layer_drift():
+    """The pinned text encoder at its full size: 35 blocks at hidden 2560 (32 / 8 heads,
+    intermediate 9728, distinct weights per block; hidden_states[-2] of the 36-block model) on
+    the DiT's caption lengths, against the encoder oracle after every block.  The gate is the
+    pages' own for this encoder in bf16 (FastVideo commit e4eef6ed20: the per-layer mean drift
+    grows smoothly, consecutive-layer ratio <= 1.5x; reading R18 allows 2x for the first step)
+    with the final mean |gpu - oracle| <= 0.025 RMS; rel-L2 is reported.  Padding rows are
+    zero."""
+    from oracle import encoder_oracle as E
+    ed = synth.ENC_FULL.replace(vocab=4096)
+    lens = [45, 10]
+    nb = ed.n_layers - 1
+    note("text encoder full depth: weights (35 blocks, ~7 GB bf16) and the oracle's 35 hidden states")
+    t0 = time.perf_counter()
+    W = synth.encoder_weights(ed, 15, nb)
+    ids = synth.token_ids(2, 64, lens, ed.vocab, 16)
+    hs = [E.encoder_hidden_states(ids[b, :L], W, ed, nb) for b, L in enumerate(lens)]
+    print(f"weights + oracle: {time.perf_counter() - t0:.1f} s", flush=True)
+    note("text encoder full depth: GPU forwards at depths 1..35")
+    m = Z.upload_encoder(W)
+    del W
+    out = torch.empty((2, 64, ed.hidden), device="cuda")
+    ws = Z.workspace(Z.zdit_encoder_workspace(Z.make_enc_cfg(ed), 2, 64))
+    drifts = [[], []]
+    for d in range(1, nb + 1):
+        out.fill_(3.0)
+        Z.zdit_encoder_fwd(Z.make_enc_cfg(ed.replace(n_layers=d + 1)), m, 2, 64, ids, lens, out, ws)
+        got = host(out)
+        for b, L in enumerate(lens):
+            drifts[b].append(drift(got[b, :L], hs[b][d]))
+            if d == nb:
+                e = rel_l2(got[b, :L], hs[b][d])
+                print(f"encoder 35 blocks branch {b}: rel-L2 {e:.2e} drift {drifts[b][-1]:.2e}", flush=True)
+                assert np.all(got[b, L:] == 0)
+    for b in range(2):
+        dr = drifts[b]
+        ratios = [dr[i] / dr[i - 1] for i in range(1, len(dr))]
+        print(f"branch {b} drift by block: " + " ".join(f"{x:.2e}" for x in dr), flush=True)
+        print(f"branch {b} ratios: first {ratios[0]:.2f}, max after {max(ratios[1:]):.2f}", flush=True)
+        assert dr[-1] <= GATE_DRIFT
+        assert ratios[0] <= 2.0 and max(ratios[1:]) <= 1.5
