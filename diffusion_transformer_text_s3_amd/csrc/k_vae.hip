@@ -49,11 +49,10 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int z = blockIdx.z;
-  const float* A = a.A + (int64_t)z * a.a_bstride;
-  const float* B = a.B + (int64_t)z * a.b_bstride;
-  float* C = a.C + (int64_t)z * a.c_bstride;
-  const float* R = a.res ? a.res + (int64_t)z * a.c_bstride : nullptr;
+  const float* A = a.A;
+  const float* B = a.B;
+  float* C = a.C;
+  const float* R = a.res;
   const int hw = a.H * a.W;
 
   // A loader: tile row lr, channels 4 FA lh .. of the step; B loader: row br, part bh
@@ -312,17 +311,16 @@ __global__ __launch_bounds__(256) void vsoftmax_kernel(float* S, int n) {
   for (int j = tid; j < n; j += 256) row[j] = expf(row[j] - mx) / sm;
 }
 
-__global__ void vtranspose_kernel(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int n, int C) {
+__global__ void vtranspose_kernel(const float* in, int64_t ld, int c0, float* out, int n, int C) {
   __shared__ float t[32][33];
-  const int b = blockIdx.z;
   const int j0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
-  const float* src = in + (int64_t)b * in_bstride + c0;
+  const float* src = in + c0;
   for (int r = threadIdx.y; r < 32; r += 8) {
     const int j = j0 + r, c = k0 + threadIdx.x;
     t[r][threadIdx.x] = (j < n && c < C) ? src[(int64_t)j * ld + c] : 0.f;
   }
   __syncthreads();
-  float* dst = out + (int64_t)b * C * n;
+  float* dst = out;
   for (int r = threadIdx.y; r < 32; r += 8) {
     const int c = k0 + r, j = j0 + threadIdx.x;
     if (c < C && j < n) dst[(int64_t)c * n + j] = t[threadIdx.x][r];
@@ -334,10 +332,10 @@ __global__ void vtranspose_kernel(const float* in, int64_t ld, int64_t in_bstrid
 hipError_t launch_vconv(const VConvArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.N <= 16) {  // the output conv (3 channels): 256 x 16 tiles
-    dim3 grid((a.M + 255) / 256, 1, a.batch);
+    dim3 grid((a.M + 255) / 256, 1);
     hipLaunchKernelGGL((vconv_kernel<256, 16>), grid, dim3(256), 0, s, a);
   } else {
-    dim3 grid((a.M + kVM - 1) / kVM, (a.N + kVN - 1) / kVN, a.batch);
+    dim3 grid((a.M + kVM - 1) / kVM, (a.N + kVN - 1) / kVN);
     hipLaunchKernelGGL((vconv_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
@@ -375,10 +373,9 @@ hipError_t launch_vsoftmax(float* S, int64_t rows, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_vtranspose(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int batch, int n,
-                             int C, hipStream_t s) {
-  dim3 grid((n + 31) / 32, (C + 31) / 32, batch);
-  hipLaunchKernelGGL(vtranspose_kernel, grid, dim3(32, 8), 0, s, in, ld, in_bstride, c0, out, n, C);
+hipError_t launch_vtranspose(const float* in, int64_t ld, int c0, float* out, int n, int C, hipStream_t s) {
+  dim3 grid((n + 31) / 32, (C + 31) / 32);
+  hipLaunchKernelGGL(vtranspose_kernel, grid, dim3(32, 8), 0, s, in, ld, c0, out, n, C);
   return hipGetLastError();
 }
 

@@ -14,18 +14,14 @@ namespace zdit {
 // pixels and is read at half the coordinates), rows of `lda` floats; if `affine` is set each
 // input value becomes a * x + d with (a, d) = affine[img][c] (then SiLU if `silu`) before the
 // product, padding staying zero.  B holds weights [N][ksize * ksize * K] (ldb floats per row).
-// GEMM mode (ksize 1, H = 1, W = M, grid z = batch): plain row-major operands with batch
-// strides.  res may alias C (each element is read before it is written by the same thread).
+// GEMM mode (ksize 1, H = 1, W = M): plain row-major operands.  res may alias C (each element is read before it is written by the same thread).
 // N <= 16 runs 256 x 16 tiles (the output conv), else 128 x 128.
 struct VConvArgs {
   const float* A;
-  int64_t a_bstride;
   int64_t lda;
   const float* B;
-  int64_t b_bstride;
   int64_t ldb;
   float* C;
-  int64_t c_bstride;
   int64_t ldc;
   const float* res;
   const float* bias;
@@ -34,7 +30,6 @@ struct VConvArgs {
   int M, N, K;          // K = channels per tap
   int H, W;             // output image size (conv mode)
   int ksize, upsample;
-  int batch;            // grid z (GEMM mode), 1 in conv mode
   int out_nchw;         // conv mode: C is [images][N][H][W] (ldc unused)
   float alpha;
 };
@@ -64,8 +59,7 @@ hipError_t launch_vlatent_in(const float* z, float* out, int images, int ch, int
                              float scale, float shift, hipStream_t s);
 // rows of S [rows][n] in place: exp(s - max) / sum
 hipError_t launch_vsoftmax(float* S, int64_t rows, int n, hipStream_t s);
-// out[b][c][j] = in[b][j][c0 + c] (in rows of ld floats), c < C, j < n
-hipError_t launch_vtranspose(const float* in, int64_t ld, int64_t in_bstride, int c0, float* out, int batch, int n,
-                             int C, hipStream_t s);
+// out[c][j] = in[j][c0 + c] (in rows of ld floats), c < C, j < n
+hipError_t launch_vtranspose(const float* in, int64_t ld, int c0, float* out, int n, int C, hipStream_t s);
 
 }  // namespace zdit

@@ -107,7 +107,7 @@ hipError_t conv(const Ctx& x, const float* in, int H, int W, int cin, int cout, 
   a.C = out; a.ldc = cout;
   a.res = res; a.bias = cw.b; a.affine = aff; a.silu = silu;
   a.M = x.B * H * W; a.N = cout; a.K = cin; a.H = H; a.W = W;
-  a.ksize = ksize; a.upsample = up; a.batch = 1; a.alpha = 1.f;
+  a.ksize = ksize; a.upsample = up; a.alpha = 1.f;
   return launch_vconv(a, x.st);
 }
 
@@ -149,16 +149,16 @@ hipError_t attention(const Ctx& x, float* X, float* Hb, int H, int W, int C, con
     s.A = qb; s.lda = 3 * C;
     s.B = qb + C; s.ldb = 3 * C;
     s.C = S; s.ldc = N;
-    s.M = N; s.N = N; s.K = C; s.H = 1; s.W = N; s.ksize = 1; s.batch = 1;
+    s.M = N; s.N = N; s.K = C; s.H = 1; s.W = N; s.ksize = 1;
     s.alpha = 1.0f / sqrtf((float)C);
     if (hipError_t e = launch_vconv(s, x.st)) return e;
     if (hipError_t e = launch_vsoftmax(S, N, N, x.st)) return e;
-    if (hipError_t e = launch_vtranspose(qb, 3 * C, 0, 2 * C, vt, 1, N, C, x.st)) return e;
+    if (hipError_t e = launch_vtranspose(qb, 3 * C, 2 * C, vt, N, C, x.st)) return e;
     VConvArgs o{};
     o.A = S; o.lda = N;
     o.B = vt; o.ldb = N;
     o.C = Hb + (int64_t)b * N * C; o.ldc = C;
-    o.M = N; o.N = C; o.K = N; o.H = 1; o.W = N; o.ksize = 1; o.batch = 1; o.alpha = 1.f;
+    o.M = N; o.N = C; o.K = N; o.H = 1; o.W = N; o.ksize = 1; o.alpha = 1.f;
     if (hipError_t e = launch_vconv(o, x.st)) return e;
   }
   return conv(x, Hb, H, W, C, C, 1, 0, nullptr, 0, at.out, X, X);
@@ -300,7 +300,7 @@ zdit_status zdit_op_vae_conv(int32_t batch, int32_t H, int32_t W, int32_t cin, i
   a.C = out; a.ldc = cout;
   a.res = res; a.bias = b; a.affine = affine; a.silu = silu ? 1 : 0;
   a.M = batch * H * W; a.N = cout; a.K = cin; a.H = H; a.W = W;
-  a.ksize = ksize; a.upsample = upsample ? 1 : 0; a.batch = 1; a.alpha = 1.f;
+  a.ksize = ksize; a.upsample = upsample ? 1 : 0; a.alpha = 1.f;
   HIP_TRY(launch_vconv(a, (hipStream_t)hip_stream));
   return ok();
 }
@@ -317,7 +317,7 @@ zdit_status zdit_op_vae_conv_out(int32_t batch, int32_t H, int32_t W, int32_t ci
   a.C = image; a.out_nchw = 1;
   a.bias = b; a.affine = affine; a.silu = 1;
   a.M = batch * H * W; a.N = cout; a.K = cin; a.H = H; a.W = W;
-  a.ksize = 3; a.batch = 1; a.alpha = 1.f;
+  a.ksize = 3; a.alpha = 1.f;
   HIP_TRY(launch_vconv(a, (hipStream_t)hip_stream));
   return ok();
 }
