@@ -804,7 +804,7 @@ def vae_bench(args):
         "roofline": {"kernel": f"vconv_kernel (3x3 conv {C} -> {C} at {Hc}x{Wc}, GroupNorm affine + SiLU fused)",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "avg_launch_ms": round(c_avg, 4),
-                     "flop_per_launch": c_fl, "launches": len(c_ms), "traffic": None},
+                     "flop_per_launch": c_fl, "launches": len(c_ms), "traffic": traffic_from_profiles("vae_conv")},
         "output_finite": finite,
     }
     if not args.no_cpu_baseline:
