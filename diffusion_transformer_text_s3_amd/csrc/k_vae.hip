@@ -27,6 +27,39 @@ __device__ inline int vlds(int r, int c) { return r * kVLd + ((c ^ ((r >> 2) & 3
 // SiLU with the hardware exp2 and reciprocal (each within a few ulp): t / (1 + e^-t)
 __device__ inline float silu_f(float t) { return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
 
+// The result tile of one wave: rows m_base + 16 i + 4 (l / 16) + e, columns n_base + 16 j + l % 16
+// of each 16 x 16 MFMA tile (lane l, register e): alpha * acc + bias (+ the residual), NHWC rows of
+// ldc floats or NCHW planes.
+template <int RJ>
+__device__ __forceinline__ void vconv_epilogue(const VConvArgs& a, const f4 (&acc)[4][RJ], int m_base, int n_base,
+                                               int lane) {
+  const int fr = lane & 15, fk = 4 * (lane >> 4);
+  const int hw = a.H * a.W;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int n = n_base + 16 * j + fr;
+      if (n >= a.N) continue;
+      const float bv = a.bias ? a.bias[n] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m_base + 16 * i + fk + e;
+        if (m >= a.M) continue;
+        int64_t o;
+        if (a.out_nchw) {
+          const int im = m / hw;
+          o = ((int64_t)im * a.N + n) * hw + (m - im * hw);
+        } else {
+          o = (int64_t)m * a.ldc + n;
+        }
+        float v = a.alpha * acc[i][j][e] + bv;
+        if (a.res) v = a.res[o] + v;
+        a.C[o] = v;
+      }
+    }
+}
+
 // 256 threads = 4 wavefronts, each owning 64 rows x (BN / (4 / (BM / 64))) columns of the
 // BM x BN output tile as 16 x 16 MFMA tiles: BM = BN = 128 (a 2 x 2 wave grid, 64 x 64 per
 // wave, 64 fp32 accumulators per lane) for the convolutions and GEMMs, BM = 256, BN = 16 (4 x 1,
@@ -51,8 +84,6 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const float* A = a.A;
   const float* B = a.B;
-  float* C = a.C;
-  const float* R = a.res;
   const int hw = a.H * a.W;
 
   // A loader: tile row lr, channels 4 FA lh .. of the step; B loader: row br, part bh
@@ -120,12 +151,15 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
 #pragma unroll
     for (int j = 0; j < FA; ++j) {
       f4 v = ra[j];
-      if (aff && aval && ac + 4 * j < a.K) {
+      if (aff) {  // uniform; the per-lane choice is a select, so no copies of v are made early
+        const bool tr = aval && ac + 4 * j < a.K;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f4 ad = rf[2 * j + (e >> 1)];
           const float t = fmaf(ad[2 * (e & 1)], v[e], ad[2 * (e & 1) + 1]);
-          v[e] = a.silu ? silu_f(t) : t;
+          float y = a.silu ? silu_f(t) : t;
+          asm volatile("" : "+v"(y));  // computed on every lane: the choice below stays a select
+          v[e] = tr ? y : v[e];
         }
       }
       *(f4*)&sA[buf][vlds(lr, FA * lh + j)] = v;
@@ -137,7 +171,7 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
   };
 
   const int wm0 = (wave % WGM) * 64, wn0 = (wave / WGM) * (BN / WGN);
-  const int fr = lane & 15, fk = 4 * (lane >> 4), fc = lane >> 4;
+  const int fr = lane & 15, fc = lane >> 4;
   f4 acc[4][RJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -162,34 +196,208 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
 #pragma unroll
         for (int j = 0; j < RJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
+    // The wait for the next step's loads stays below the MFMAs.  The transform and LDS stores
+    // run at raised wave priority: the other workgroups on the CU are then in their MFMA
+    // phases, and this wave gets back to its own MFMAs sooner.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     if (s + 1 < nsteps) store(buf ^ 1);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
 
-  // lane l holds rows 4 * (l / 16) + e, column l % 16 of each 16 x 16 result tile
+  vconv_epilogue<RJ>(a, acc, m0 + wm0, n0 + wn0, lane);
+}
+
+// ------------------------------------------------------------ convolution, direct-to-LDS form
+// The same tiles, K steps, LDS layout, fragment reads and MFMA order as vconv_kernel<128, 128>
+// (so the same sums in the same order), for inputs that need no transform: the A and B tiles
+// go from memory straight into LDS with buffer loads (buffer_load_dword ... lds), no staging
+// registers, selects or LDS stores, and two steps ahead through a ring of three 16 KB stages.
+// The fp32 MFMA shares its issue cycles with the vector ALU, so the fewer vector instructions
+// per MFMA the better.
+// Each operand is read through a buffer resource over the rows one tile can touch (bounds
+// checked by the hardware): a lane's offset is past the end for output rows past M, for taps
+// outside the image and for weight rows past N, and such a load returns zeros.  A lane's A
+// offsets change only when the tap does; the channel step is the scalar offset.
+constexpr int kDStage = 2 * kVM * kVLd;  // floats: A rows, then B rows
+constexpr int kBufFlags = 0x00020000;   // raw (offset-addressed) buffer, word 3
+constexpr int kOob = 0x7ffffff0;        // an offset past every resource's end
+// s_waitcnt immediate waiting for vmcnt <= n only (expcnt and lgkmcnt fields at their maximum)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__device__ __forceinline__ void vdma16(__amdgpu_buffer_rsrc_t rs, float* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void vbarrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Source pixels (within the tile's image) that the tile's output rows read: [lo, hi).
+struct VSpan {
+  int img, lo, hi;
+};
+__device__ __forceinline__ VSpan vconv_span(const VConvArgs& a, int m0) {
+  const int hw = a.H * a.W;
+  VSpan sp;
+  sp.img = m0 / hw;
+  const int p0 = m0 - sp.img * hw;                   // first output pixel in the image
+  const int p1 = min(m0 + kVM, min(a.M, (sp.img + 1) * hw)) - 1 - sp.img * hw;  // last
+  const int rad = a.ksize >> 1;
+  const int Ws = a.upsample ? a.W >> 1 : a.W;
+  if (a.H == 1) {  // one row per image (GEMM mode): columns
+    int x0 = max(0, p0 - rad), x1 = min(a.W - 1, p1 + rad);
+    if (a.upsample) { x0 >>= 1; x1 >>= 1; }
+    sp.lo = x0;
+    sp.hi = x1 + 1;
+  } else {
+    int y0 = max(0, p0 / a.W - rad), y1 = min(a.H - 1, p1 / a.W + rad);
+    if (a.upsample) { y0 >>= 1; y1 >>= 1; }
+    sp.lo = y0 * Ws;
+    sp.hi = (y1 + 1) * Ws;
+  }
+  return sp;
+}
+
+__global__ __launch_bounds__(256) void vconv_direct_kernel(VConvArgs a) {
+  __shared__ __attribute__((aligned(16))) float st0[kDStage];
+  __shared__ __attribute__((aligned(16))) float st1[kDStage];
+  __shared__ __attribute__((aligned(16))) float st2[kDStage];
+  const int tid = threadIdx.x;
+  // the wave index in a scalar register: the LDS destinations of the loads are then scalar
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = blockIdx.x * kVM, n0 = blockIdx.y * kVN;
+  const int hw = a.H * a.W;
+  const int rad = a.ksize >> 1;
+  const int Hs = a.upsample ? a.H >> 1 : a.H, Ws = a.upsample ? a.W >> 1 : a.W;
+  const int csteps = a.K / kVK;  // K % 16 == 0 on this path
+  const int nsteps = a.ksize * a.ksize * csteps;
+
+  const VSpan sp = vconv_span(a, m0);
+  const float* Abase = a.A + ((int64_t)sp.img * Hs * Ws + sp.lo) * a.lda;
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Abase, 0, (int)((int64_t)(sp.hi - sp.lo) * a.lda * 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.B + (int64_t)n0 * a.ldb), 0, (int)((int64_t)min(a.N - n0, kVN) * a.ldb * 4), kBufFlags);
+
+  // This wave loads 16-row blocks 2 wave and 2 wave + 1 of A and of B; one instruction puts
+  // lane L at slot L of the block (row L / 4, 16-byte slot L % 4), so lane L fetches the
+  // logical chunk whose swizzled slot that is.
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  int py[2], px[2], voa[2], vob[2];
+  bool mok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * wave + i) * 16 + (lane >> 2);
+    const int m = m0 + r;
+    mok[i] = m < a.M;
+    const int p = m - sp.img * hw;
+    py[i] = p / a.W;
+    px[i] = p - py[i] * a.W;
+    const int n = n0 + r;
+    vob[i] = n < a.N ? (int)(r * a.ldb * 4) + lchunk * 16 : kOob;
+  }
+  // A offsets of the tap (ky, kx)
+  auto tap_offsets = [&](int ky, int kx) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int yy = py[i] + ky - rad, xx = px[i] + kx - rad;
+      const bool ok = mok[i] && yy >= 0 && yy < a.H && xx >= 0 && xx < a.W;
+      const int ys = a.upsample ? yy >> 1 : yy, xs = a.upsample ? xx >> 1 : xx;
+      voa[i] = ok ? (ys * Ws + xs - sp.lo) * (int)a.lda * 4 + lchunk * 16 : kOob;
+    }
+  };
+
+  // issue position: tap (iky, ikx), channel step ics; past the last step the last one repeats
+  // (into a stage no one reads again) so that every step has the same number of loads
+  int iky = 0, ikx = 0, itap = 0, ics = 0, issued = 0;
+  tap_offsets(0, 0);
+  auto issue = [&](float* stage) {
+    const int soa = ics * kVK * 4, sob = (itap * a.K + ics * kVK) * 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vdma16(rsa, stage + (2 * wave + i) * 16 * kVLd, voa[i], soa);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) vdma16(rsb, stage + (kVM + (2 * wave + i) * 16) * kVLd, vob[i], sob);
+    if (++issued < nsteps) {
+      if (++ics == csteps) {
+        ics = 0;
+        ++itap;
+        if (++ikx == a.ksize) {
+          ikx = 0;
+          ++iky;
+        }
+        tap_offsets(iky, ikx);
+      }
+    }
+  };
+
+  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
+  const int fr = lane & 15, fc = lane >> 4;
+  f4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      const int n = n0 + wn0 + 16 * j + fr;
-      if (n >= a.N) continue;
-      const float bv = a.bias ? a.bias[n] : 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // one step: this wave's loads of the step have landed (the next step's four may still be in
+  // flight), the barrier makes every wave's visible and frees the stage read in the step
+  // before, which takes the loads of two steps ahead
+  auto step = [&](const float* cur, float* freed) {
+    __builtin_amdgcn_s_waitcnt(vm_wait(4));
+    vbarrier();
+    issue(freed);
+    const float* sA = cur;
+    const float* sB = cur + kVM * kVLd;
+    f4 af[4], bf[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm0 + 16 * i + fk + e;
-        if (m >= a.M) continue;
-        int64_t o;
-        if (a.out_nchw) {
-          const int im = m / hw;
-          o = ((int64_t)im * a.N + n) * hw + (m - im * hw);
-        } else {
-          o = (int64_t)m * a.ldc + n;
-        }
-        float v = a.alpha * acc[i][j][e] + bv;
-        if (R) v = R[o] + v;
-        C[o] = v;
-      }
+    for (int i = 0; i < 4; ++i) af[i] = *(const f4*)&sA[vlds(wm0 + 16 * i + fr, fc)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = *(const f4*)&sB[vlds(wn0 + 16 * j + fr, fc)];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
+  };
+
+  issue(st0);
+  issue(st1);
+  int s = 0;
+  for (; s + 3 <= nsteps; s += 3) {
+    step(st0, st2);
+    step(st1, st0);
+    step(st2, st1);
+  }
+  if (s < nsteps) step(st0, st2);
+  if (s + 1 < nsteps) step(st1, st0);
+  // the loads past the end are still landing in dead stages: drain them before the wave ends
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  vconv_epilogue<4>(a, acc, m0 + wm0, n0 + wn0, lane);
+}
+
+// out = SiLU(a x + d) (silu != 0) or a x + d per (image, channel), with the affine of
+// [images][C][2]; the same arithmetic as the transform of vconv_kernel.  out may alias x.
+__global__ __launch_bounds__(256) void vact_kernel(const float* x, const float* affine, int64_t quads_per_image,
+                                                   int cq, int64_t quads, int silu, float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+    const int64_t img = i / quads_per_image;
+    const int q = (int)(i & (cq - 1));
+    const float* ad = affine + (img * cq * 4 + 4 * q) * 2;
+    const f4 ad0 = *(const f4*)ad, ad1 = *(const f4*)(ad + 4);
+    f4 v = *(const f4*)(x + 4 * i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f4 p = e < 2 ? ad0 : ad1;
+      const float t = fmaf(p[2 * (e & 1)], v[e], p[2 * (e & 1) + 1]);
+      v[e] = silu ? silu_f(t) : t;
     }
+    *(f4*)(out + 4 * i) = v;
+  }
 }
 
 // ------------------------------------------------------------------------------ GroupNorm
@@ -336,8 +544,36 @@ hipError_t launch_vconv(const VConvArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((vconv_kernel<256, 16>), grid, dim3(256), 0, s, a);
   } else {
     dim3 grid((a.M + kVM - 1) / kVM, (a.N + kVN - 1) / kVN);
-    hipLaunchKernelGGL((vconv_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
+    if (vconv_direct_ok(a))
+      hipLaunchKernelGGL(vconv_direct_kernel, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((vconv_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+bool vconv_direct_ok(const VConvArgs& a) {
+  if (a.affine || a.N <= 16 || a.K % kVK || a.lda % 4 || a.ldb % 4) return false;
+  if (((uintptr_t)a.A | (uintptr_t)a.B) & 15) return false;
+  const int64_t hw = (int64_t)a.H * a.W;
+  if (a.M != hw && hw % kVM) return false;  // a tile lies in one image
+  // the largest span of source rows a tile can read, in bytes, within a 32-bit buffer offset
+  const int64_t Ws = a.upsample ? a.W / 2 : a.W;
+  const int rad = a.ksize / 2;
+  const int64_t px = a.H == 1 ? kVM + 2 * rad : (kVM / a.W + 2 + 2 * rad) * Ws;
+  const int64_t limit = (int64_t)0x7fffffff - 4096;
+  if (px * a.lda * 4 > limit || (int64_t)kVN * a.ldb * 4 > limit) return false;
+  if ((int64_t)a.ksize * a.ksize * a.K * 4 > limit) return false;
+  return true;
+}
+
+hipError_t launch_vact(const float* x, const float* affine, int images, int64_t hw, int C, int silu, float* out,
+                       hipStream_t s) {
+  const int64_t quads = (int64_t)images * hw * C / 4;
+  if (quads == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((quads + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(vact_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, affine, hw * C / 4, C / 4, quads,
+                     silu, out);
   return hipGetLastError();
 }
 

@@ -52,6 +52,14 @@ int vgn_chunks(int HW, int C);
 size_t vgn_part_floats(int images, int HW, int C);
 
 hipError_t launch_vconv(const VConvArgs& a, hipStream_t s);
+// whether launch_vconv runs the direct-to-LDS form (no input transform, channels a multiple of
+// 16, a tile within one image, buffer offsets within 32 bits); otherwise the staged form
+bool vconv_direct_ok(const VConvArgs& a);
+// out = SiLU(a x + d) (silu != 0) or a x + d over NHWC x [images][hw][C], affine [images][C][2]
+// (C a power of two, at least 4); bit-identical to the staged conv's input transform; out may
+// alias x
+hipError_t launch_vact(const float* x, const float* affine, int images, int64_t hw, int C, int silu, float* out,
+                       hipStream_t s);
 hipError_t launch_vgn(VGnArgs a, hipStream_t s);   // stats + affine (two passes over x)
 // latent [images][ch][h][w] -> NHWC [images][h][w][ch], each value z / scale + shift (unscale
 // != 0) or copied

@@ -119,21 +119,26 @@ hipError_t gnorm(const Ctx& x, const float* in, int hw, int C, const zdit_vae_no
   return launch_vgn(a, x.st);
 }
 
-// x (in *X) -> *X, through H and (width change) T; swaps the buffers it leaves the result in
+// x (in *X) -> *X, through H and (width change) T; swaps the buffers it leaves the result in.
+// Each convolution's input SiLU(GroupNorm(.)) is written once (launch_vact) and read by the
+// direct-to-LDS convolution: conv1's into T (free until the shortcut is written there), conv2's
+// over H in place.
 hipError_t resnet(const Ctx& x, float*& X, float*& Hb, float*& T, int H, int W, int cin, int cout,
                   const zdit_vae_resnet& r) {
   const int hw = H * W;
   float* aff = x.f(x.pl.aff);
   if (hipError_t e = gnorm(x, X, hw, cin, r.gn1)) return e;
-  if (hipError_t e = conv(x, X, H, W, cin, cout, 3, 0, aff, 1, r.conv1, nullptr, Hb)) return e;
+  if (hipError_t e = launch_vact(X, aff, x.B, hw, cin, 1, T, x.st)) return e;
+  if (hipError_t e = conv(x, T, H, W, cin, cout, 3, 0, nullptr, 0, r.conv1, nullptr, Hb)) return e;
   if (hipError_t e = gnorm(x, Hb, hw, cout, r.gn2)) return e;
+  if (hipError_t e = launch_vact(Hb, aff, x.B, hw, cout, 1, Hb, x.st)) return e;
   if (r.shortcut.w) {
     if (hipError_t e = conv(x, X, H, W, cin, cout, 1, 0, nullptr, 0, r.shortcut, nullptr, T)) return e;
-    if (hipError_t e = conv(x, Hb, H, W, cout, cout, 3, 0, aff, 1, r.conv2, T, T)) return e;
+    if (hipError_t e = conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, T, T)) return e;
     std::swap(X, T);
     return hipSuccess;
   }
-  return conv(x, Hb, H, W, cout, cout, 3, 0, aff, 1, r.conv2, X, X);
+  return conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, X, X);
 }
 
 hipError_t attention(const Ctx& x, float* X, float* Hb, int H, int W, int C, const zdit_vae_attn& at) {
@@ -141,8 +146,10 @@ hipError_t attention(const Ctx& x, float* X, float* Hb, int H, int W, int C, con
   float* qkv = x.f(x.pl.qkv);
   float* vt = x.f(x.pl.vt);
   float* S = x.f(x.pl.S);
+  // GroupNorm(x) into H (free until P v is written there), then the q/k/v map
   if (hipError_t e = gnorm(x, X, N, C, at.gn)) return e;
-  if (hipError_t e = conv(x, X, H, W, C, 3 * C, 1, 0, x.f(x.pl.aff), 0, at.qkv, nullptr, qkv)) return e;
+  if (hipError_t e = launch_vact(X, x.f(x.pl.aff), x.B, N, C, 0, Hb, x.st)) return e;
+  if (hipError_t e = conv(x, Hb, H, W, C, 3 * C, 1, 0, nullptr, 0, at.qkv, nullptr, qkv)) return e;
   for (int b = 0; b < x.B; ++b) {
     const float* qb = qkv + (int64_t)b * N * 3 * C;
     VConvArgs s{};
@@ -255,7 +262,8 @@ zdit_status zdit_vae_decode(const zdit_vae_cfg* cfg, const zdit_vae_w* w, int32_
     cin = co;
   }
   HIP_TRY(gnorm(x, X, H * W, cl, w->norm_out));
-  HIP_TRY(conv(x, X, H, W, cl, c.out_ch, 3, 0, x.f(pl.aff), 1, w->conv_out, nullptr, image, 1));
+  HIP_TRY(launch_vact(X, x.f(pl.aff), batch, (int64_t)H * W, cl, 1, T, st));
+  HIP_TRY(conv(x, T, H, W, cl, c.out_ch, 3, 0, nullptr, 0, w->conv_out, nullptr, image, 1));
   return ok();
 }
 

@@ -53,6 +53,17 @@ CONV_CASES = [
     (1, 32, 32, 512, 512, 3, 0, True, True),    # full width, 8 M tiles x 4 N tiles, K = 4608
     (1, 20, 18, 32, 16, 3, 0, True, True),      # N <= 16: the 256 x 16 tile form, two M tiles with a tail
     (2, 7, 9, 64, 3, 1, 0, False, False),       # 256 x 16 tiles, 3 of 16 columns stored
+    # no input transform: the direct-to-LDS form where a tile lies in one image
+    (2, 16, 16, 64, 96, 3, 0, False, False),    # two images of 256 pixels, N < 128
+    (1, 24, 20, 256, 136, 3, 0, False, True),   # one image, ragged M tail, N tail of 8, residual
+    (1, 32, 32, 512, 512, 3, 0, False, True),   # full width, K = 4608, residual in place
+    (2, 16, 32, 128, 128, 3, 1, False, False),  # two images, upsample from 8 x 16
+    (3, 16, 8, 48, 128, 3, 0, False, False),    # 128-pixel images, three channel steps per tap
+    (1, 1, 200, 64, 130, 1, 0, False, False),   # one-row image, 1x1
+    (1, 1, 300, 32, 64, 3, 0, False, False),    # one-row image, 3x3 (rows above and below are padding)
+    # no transform, staged form: channels not a multiple of 16; images that split a tile
+    (1, 8, 8, 20, 64, 3, 0, False, False),
+    (2, 8, 24, 64, 160, 3, 0, False, False),
 ]
 
 
@@ -86,6 +97,27 @@ def test_vae_conv_matches_oracle(case):
     tol = 2e-6 * bound + 1e-6 * (np.abs(ref) + 1)
     print(f"conv: max |err| {err.max():.2e}, max err/tol {(err / tol).max():.3f}", flush=True)
     assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("B,H,W,cin,cout,k,up", [(2, 16, 16, 64, 96, 3, 0), (1, 24, 20, 256, 136, 3, 0),
+                                                   (2, 16, 32, 128, 128, 3, 1), (1, 1, 300, 32, 64, 3, 0)])
+def test_vae_conv_direct_form_bit_identical_to_staged_form(B, H, W, cin, cout, k, up):
+    """Without an input transform the convolution runs in its direct-to-LDS form; with the
+    identity affine (a = 1, d = 0, no SiLU: every value unchanged) it runs in the staged form.
+    Both take the same K steps in the same order, so the results agree bit for bit, residual
+    included."""
+    note(f"vae conv direct vs staged B={B} {H}x{W} {cin}->{cout} k={k} up={up}")
+    g = _g(B + H + W + cin + cout)
+    Hi, Wi = (H // 2, W // 2) if up else (H, W)
+    x = dev(g.standard_normal((B, Hi, Wi, cin)).astype(np.float32))
+    w = Z.vae_conv_weight((g.standard_normal((cout, cin, k, k)) / np.sqrt(cin * k * k)).astype(np.float32))
+    b = dev((0.1 * g.standard_normal(cout)).astype(np.float32))
+    r0 = dev(g.standard_normal((B, H, W, cout)).astype(np.float32))
+    ident = torch.stack([torch.ones((B, cin), device="cuda"), torch.zeros((B, cin), device="cuda")], dim=-1).contiguous()
+    direct, staged = r0.clone(), r0.clone()
+    Z.zdit_op_vae_conv(B, H, W, cin, cout, k, up, x, None, 0, w, b, direct, direct)
+    Z.zdit_op_vae_conv(B, H, W, cin, cout, k, up, x, ident, 0, w, b, staged, staged)
+    assert torch.equal(direct, staged)
 
 
 def test_vae_conv_padding_reads_nothing_outside_the_image():
