@@ -686,8 +686,9 @@ def kernel_only(which):
         ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, Me, D, I))
         for _ in range(3):
             Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, Me, D, I, A, Wd, None, None, X, ws)
-    elif which in ("vae_conv", "vae_upconv"):
-        conv = vae_conv_runner(which == "vae_upconv", stream)
+    elif which in ("vae_conv", "vae_upconv", "vae_conv1024"):
+        conv = (vae_conv_runner(False, stream, 1024, 128, True) if which == "vae_conv1024"
+                else vae_conv_runner(which == "vae_upconv", stream))
         for _ in range(16):
             conv()
     else:
@@ -698,15 +699,15 @@ def kernel_only(which):
     print(f"kernel-only {which}: launches done", flush=True)
 
 
-def vae_conv_runner(upsample, stream):
+def vae_conv_runner(upsample, stream, side=256, C=512, residual=False):
     """One VAE conv at its decode shape: the 3x3 conv 512 -> 512 at 256 x 256 on an input that
     already holds SiLU(GroupNorm(x)) (upsample False; the stage-1 ResNet convs, which the decoder
     runs in the direct-to-LDS form after one activation pass), or the upsample conv 512 -> 512
-    from 256 x 256 to 512 x 512 (upsample True).  Returns the launch function (with .flops)."""
+    from 256 x 256 to 512 x 512 (upsample True); side, C and residual give other decoder shapes
+    (side 1024, C 128, residual: the stage-3 conv2).  Returns the launch function (with .flops)."""
     import torch
     from diffusion_transformer_text_s3_amd import binding as Z
-    C = 512
-    Hc = 512 if upsample else 256
+    Hc = 2 * side if upsample else side
     Hi = Hc // 2 if upsample else Hc
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
@@ -717,7 +718,7 @@ def vae_conv_runner(upsample, stream):
     up = 1 if upsample else 0
 
     def launch():
-        Z.zdit_op_vae_conv(1, Hc, Hc, C, C, 3, up, x, None, 0, wt, bias, None, out, stream)
+        Z.zdit_op_vae_conv(1, Hc, Hc, C, C, 3, up, x, None, 0, wt, bias, out if residual else None, out, stream)
 
     launch.flops = 2 * 9 * C * C * Hc * Hc
     launch.keep = (x, wt, bias, out)
@@ -843,7 +844,7 @@ def main():
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--kernel-only", default=None,
                     choices=["qkv", "attn", "out", "swiglu", "w2", "rmsnorm", "adaln", "euler", "copy", "enc_down",
-                             "vae_conv", "vae_upconv"],
+                             "vae_conv", "vae_upconv", "vae_conv1024"],
                     help="launch only one kernel at its main-block shape on rotating operands (or a plain device "
                          "copy of 170,393,600 bytes, the counter calibration; or the encoder's split-K down "
                          "projection; or a VAE conv at its decode shape), for rocprofv3 --pmc runs")

@@ -29,35 +29,54 @@ __device__ inline float silu_f(float t) { return t * __builtin_amdgcn_rcpf(1.0f 
 
 // The result tile of one wave: rows m_base + 16 i + 4 (l / 16) + e, columns n_base + 16 j + l % 16
 // of each 16 x 16 MFMA tile (lane l, register e): alpha * acc + bias (+ the residual), NHWC rows of
-// ldc floats or NCHW planes.
+// ldc floats or NCHW planes.  The residual values of a 16-row slice are loaded before its first
+// store, so those loads are in flight together (each element is read and written by its own lane
+// only, so a residual that aliases the output is still read before it is overwritten).
 template <int RJ>
 __device__ __forceinline__ void vconv_epilogue(const VConvArgs& a, const f4 (&acc)[4][RJ], int m_base, int n_base,
                                                int lane) {
   const int fr = lane & 15, fk = 4 * (lane >> 4);
   const int hw = a.H * a.W;
+  auto offset = [&](int m, int n) -> int64_t {
+    if (a.out_nchw) {
+      const int im = m / hw;
+      return ((int64_t)im * a.N + n) * hw + (m - im * hw);
+    }
+    return (int64_t)m * a.ldc + n;
+  };
+  float bv[RJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < RJ; ++j) {
+    const int n = n_base + 16 * j + fr;
+    bv[j] = a.bias && n < a.N ? a.bias[n] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the residual of one 16-row slice: 4 RJ loads in flight, then the stores
+    f4 rv[RJ];
+    if (a.res) {
+#pragma unroll
+      for (int j = 0; j < RJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m_base + 16 * i + fk + e, n = n_base + 16 * j + fr;
+          rv[j][e] = m < a.M && n < a.N ? a.res[offset(m, n)] : 0.f;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
       const int n = n_base + 16 * j + fr;
       if (n >= a.N) continue;
-      const float bv = a.bias ? a.bias[n] : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m_base + 16 * i + fk + e;
         if (m >= a.M) continue;
-        int64_t o;
-        if (a.out_nchw) {
-          const int im = m / hw;
-          o = ((int64_t)im * a.N + n) * hw + (m - im * hw);
-        } else {
-          o = (int64_t)m * a.ldc + n;
-        }
-        float v = a.alpha * acc[i][j][e] + bv;
-        if (a.res) v = a.res[o] + v;
-        a.C[o] = v;
+        float v = a.alpha * acc[i][j][e] + bv[j];
+        if (a.res) v = rv[j][e] + v;
+        a.C[offset(m, n)] = v;
       }
     }
+  }
 }
 
 // 256 threads = 4 wavefronts, each owning 64 rows x (BN / (4 / (BM / 64))) columns of the
@@ -262,7 +281,7 @@ __device__ __forceinline__ VSpan vconv_span(const VConvArgs& a, int m0) {
   return sp;
 }
 
-__global__ __launch_bounds__(256) void vconv_direct_kernel(VConvArgs a) {
+__global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
   __shared__ __attribute__((aligned(16))) float st0[kDStage];
   __shared__ __attribute__((aligned(16))) float st1[kDStage];
   __shared__ __attribute__((aligned(16))) float st2[kDStage];
