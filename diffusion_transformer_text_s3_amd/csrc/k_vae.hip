@@ -32,8 +32,8 @@ __device__ inline float silu_f(float t) { return t * __builtin_amdgcn_rcpf(1.0f 
 // ldc floats or NCHW planes.  The residual values of a 16-row slice are loaded before its first
 // store, so those loads are in flight together (each element is read and written by its own lane
 // only, so a residual that aliases the output is still read before it is overwritten).
-template <int RJ>
-__device__ __forceinline__ void vconv_epilogue(const VConvArgs& a, const f4 (&acc)[4][RJ], int m_base, int n_base,
+template <int RJ, bool STATS = false>
+__device__ __forceinline__ void vconv_epilogue(const VConvArgs& a, f4 (&acc)[4][RJ], int m_base, int n_base,
                                                int lane) {
   const int fr = lane & 15, fk = 4 * (lane >> 4);
   const int hw = a.H * a.W;
@@ -74,7 +74,40 @@ __device__ __forceinline__ void vconv_epilogue(const VConvArgs& a, const f4 (&ac
         float v = a.alpha * acc[i][j][e] + bv[j];
         if (a.res) v = rv[j][e] + v;
         a.C[offset(m, n)] = v;
+        if constexpr (STATS) acc[i][j][e] = v;
       }
+    }
+  }
+  if constexpr (STATS) {
+    if (!a.gn_part) return;
+    // GroupNorm statistics of this wave's 64 rows (a half tile), per column: the mean of the
+    // valid rows, then the sum of squared deviations from it.  A column's 64 rows are 16 values
+    // in each of the four lanes l % 16 + 16 g; the lanes combine by two xor exchanges, which
+    // leave the same sum in all four.
+    const int nv = min(max(a.M - m_base, 0), 64);
+    if (nv == 0) return;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t += 16 * i + fk + e < nv ? acc[i][j][e] : 0.f;
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      const float mean = t / (float)nv;
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = 16 * i + fk + e < nv ? acc[i][j][e] - mean : 0.f;
+          q = fmaf(d, d, q);
+        }
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+      const int n = n_base + 16 * j + fr;
+      if (lane < 16 && n < a.N) a.gn_part[(int64_t)(m_base >> 6) * a.N + n] = make_float2(mean, q);
     }
   }
 }
@@ -396,7 +429,93 @@ __global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
   if (s + 1 < nsteps) step(st1, st0);
   // the loads past the end are still landing in dead stages: drain them before the wave ends
   __builtin_amdgcn_s_waitcnt(vm_wait(0));
-  vconv_epilogue<4>(a, acc, m0 + wm0, n0 + wn0, lane);
+  vconv_epilogue<4, true>(a, acc, m0 + wm0, n0 + wn0, lane);
+}
+
+// GroupNorm from the half-tile statistics of a convolution (mean_h, M2_h over n_h rows per
+// channel), combined in float64 with the pairwise update of Chan, Golub and LeVeque: merging
+// (n_a, m_a, M2_a) and (n_b, m_b, M2_b) gives n = n_a + n_b, m = m_a + (m_b - m_a) n_b / n and
+// M2 = M2_a + M2_b + (m_b - m_a)^2 n_a n_b / n.  Every merge runs in a fixed order.
+__device__ __forceinline__ void chan_merge(double& n, double& m, double& q, double nb, double mb, double qb) {
+  const double t = n + nb, d = mb - m;
+  m += d * nb / t;
+  q += qb + d * d * n * nb / t;
+  n = t;
+}
+
+constexpr int kGnChunk = 64;  // half tiles per workgroup of the first level
+
+// First level, one workgroup per (chunk of kGnChunk half tiles, image): per channel (one thread,
+// coalesced over the channels) the chunk's count, mean and M2 (the exact two-sum identity
+// M2 = sum of M2_h + n_h (m_h - m)^2), then per group the channels merged in order.
+__global__ __launch_bounds__(256) void vgn_conv_chunk_kernel(const float2* part, VGnArgs a, double* chunk) {
+  __shared__ double cs[3][1024];
+  const int tid = threadIdx.x;
+  const int ck = blockIdx.x, img = blockIdx.y;
+  const int hpi = (a.HW + 63) / 64;
+  const int h0 = ck * kGnChunk, h1 = min(h0 + kGnChunk, hpi);
+  const float2* p = part + (int64_t)img * hpi * a.C;
+  for (int c = tid; c < a.C; c += 256) {
+    double n = 0.0, sum = 0.0;
+    for (int h = h0; h < h1; ++h) {
+      const double nh = (double)min(64, a.HW - 64 * h);
+      n += nh;
+      sum += nh * (double)p[(int64_t)h * a.C + c].x;
+    }
+    const double m = sum / n;
+    double q = 0.0;
+    for (int h = h0; h < h1; ++h) {
+      const double nh = (double)min(64, a.HW - 64 * h);
+      const float2 v = p[(int64_t)h * a.C + c];
+      const double d = (double)v.x - m;
+      q += (double)v.y + nh * d * d;
+    }
+    cs[0][c] = n;
+    cs[1][c] = m;
+    cs[2][c] = q;
+  }
+  __syncthreads();
+  const int cpg = a.C / a.groups;
+  for (int g = tid; g < a.groups; g += 256) {
+    const int c0 = g * cpg;
+    double n = cs[0][c0], m = cs[1][c0], q = cs[2][c0];
+    for (int cc = 1; cc < cpg; ++cc) chan_merge(n, m, q, cs[0][c0 + cc], cs[1][c0 + cc], cs[2][c0 + cc]);
+    double* o = chunk + (((int64_t)img * gridDim.x + ck) * a.groups + g) * 3;
+    o[0] = n;
+    o[1] = m;
+    o[2] = q;
+  }
+}
+
+// Second level, one workgroup per (group, image): the chunks merged in order, then
+// 1/sqrt(M2 / n + eps) and the per-channel affine, as vgn_finalize_kernel.
+__global__ __launch_bounds__(64) void vgn_conv_final_kernel(const double* chunk, int nck, VGnArgs a) {
+  __shared__ double ms[2];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x, img = blockIdx.y;
+  if (tid == 0) {
+    const double* c = chunk + ((int64_t)img * nck * a.groups + g) * 3;
+    double n = c[0], m = c[1], q = c[2];
+    for (int k = 1; k < nck; ++k) {
+      const double* e = c + (int64_t)k * a.groups * 3;
+      chan_merge(n, m, q, e[0], e[1], e[2]);
+    }
+    const double rstd = 1.0 / sqrt(q / n + (double)a.eps);
+    double* st = a.stat + ((int64_t)img * a.groups + g) * 2;
+    st[0] = m;
+    st[1] = rstd;
+    ms[0] = m;
+    ms[1] = rstd;
+  }
+  __syncthreads();
+  const double mean = ms[0], rstd = ms[1];
+  const int cpg = a.C / a.groups;
+  for (int cc = tid; cc < cpg; cc += 64) {
+    const int c = g * cpg + cc;
+    const double ga = (double)a.gamma[c] * rstd;
+    a.affine[((int64_t)img * a.C + c) * 2] = (float)ga;
+    a.affine[((int64_t)img * a.C + c) * 2 + 1] = (float)((double)a.beta[c] - mean * ga);
+  }
 }
 
 // out = SiLU(a x + d) (silu != 0) or a x + d per (image, channel), with the affine of
@@ -602,6 +721,19 @@ int vgn_chunks(int HW, int C) {
 }
 
 size_t vgn_part_floats(int images, int HW, int C) { return (size_t)images * vgn_chunks(HW, C) * C; }
+
+size_t vgn_conv_chunk_doubles(int images, int HW, int groups) {
+  const int hpi = (HW + 63) / 64;
+  return (size_t)images * ((hpi + kGnChunk - 1) / kGnChunk) * groups * 3;
+}
+
+hipError_t launch_vgn_from_conv(const float2* part, double* chunk, const VGnArgs& a, hipStream_t s) {
+  const int hpi = (a.HW + 63) / 64;
+  const int nck = (hpi + kGnChunk - 1) / kGnChunk;
+  hipLaunchKernelGGL(vgn_conv_chunk_kernel, dim3(nck, a.images), dim3(256), 0, s, part, a, chunk);
+  hipLaunchKernelGGL(vgn_conv_final_kernel, dim3(a.groups, a.images), dim3(64), 0, s, chunk, nck, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_vgn(VGnArgs a, hipStream_t s) {
   a.chunk = std::max(256 / (a.C / 4), 65536 / a.C);

@@ -32,6 +32,10 @@ struct VConvArgs {
   int ksize, upsample;
   int out_nchw;         // conv mode: C is [images][N][H][W] (ldc unused)
   float alpha;
+  // direct-to-LDS form only (vconv_direct_ok): GroupNorm statistics of the output, per 64-row
+  // half tile h (rows 64 h .. 64 h + 63) and channel n, at gn_part[h N + n]: the mean of the
+  // half's valid rows and the sum of squared deviations from it (nullable)
+  float2* gn_part;
 };
 
 // GroupNorm statistics over NHWC activations x [images][HW][C], groups of C / groups
@@ -61,6 +65,13 @@ bool vconv_direct_ok(const VConvArgs& a);
 hipError_t launch_vact(const float* x, const float* affine, int images, int64_t hw, int C, int silu, float* out,
                        hipStream_t s);
 hipError_t launch_vgn(VGnArgs a, hipStream_t s);   // stats + affine (two passes over x)
+// stats + affine from the half-tile statistics a convolution wrote (VConvArgs::gn_part) for
+// x [images][HW][C] (C <= 1024): per (image, group) the halves' means and squared deviations
+// combined in float64 with Chan et al.'s pairwise update, through chunk results in `chunk`
+// (vgn_conv_chunk_doubles); the halves of an image are ceil(HW / 64) in a row (the direct
+// form's tiles never straddle images)
+size_t vgn_conv_chunk_doubles(int images, int HW, int groups);
+hipError_t launch_vgn_from_conv(const float2* part, double* chunk, const VGnArgs& a, hipStream_t s);
 // latent [images][ch][h][w] -> NHWC [images][h][w][ch], each value z / scale + shift (unscale
 // != 0) or copied
 hipError_t launch_vlatent_in(const float* z, float* out, int images, int ch, int h, int w, int unscale,

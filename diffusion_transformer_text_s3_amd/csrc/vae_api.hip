@@ -46,9 +46,10 @@ zdit_status check_shape(int batch, int lat_h, int lat_w) {
 bool ok_ptr(const void* p) { return p && aligned16(p); }
 
 // Workspace regions (byte offsets): the NHWC latent, three activation buffers of the largest
-// stage, GroupNorm partials, statistics and affines, and the attention's q/k/v, v^T and scores.
+// stage, GroupNorm partials, the half-tile statistics the convolutions write, statistics and
+// affines, and the attention's q/k/v, v^T and scores (gp_bytes 0: no half-tile statistics).
 struct VaePlan {
-  size_t lat, X, H, T, part, stat, aff, qkv, vt, S, total;
+  size_t lat, X, H, T, part, gp, gp_bytes, gc, stat, aff, qkv, vt, S, total;
 };
 
 int dec_width(const zdit_vae_cfg& c, int i) { return c.widths[3 - i]; }
@@ -79,6 +80,11 @@ VaePlan plan_vae(const zdit_vae_cfg& c, int B, int h, int w) {
   p.H = off; off += al256((size_t)act * 4);
   p.T = off; off += al256((size_t)act * 4);
   p.part = off; off += al256(part * 4);
+  // half tiles of 64 rows: at most act / 64 + one partial half per image, per channel
+  p.gp_bytes = al256(((size_t)act / 64 + (size_t)B * 1024) * 8);
+  p.gp = off; off += p.gp_bytes;
+  // their first-level merges: per image, chunk of 64 half tiles and group
+  p.gc = off; off += al256(((size_t)act / 4096 + (size_t)B * c.groups) * 3 * 8);
   p.stat = off; off += al256((size_t)B * c.groups * 2 * 8);
   p.aff = off; off += al256((size_t)B * 1024 * 2 * 4);
   p.qkv = off; off += al256((size_t)B * n0 * 3 * C * 4);
@@ -88,18 +94,25 @@ VaePlan plan_vae(const zdit_vae_cfg& c, int B, int h, int w) {
   return p;
 }
 
-// One launcher context: the workspace regions and the stream.
+// One launcher context: the workspace regions and the stream.  gp_valid: the half-tile
+// statistics region holds those of the last output written by a convolution with stats on.
 struct Ctx {
   const zdit_vae_cfg& c;
   char* ws;
   const VaePlan& pl;
   int B;
   hipStream_t st;
+  mutable bool gp_valid = false;
   float* f(size_t off) const { return (float*)(ws + off); }
 };
 
+// stats: the output is GroupNorm's next input; the direct-to-LDS form then writes its half-tile
+// statistics and gnorm uses them.  They are used only where H W is a multiple of 128, where every
+// batch size runs the direct form: the choice then depends on the image size alone, so a batch
+// item's statistics, and its image, are bit-identical to those of the same image decoded alone
+// (the direct and staged forms give the same bits, the two GroupNorm paths do not).
 hipError_t conv(const Ctx& x, const float* in, int H, int W, int cin, int cout, int ksize, int up, const float* aff,
-                int silu, const zdit_vae_conv& cw, const float* res, float* out, int out_nchw = 0) {
+                int silu, const zdit_vae_conv& cw, const float* res, float* out, int out_nchw = 0, bool stats = false) {
   VConvArgs a{};
   a.out_nchw = out_nchw;
   a.A = in; a.lda = cin;
@@ -108,6 +121,11 @@ hipError_t conv(const Ctx& x, const float* in, int H, int W, int cin, int cout, 
   a.res = res; a.bias = cw.b; a.affine = aff; a.silu = silu;
   a.M = x.B * H * W; a.N = cout; a.K = cin; a.H = H; a.W = W;
   a.ksize = ksize; a.upsample = up; a.alpha = 1.f;
+  if (stats) {
+    const size_t need = ((size_t)(a.M + 63) / 64 + x.B) * cout * 8;
+    x.gp_valid = (int64_t)H * W % 128 == 0 && x.pl.gp_bytes >= need && vconv_direct_ok(a);
+    if (x.gp_valid) a.gn_part = (float2*)(x.ws + x.pl.gp);
+  }
   return launch_vconv(a, x.st);
 }
 
@@ -116,6 +134,10 @@ hipError_t gnorm(const Ctx& x, const float* in, int hw, int C, const zdit_vae_no
   a.x = in; a.images = x.B; a.HW = hw; a.C = C; a.groups = x.c.groups;
   a.part = x.f(x.pl.part); a.stat = (double*)(x.ws + x.pl.stat);
   a.gamma = n.gamma; a.beta = n.beta; a.affine = x.f(x.pl.aff); a.eps = x.c.eps;
+  if (x.gp_valid) {
+    x.gp_valid = false;
+    return launch_vgn_from_conv((const float2*)(x.ws + x.pl.gp), (double*)(x.ws + x.pl.gc), a, x.st);
+  }
   return launch_vgn(a, x.st);
 }
 
@@ -129,16 +151,16 @@ hipError_t resnet(const Ctx& x, float*& X, float*& Hb, float*& T, int H, int W, 
   float* aff = x.f(x.pl.aff);
   if (hipError_t e = gnorm(x, X, hw, cin, r.gn1)) return e;
   if (hipError_t e = launch_vact(X, aff, x.B, hw, cin, 1, T, x.st)) return e;
-  if (hipError_t e = conv(x, T, H, W, cin, cout, 3, 0, nullptr, 0, r.conv1, nullptr, Hb)) return e;
+  if (hipError_t e = conv(x, T, H, W, cin, cout, 3, 0, nullptr, 0, r.conv1, nullptr, Hb, 0, true)) return e;
   if (hipError_t e = gnorm(x, Hb, hw, cout, r.gn2)) return e;
   if (hipError_t e = launch_vact(Hb, aff, x.B, hw, cout, 1, Hb, x.st)) return e;
   if (r.shortcut.w) {
     if (hipError_t e = conv(x, X, H, W, cin, cout, 1, 0, nullptr, 0, r.shortcut, nullptr, T)) return e;
-    if (hipError_t e = conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, T, T)) return e;
+    if (hipError_t e = conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, T, T, 0, true)) return e;
     std::swap(X, T);
     return hipSuccess;
   }
-  return conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, X, X);
+  return conv(x, Hb, H, W, cout, cout, 3, 0, nullptr, 0, r.conv2, X, X, 0, true);
 }
 
 hipError_t attention(const Ctx& x, float* X, float* Hb, int H, int W, int C, const zdit_vae_attn& at) {
@@ -168,7 +190,7 @@ hipError_t attention(const Ctx& x, float* X, float* Hb, int H, int W, int C, con
     o.M = N; o.N = C; o.K = N; o.H = 1; o.W = N; o.ksize = 1; o.alpha = 1.f;
     if (hipError_t e = launch_vconv(o, x.st)) return e;
   }
-  return conv(x, Hb, H, W, C, C, 1, 0, nullptr, 0, at.out, X, X);
+  return conv(x, Hb, H, W, C, C, 1, 0, nullptr, 0, at.out, X, X, 0, true);
 }
 
 zdit_status check_conv_w(const zdit_vae_conv& c, const char* what) {
@@ -245,7 +267,7 @@ zdit_status zdit_vae_decode(const zdit_vae_cfg* cfg, const zdit_vae_w* w, int32_
   const int c0 = dec_width(c, 0);
   HIP_TRY(launch_vlatent_in(latent, x.f(pl.lat), batch, c.latent_ch, H, W, !(c.flags & ZDIT_VAE_INPUT_UNSCALED),
                             c.scale, c.shift, st));
-  HIP_TRY(conv(x, x.f(pl.lat), H, W, c.latent_ch, c0, 3, 0, nullptr, 0, w->conv_in, nullptr, X));
+  HIP_TRY(conv(x, x.f(pl.lat), H, W, c.latent_ch, c0, 3, 0, nullptr, 0, w->conv_in, nullptr, X, 0, true));
   HIP_TRY(resnet(x, X, Hb, T, H, W, c0, c0, w->mid[0]));
   HIP_TRY(attention(x, X, Hb, H, W, c0, w->attn));
   HIP_TRY(resnet(x, X, Hb, T, H, W, c0, c0, w->mid[1]));
@@ -256,7 +278,7 @@ zdit_status zdit_vae_decode(const zdit_vae_cfg* cfg, const zdit_vae_w* w, int32_
     if (i < 3) {
       H *= 2;
       W *= 2;
-      HIP_TRY(conv(x, X, H, W, co, co, 3, 1, nullptr, 0, w->upconv[i], nullptr, T));
+      HIP_TRY(conv(x, X, H, W, co, co, 3, 1, nullptr, 0, w->upconv[i], nullptr, T, 0, true));
       std::swap(X, T);
     }
     cin = co;
