@@ -631,6 +631,46 @@ __global__ void vlatent_in_kernel(const float* z, float* out, int images, int ch
 }
 
 // one workgroup per row: max, then the sum of exp(s - max), then exp(s - max) / sum
+// A row of at most 1024 Q values per workgroup held in registers (Q float4 per thread, columns
+// 4 (t + 256 k) .. + 3): one read and one write of the row, the same arithmetic as
+// vsoftmax_kernel (expf of s - max, then an IEEE division by the sum; the sum's order differs).
+template <int Q>
+__global__ __launch_bounds__(256) void vsoftmax_reg_kernel(float* S, int n) {
+  __shared__ float red[8];
+  float* row = S + (int64_t)blockIdx.x * n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq = n >> 2;
+  f4 v[Q];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const int q = tid + 256 * k;
+    v[k] = q < nq ? *(const f4*)(row + 4 * q) : f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    mx = fmaxf(mx, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sm = 0.f;
+#pragma unroll
+  for (int k = 0; k < Q; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[k][e] = expf(v[k][e] - mx);  // exp(-inf) = 0 past the row's end
+      sm += v[k][e];
+    }
+  for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+  if (lane == 0) red[4 + wave] = sm;
+  __syncthreads();
+  sm = (red[4] + red[5]) + (red[6] + red[7]);
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const int q = tid + 256 * k;
+    if (q < nq) *(f4*)(row + 4 * q) = v[k] / sm;
+  }
+}
+
 __global__ __launch_bounds__(256) void vsoftmax_kernel(float* S, int n) {
   __shared__ float red[256];
   float* row = S + (int64_t)blockIdx.x * n;
@@ -756,7 +796,15 @@ hipError_t launch_vlatent_in(const float* z, float* out, int images, int ch, int
 
 hipError_t launch_vsoftmax(float* S, int64_t rows, int n, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(vsoftmax_kernel, dim3((unsigned)rows), dim3(256), 0, s, S, n);
+  const dim3 g((unsigned)rows), b(256);
+  if (n % 4 || ((uintptr_t)S & 15) || n > 16384)
+    hipLaunchKernelGGL(vsoftmax_kernel, g, b, 0, s, S, n);
+  else if (n <= 1024)
+    hipLaunchKernelGGL(vsoftmax_reg_kernel<1>, g, b, 0, s, S, n);
+  else if (n <= 4096)
+    hipLaunchKernelGGL(vsoftmax_reg_kernel<4>, g, b, 0, s, S, n);
+  else
+    hipLaunchKernelGGL(vsoftmax_reg_kernel<16>, g, b, 0, s, S, n);
   return hipGetLastError();
 }
 

@@ -174,7 +174,7 @@ def test_vae_conv_out_matches_oracle():
 
 
 # ------------------------------------------------------------------------------ attention
-@pytest.mark.parametrize("B,H,W,C", [(2, 8, 6, 64), (1, 16, 16, 512)])
+@pytest.mark.parametrize("B,H,W,C", [(2, 8, 6, 64), (1, 16, 16, 512), (1, 40, 50, 64)])
 def test_vae_attention_matches_oracle(B, H, W, C):
     note(f"vae attention B={B} {H}x{W} C={C}")
     vd = synth.VAE_TINY if C == 64 else synth.VAE_FULL
