@@ -262,17 +262,30 @@ __global__ __launch_bounds__(256) void vconv_kernel(VConvArgs a) {
 }
 
 // ------------------------------------------------------------ convolution, direct-to-LDS form
-// The same tiles, K steps, LDS layout, fragment reads and MFMA order as vconv_kernel<128, 128>
+// The same tiles, K steps, LDS layout, fragment reads and MFMA order as vconv_kernel<BM, BN>
 // (so the same sums in the same order), for inputs that need no transform: the A and B tiles
 // go from memory straight into LDS with buffer loads (buffer_load_dword ... lds), no staging
-// registers, selects or LDS stores, and two steps ahead through a ring of three 16 KB stages.
+// registers, selects or LDS stores, and two steps ahead through a ring of three stages.
 // The fp32 MFMA shares its issue cycles with the vector ALU, so the fewer vector instructions
 // per MFMA the better.
 // Each operand is read through a buffer resource over the rows one tile can touch (bounds
 // checked by the hardware): a lane's offset is past the end for output rows past M, for taps
 // outside the image and for weight rows past N, and such a load returns zeros.  A lane's A
 // offsets change only when the tap does; the channel step is the scalar offset.
-constexpr int kDStage = 2 * kVM * kVLd;  // floats: A rows, then B rows
+// Tile shapes: 128 x 128 (2 x 2 waves of 64 x 64; each wave loads two 16-row blocks of A and two
+// of B per step) and 256 x 16 for the output conv (4 x 1 waves of 64 x 16; each wave loads four A
+// blocks and its own copy of the one B block, so every wave issues the same number of loads).
+template <int BM, int BN>
+struct VDirect {
+  static constexpr int WGM = BM / 64, WGN = 4 / WGM;
+  static constexpr int RJ = BN / WGN / 16;           // 16-wide column tiles per wave
+  static constexpr int ABLK = BM / 64;               // A blocks per wave
+  static constexpr bool PRIV_B = BN < 64;            // B private to each wave
+  static constexpr int BBLK = PRIV_B ? BN / 16 : BN / 64;
+  static constexpr int LOADS = ABLK + BBLK;          // loads per wave per step
+  static constexpr int BROWS = PRIV_B ? 4 * BN : BN;  // B rows in a stage
+  static constexpr int STAGE = (BM + BROWS) * kVLd;   // floats: A rows, then B rows
+};
 constexpr int kBufFlags = 0x00020000;   // raw (offset-addressed) buffer, word 3
 constexpr int kOob = 0x7ffffff0;        // an offset past every resource's end
 // s_waitcnt immediate waiting for vmcnt <= n only (expcnt and lgkmcnt fields at their maximum)
@@ -292,12 +305,13 @@ __device__ __forceinline__ void vbarrier() {
 struct VSpan {
   int img, lo, hi;
 };
+template <int BM>
 __device__ __forceinline__ VSpan vconv_span(const VConvArgs& a, int m0) {
   const int hw = a.H * a.W;
   VSpan sp;
   sp.img = m0 / hw;
   const int p0 = m0 - sp.img * hw;                   // first output pixel in the image
-  const int p1 = min(m0 + kVM, min(a.M, (sp.img + 1) * hw)) - 1 - sp.img * hw;  // last
+  const int p1 = min(m0 + BM, min(a.M, (sp.img + 1) * hw)) - 1 - sp.img * hw;  // last
   const int rad = a.ksize >> 1;
   const int Ws = a.upsample ? a.W >> 1 : a.W;
   if (a.H == 1) {  // one row per image (GEMM mode): columns
@@ -314,48 +328,54 @@ __device__ __forceinline__ VSpan vconv_span(const VConvArgs& a, int m0) {
   return sp;
 }
 
-__global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
-  __shared__ __attribute__((aligned(16))) float st0[kDStage];
-  __shared__ __attribute__((aligned(16))) float st1[kDStage];
-  __shared__ __attribute__((aligned(16))) float st2[kDStage];
+template <int BM, int BN>
+__global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void vconv_direct_kernel(VConvArgs a) {
+  using D = VDirect<BM, BN>;
+  __shared__ __attribute__((aligned(16))) float st0[D::STAGE];
+  __shared__ __attribute__((aligned(16))) float st1[D::STAGE];
+  __shared__ __attribute__((aligned(16))) float st2[D::STAGE];
   const int tid = threadIdx.x;
   // the wave index in a scalar register: the LDS destinations of the loads are then scalar
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = blockIdx.x * kVM, n0 = blockIdx.y * kVN;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int hw = a.H * a.W;
   const int rad = a.ksize >> 1;
   const int Hs = a.upsample ? a.H >> 1 : a.H, Ws = a.upsample ? a.W >> 1 : a.W;
   const int csteps = a.K / kVK;  // K % 16 == 0 on this path
   const int nsteps = a.ksize * a.ksize * csteps;
 
-  const VSpan sp = vconv_span(a, m0);
+  const VSpan sp = vconv_span<BM>(a, m0);
   const float* Abase = a.A + ((int64_t)sp.img * Hs * Ws + sp.lo) * a.lda;
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)Abase, 0, (int)((int64_t)(sp.hi - sp.lo) * a.lda * 4), kBufFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.B + (int64_t)n0 * a.ldb), 0, (int)((int64_t)min(a.N - n0, kVN) * a.ldb * 4), kBufFlags);
+      (void*)(a.B + (int64_t)n0 * a.ldb), 0, (int)((int64_t)min(a.N - n0, BN) * a.ldb * 4), kBufFlags);
 
-  // This wave loads 16-row blocks 2 wave and 2 wave + 1 of A and of B; one instruction puts
-  // lane L at slot L of the block (row L / 4, 16-byte slot L % 4), so lane L fetches the
-  // logical chunk whose swizzled slot that is.
+  // This wave loads A blocks ABLK wave + i and B blocks BBLK wave + i (or, B private, all of B
+  // into its own copy); one instruction puts lane L at slot L of a 16-row block (row L / 4,
+  // 16-byte slot L % 4), so lane L fetches the logical chunk whose swizzled slot that is.
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  int py[2], px[2], voa[2], vob[2];
-  bool mok[2];
+  int py[D::ABLK], px[D::ABLK], voa[D::ABLK], vob[D::BBLK];
+  bool mok[D::ABLK];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (2 * wave + i) * 16 + (lane >> 2);
+  for (int i = 0; i < D::ABLK; ++i) {
+    const int r = (D::ABLK * wave + i) * 16 + (lane >> 2);
     const int m = m0 + r;
     mok[i] = m < a.M;
     const int p = m - sp.img * hw;
     py[i] = p / a.W;
     px[i] = p - py[i] * a.W;
-    const int n = n0 + r;
-    vob[i] = n < a.N ? (int)(r * a.ldb * 4) + lchunk * 16 : kOob;
   }
+#pragma unroll
+  for (int i = 0; i < D::BBLK; ++i) {
+    const int r = ((D::PRIV_B ? 0 : D::BBLK * wave) + i) * 16 + (lane >> 2);
+    vob[i] = n0 + r < a.N ? (int)(r * a.ldb * 4) + lchunk * 16 : kOob;
+  }
+  const int bdst = D::PRIV_B ? BM + wave * BN : BM + D::BBLK * wave * 16;  // first B row this wave loads
   // A offsets of the tap (ky, kx)
   auto tap_offsets = [&](int ky, int kx) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < D::ABLK; ++i) {
       const int yy = py[i] + ky - rad, xx = px[i] + kx - rad;
       const bool ok = mok[i] && yy >= 0 && yy < a.H && xx >= 0 && xx < a.W;
       const int ys = a.upsample ? yy >> 1 : yy, xs = a.upsample ? xx >> 1 : xx;
@@ -370,9 +390,9 @@ __global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
   auto issue = [&](float* stage) {
     const int soa = ics * kVK * 4, sob = (itap * a.K + ics * kVK) * 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vdma16(rsa, stage + (2 * wave + i) * 16 * kVLd, voa[i], soa);
+    for (int i = 0; i < D::ABLK; ++i) vdma16(rsa, stage + (D::ABLK * wave + i) * 16 * kVLd, voa[i], soa);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) vdma16(rsb, stage + (kVM + (2 * wave + i) * 16) * kVLd, vob[i], sob);
+    for (int i = 0; i < D::BBLK; ++i) vdma16(rsb, stage + (bdst + i * 16) * kVLd, vob[i], sob);
     if (++issued < nsteps) {
       if (++ics == csteps) {
         ics = 0;
@@ -386,34 +406,34 @@ __global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
     }
   };
 
-  const int wm0 = (wave & 1) * 64, wn0 = (wave >> 1) * 64;
+  const int wm0 = (wave % D::WGM) * 64, wn0 = (wave / D::WGM) * (BN / D::WGN);
   const int fr = lane & 15, fc = lane >> 4;
-  f4 acc[4][4];
+  f4 acc[4][D::RJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < D::RJ; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // one step: this wave's loads of the step have landed (the next step's four may still be in
+  // one step: this wave's loads of the step have landed (the next step's may still be in
   // flight), the barrier makes every wave's visible and frees the stage read in the step
   // before, which takes the loads of two steps ahead
   auto step = [&](const float* cur, float* freed) {
-    __builtin_amdgcn_s_waitcnt(vm_wait(4));
+    __builtin_amdgcn_s_waitcnt(vm_wait(D::LOADS));
     vbarrier();
     issue(freed);
     const float* sA = cur;
-    const float* sB = cur + kVM * kVLd;
-    f4 af[4], bf[4];
+    const float* sB = cur + (D::PRIV_B ? BM + wave * BN : BM) * kVLd;
+    f4 af[4], bf[D::RJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = *(const f4*)&sA[vlds(wm0 + 16 * i + fr, fc)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *(const f4*)&sB[vlds(wn0 + 16 * j + fr, fc)];
+    for (int j = 0; j < D::RJ; ++j) bf[j] = *(const f4*)&sB[vlds(wn0 + 16 * j + fr, fc)];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < D::RJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][kk], bf[j][kk], acc[i][j], 0, 0, 0);
   };
 
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(256, 3) void vconv_direct_kernel(VConvArgs a) {
   if (s + 1 < nsteps) step(st1, st0);
   // the loads past the end are still landing in dead stages: drain them before the wave ends
   __builtin_amdgcn_s_waitcnt(vm_wait(0));
-  vconv_epilogue<4, true>(a, acc, m0 + wm0, n0 + wn0, lane);
+  vconv_epilogue<D::RJ, true>(a, acc, m0 + wm0, n0 + wn0, lane);
 }
 
 // GroupNorm from the half-tile statistics of a convolution (mean_h, M2_h over n_h rows per
@@ -715,34 +735,42 @@ __global__ void vtranspose_kernel(const float* in, int64_t ld, int c0, float* ou
 
 }  // namespace
 
+namespace {
+bool direct_ok(const VConvArgs& a, int BM, int BN) {
+  if (a.affine || a.K % kVK || a.lda % 4 || a.ldb % 4) return false;
+  if (((uintptr_t)a.A | (uintptr_t)a.B) & 15) return false;
+  const int64_t hw = (int64_t)a.H * a.W;
+  if (a.M != hw && hw % BM) return false;  // a tile lies in one image
+  // the largest span of source rows a tile can read, in bytes, within a 32-bit buffer offset
+  const int64_t Ws = a.upsample ? a.W / 2 : a.W;
+  const int rad = a.ksize / 2;
+  const int64_t px = a.H == 1 ? BM + 2 * rad : (BM / a.W + 2 + 2 * rad) * Ws;
+  const int64_t limit = (int64_t)0x7fffffff - 4096;
+  if (px * a.lda * 4 > limit || (int64_t)BN * a.ldb * 4 > limit) return false;
+  if ((int64_t)a.ksize * a.ksize * a.K * 4 > limit) return false;
+  return true;
+}
+}  // namespace
+
+bool vconv_direct_ok(const VConvArgs& a) { return a.N <= 16 ? direct_ok(a, 256, 16) : direct_ok(a, kVM, kVN); }
+
 hipError_t launch_vconv(const VConvArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const bool direct = vconv_direct_ok(a);
   if (a.N <= 16) {  // the output conv (3 channels): 256 x 16 tiles
     dim3 grid((a.M + 255) / 256, 1);
-    hipLaunchKernelGGL((vconv_kernel<256, 16>), grid, dim3(256), 0, s, a);
+    if (direct)
+      hipLaunchKernelGGL((vconv_direct_kernel<256, 16>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((vconv_kernel<256, 16>), grid, dim3(256), 0, s, a);
   } else {
     dim3 grid((a.M + kVM - 1) / kVM, (a.N + kVN - 1) / kVN);
-    if (vconv_direct_ok(a))
-      hipLaunchKernelGGL(vconv_direct_kernel, grid, dim3(256), 0, s, a);
+    if (direct)
+      hipLaunchKernelGGL((vconv_direct_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((vconv_kernel<kVM, kVN>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
-}
-
-bool vconv_direct_ok(const VConvArgs& a) {
-  if (a.affine || a.N <= 16 || a.K % kVK || a.lda % 4 || a.ldb % 4) return false;
-  if (((uintptr_t)a.A | (uintptr_t)a.B) & 15) return false;
-  const int64_t hw = (int64_t)a.H * a.W;
-  if (a.M != hw && hw % kVM) return false;  // a tile lies in one image
-  // the largest span of source rows a tile can read, in bytes, within a 32-bit buffer offset
-  const int64_t Ws = a.upsample ? a.W / 2 : a.W;
-  const int rad = a.ksize / 2;
-  const int64_t px = a.H == 1 ? kVM + 2 * rad : (kVM / a.W + 2 + 2 * rad) * Ws;
-  const int64_t limit = (int64_t)0x7fffffff - 4096;
-  if (px * a.lda * 4 > limit || (int64_t)kVN * a.ldb * 4 > limit) return false;
-  if ((int64_t)a.ksize * a.ksize * a.K * 4 > limit) return false;
-  return true;
 }
 
 hipError_t launch_vact(const float* x, const float* affine, int images, int64_t hw, int C, int silu, float* out,

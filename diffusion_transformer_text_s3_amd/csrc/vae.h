@@ -57,7 +57,8 @@ size_t vgn_part_floats(int images, int HW, int C);
 
 hipError_t launch_vconv(const VConvArgs& a, hipStream_t s);
 // whether launch_vconv runs the direct-to-LDS form (no input transform, channels a multiple of
-// 16, a tile within one image, buffer offsets within 32 bits); otherwise the staged form
+// 16, a tile (128 or, for N <= 16, 256 rows) within one image, buffer offsets within 32 bits);
+// otherwise the staged form
 bool vconv_direct_ok(const VConvArgs& a);
 // out = SiLU(a x + d) (silu != 0) or a x + d over NHWC x [images][hw][C], affine [images][C][2]
 // (C a power of two, at least 4); bit-identical to the staged conv's input transform; out may

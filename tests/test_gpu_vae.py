@@ -61,6 +61,8 @@ CONV_CASES = [
     (3, 16, 8, 48, 128, 3, 0, False, False),    # 128-pixel images, three channel steps per tap
     (1, 1, 200, 64, 130, 1, 0, False, False),   # one-row image, 1x1
     (1, 1, 300, 32, 64, 3, 0, False, False),    # one-row image, 3x3 (rows above and below are padding)
+    (1, 20, 18, 32, 16, 3, 0, False, True),     # N <= 16 direct form (256 x 16 tiles): ragged M, residual
+    (2, 16, 16, 64, 3, 3, 0, False, False),     # N <= 16 direct form, two images of 256 pixels, 3 of 16 columns
     # no transform, staged form: channels not a multiple of 16; images that split a tile
     (1, 8, 8, 20, 64, 3, 0, False, False),
     (2, 8, 24, 64, 160, 3, 0, False, False),
@@ -100,7 +102,8 @@ def test_vae_conv_matches_oracle(case):
 
 
 @pytest.mark.parametrize("B,H,W,cin,cout,k,up", [(2, 16, 16, 64, 96, 3, 0), (1, 24, 20, 256, 136, 3, 0),
-                                                   (2, 16, 32, 128, 128, 3, 1), (1, 1, 300, 32, 64, 3, 0)])
+                                                   (2, 16, 32, 128, 128, 3, 1), (1, 1, 300, 32, 64, 3, 0),
+                                                   (2, 16, 16, 64, 3, 3, 0), (1, 20, 18, 32, 16, 3, 0)])
 def test_vae_conv_direct_form_bit_identical_to_staged_form(B, H, W, cin, cout, k, up):
     """Without an input transform the convolution runs in its direct-to-LDS form; with the
     identity affine (a = 1, d = 0, no SiLU: every value unchanged) it runs in the staged form.
