@@ -457,13 +457,14 @@ __global__ __launch_bounds__(256, BM == 128 ? 3 : 2) void vconv_direct_kernel(VC
 // (n_a, m_a, M2_a) and (n_b, m_b, M2_b) gives n = n_a + n_b, m = m_a + (m_b - m_a) n_b / n and
 // M2 = M2_a + M2_b + (m_b - m_a)^2 n_a n_b / n.  Every merge runs in a fixed order.
 __device__ __forceinline__ void chan_merge(double& n, double& m, double& q, double nb, double mb, double qb) {
+  if (nb == 0.0) return;  // an empty set (a thread with no chunks)
   const double t = n + nb, d = mb - m;
   m += d * nb / t;
   q += qb + d * d * n * nb / t;
   n = t;
 }
 
-constexpr int kGnChunk = 64;  // half tiles per workgroup of the first level
+constexpr int kGnChunk = 16;  // half tiles per workgroup of the first level
 
 // First level, one workgroup per (chunk of kGnChunk half tiles, image): per channel (one thread,
 // coalesced over the channels) the chunk's count, mean and M2 (the exact two-sum identity
@@ -507,34 +508,45 @@ __global__ __launch_bounds__(256) void vgn_conv_chunk_kernel(const float2* part,
   }
 }
 
-// Second level, one workgroup per (group, image): the chunks merged in order, then
-// 1/sqrt(M2 / n + eps) and the per-channel affine, as vgn_finalize_kernel.
-__global__ __launch_bounds__(64) void vgn_conv_final_kernel(const double* chunk, int nck, VGnArgs a) {
-  __shared__ double ms[2];
+// Second level, one workgroup per (group, image): thread t merges chunks t, t + 256, ... in
+// order, then the 256 results merge pairwise in a fixed tree; then 1/sqrt(M2 / n + eps) and the
+// per-channel affine, as vgn_finalize_kernel.
+__global__ __launch_bounds__(256) void vgn_conv_final_kernel(const double* chunk, int nck, VGnArgs a) {
+  __shared__ double rn[256], rm[256], rq[256];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, img = blockIdx.y;
-  if (tid == 0) {
-    const double* c = chunk + ((int64_t)img * nck * a.groups + g) * 3;
-    double n = c[0], m = c[1], q = c[2];
-    for (int k = 1; k < nck; ++k) {
-      const double* e = c + (int64_t)k * a.groups * 3;
-      chan_merge(n, m, q, e[0], e[1], e[2]);
-    }
-    const double rstd = 1.0 / sqrt(q / n + (double)a.eps);
-    double* st = a.stat + ((int64_t)img * a.groups + g) * 2;
-    st[0] = m;
-    st[1] = rstd;
-    ms[0] = m;
-    ms[1] = rstd;
+  const double* c = chunk + ((int64_t)img * nck * a.groups + g) * 3;
+  double n = 0.0, m = 0.0, q = 0.0;
+  for (int k = tid; k < nck; k += 256) {
+    const double* e = c + (int64_t)k * a.groups * 3;
+    chan_merge(n, m, q, e[0], e[1], e[2]);
   }
+  rn[tid] = n;
+  rm[tid] = m;
+  rq[tid] = q;
   __syncthreads();
-  const double mean = ms[0], rstd = ms[1];
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      double n2 = rn[tid], m2 = rm[tid], q2 = rq[tid];
+      chan_merge(n2, m2, q2, rn[tid + w], rm[tid + w], rq[tid + w]);
+      rn[tid] = n2;
+      rm[tid] = m2;
+      rq[tid] = q2;
+    }
+    __syncthreads();
+  }
+  const double mean = rm[0], rstd = 1.0 / sqrt(rq[0] / rn[0] + (double)a.eps);
+  if (tid == 0) {
+    double* st = a.stat + ((int64_t)img * a.groups + g) * 2;
+    st[0] = mean;
+    st[1] = rstd;
+  }
   const int cpg = a.C / a.groups;
-  for (int cc = tid; cc < cpg; cc += 64) {
-    const int c = g * cpg + cc;
-    const double ga = (double)a.gamma[c] * rstd;
-    a.affine[((int64_t)img * a.C + c) * 2] = (float)ga;
-    a.affine[((int64_t)img * a.C + c) * 2 + 1] = (float)((double)a.beta[c] - mean * ga);
+  for (int cc = tid; cc < cpg; cc += 256) {
+    const int ch = g * cpg + cc;
+    const double ga = (double)a.gamma[ch] * rstd;
+    a.affine[((int64_t)img * a.C + ch) * 2] = (float)ga;
+    a.affine[((int64_t)img * a.C + ch) * 2 + 1] = (float)((double)a.beta[ch] - mean * ga);
   }
 }
 
@@ -799,7 +811,7 @@ hipError_t launch_vgn_from_conv(const float2* part, double* chunk, const VGnArgs
   const int hpi = (a.HW + 63) / 64;
   const int nck = (hpi + kGnChunk - 1) / kGnChunk;
   hipLaunchKernelGGL(vgn_conv_chunk_kernel, dim3(nck, a.images), dim3(256), 0, s, part, a, chunk);
-  hipLaunchKernelGGL(vgn_conv_final_kernel, dim3(a.groups, a.images), dim3(64), 0, s, chunk, nck, a);
+  hipLaunchKernelGGL(vgn_conv_final_kernel, dim3(a.groups, a.images), dim3(256), 0, s, chunk, nck, a);
   return hipGetLastError();
 }
 

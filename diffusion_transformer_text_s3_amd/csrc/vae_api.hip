@@ -83,8 +83,8 @@ VaePlan plan_vae(const zdit_vae_cfg& c, int B, int h, int w) {
   // half tiles of 64 rows: at most act / 64 + one partial half per image, per channel
   p.gp_bytes = al256(((size_t)act / 64 + (size_t)B * 1024) * 8);
   p.gp = off; off += p.gp_bytes;
-  // their first-level merges: per image, chunk of 64 half tiles and group
-  p.gc = off; off += al256(((size_t)act / 4096 + (size_t)B * c.groups) * 3 * 8);
+  // their first-level merges: per image, chunk of 16 half tiles (1024 rows) and group
+  p.gc = off; off += al256(((size_t)act / 1024 + (size_t)B * c.groups) * 3 * 8);
   p.stat = off; off += al256((size_t)B * c.groups * 2 * 8);
   p.aff = off; off += al256((size_t)B * 1024 * 2 * 4);
   p.qkv = off; off += al256((size_t)B * n0 * 3 * C * 4);
