@@ -63,6 +63,11 @@ CONV_CASES = [
     (1, 1, 300, 32, 64, 3, 0, False, False),    # one-row image, 3x3 (rows above and below are padding)
     (1, 20, 18, 32, 16, 3, 0, False, True),     # N <= 16 direct form (256 x 16 tiles): ragged M, residual
     (2, 16, 16, 64, 3, 3, 0, False, False),     # N <= 16 direct form, two images of 256 pixels, 3 of 16 columns
+    (3, 4, 32, 32, 64, 3, 0, False, False),     # direct: images of exactly one 128-row tile
+    (2, 256, 1, 48, 80, 3, 0, False, True),     # direct: one-pixel-wide images (every side tap is padding)
+    (2, 128, 2, 64, 64, 3, 1, False, False),    # direct: upsample from one input column
+    (1, 8, 16, 1024, 64, 3, 0, False, False),   # direct: the widest input, K = 9216
+    (4, 8, 16, 128, 256, 1, 0, False, True),    # direct: 1x1 over four 128-pixel images, residual
     # no transform, staged form: channels not a multiple of 16; images that split a tile
     (1, 8, 8, 20, 64, 3, 0, False, False),
     (2, 8, 24, 64, 160, 3, 0, False, False),
