@@ -50,10 +50,17 @@ __device__ __forceinline__ void sdma_16(const __amdgpu_buffer_rsrc_t rs, const u
                                            0, 0);
 }
 
+// RES = 0: A chunks double-buffered, one barrier per chunk.  RES = 2 or 4: a K range of at most
+// RES chunks has all of them resident (RES x 32 KB of LDS), loaded together with the first
+// weight slabs; one barrier, then every slab of the range with no further wait for A, so the
+// weight stream keeps KU_B slabs in flight throughout (the double-buffered form drops to 8 at each
+// chunk boundary, where its wait for the next chunk's loads also covers the older weight loads).
+template <int RES>
 __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
-  // two separate objects, so reads of one chunk buffer are not ordered behind the in-flight
-  // direct-to-LDS writes of the other
+  // separate objects, so reads of one chunk buffer are not ordered behind the in-flight
+  // direct-to-LDS writes of another
   __shared__ uint4 A0[KCH_CHUNKS], A1[KCH_CHUNKS];
+  __shared__ uint4 A2[RES > 2 ? KCH_CHUNKS : 1], A3[RES > 2 ? KCH_CHUNKS : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ct = blockIdx.x, split = blockIdx.y, m0 = blockIdx.z * KM;
@@ -139,20 +146,62 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
     __builtin_amdgcn_sched_barrier(0);                                                                \
   }
 
-  dma_a(0, A0);
-#pragma unroll
-  for (int u = 0; u < KU_B; ++u) bq[u] = ldb(u);
-  __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(KU_B));
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  int ch = 0;
-  for (; ch + 2 <= nch; ch += 2) {
-    ZDIT_SK_CHUNK(ch, A0, A1)
-    ZDIT_SK_CHUNK(ch + 1, A1, A0)
+  // The slabs of one resident chunk CH in buffer CUR (RES > 0): no loads of A, no barrier.
+#define ZDIT_SK_RESIDENT(CH, CUR)                                                                      \
+  {                                                                                                   \
+    _Pragma("unroll") for (int s = 0; s < KCH_SL; ++s) {                                              \
+      const int tt = (CH) * KCH_SL + s;                                                               \
+      const int q = ((CH) & 1) * KCH_SL + s;                                                          \
+      if (tt < nk) {                                                                                  \
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, bq[q]);                                          \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                               \
+          const int r = 16 * i + fr;                                                                  \
+          const bf16x8 af = __builtin_bit_cast(bf16x8, CUR[aslot(r, s * 4 + fh)]);                    \
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i], 0, 0, 0);                  \
+        }                                                                                             \
+      }                                                                                               \
+      bq[q] = ldb(tt + KU_B);                                                                         \
+    }                                                                                                 \
   }
-  if (ch < nch) ZDIT_SK_CHUNK(ch, A0, A1)
+
+  if constexpr (RES == 0) {
+    dma_a(0, A0);
+#pragma unroll
+    for (int u = 0; u < KU_B; ++u) bq[u] = ldb(u);
+    __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(KU_B));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    int ch = 0;
+    for (; ch + 2 <= nch; ch += 2) {
+      ZDIT_SK_CHUNK(ch, A0, A1)
+      ZDIT_SK_CHUNK(ch + 1, A1, A0)
+    }
+    if (ch < nch) ZDIT_SK_CHUNK(ch, A0, A1)
+  } else {
+    // every chunk of the range (nch <= RES), then the first weight slabs; waiting until at most
+    // KU_B loads are in flight leaves exactly those weight loads, so all of A has landed
+    dma_a(0, A0);
+    if (nch > 1) dma_a(1, A1);
+    if constexpr (RES > 2) {
+      if (nch > 2) dma_a(2, A2);
+      if (nch > 3) dma_a(3, A3);
+    }
+#pragma unroll
+    for (int u = 0; u < KU_B; ++u) bq[u] = ldb(u);
+    __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(KU_B));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    ZDIT_SK_RESIDENT(0, A0)
+    if (nch > 1) ZDIT_SK_RESIDENT(1, A1)
+    if constexpr (RES > 2) {
+      if (nch > 2) ZDIT_SK_RESIDENT(2, A2)
+      if (nch > 3) ZDIT_SK_RESIDENT(3, A3)
+    }
+  }
 #undef ZDIT_SK_CHUNK
+#undef ZDIT_SK_RESIDENT
   // the loads past the range are still landing
   __builtin_amdgcn_s_waitcnt(s_waitcnt_vm(0));
 
@@ -426,7 +475,13 @@ hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream
     a.u_ld = g.out.ld;
   }
   dim3 grid(direct ? (g.N + KWG / 2 - 1) / (KWG / 2) : vtiles, a.splits, (g.M + KM - 1) / KM);
-  hipLaunchKernelGGL(gemm_splitk_kernel, grid, dim3(512), 0, s, a);
+  const int nch = a.ks / KCH;  // chunks of a full range
+  if (nch <= 2)
+    hipLaunchKernelGGL(gemm_splitk_kernel<2>, grid, dim3(512), 0, s, a);
+  else if (nch <= 4)
+    hipLaunchKernelGGL(gemm_splitk_kernel<4>, grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(gemm_splitk_kernel<0>, grid, dim3(512), 0, s, a);
   if (direct) return hipGetLastError();
   if (fuse && fuse->kind == SplitKFuse::QK_NORM_ROPE) {
     if (epi != EPI_STORE || !c_rows) return hipErrorInvalidValue;
