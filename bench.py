@@ -841,8 +841,8 @@ def vae_cpu_baseline(vd, seed):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["1024", "1536", "encoder", "vae"], default="1024",
                     help="the DiT pass at 1024^2 (default) or 1536x1024, the text encoder forward, or the VAE "
                          "decode of a 1024x1024 image")
