@@ -12,11 +12,13 @@ pair, one full-width block at 256 px (at the MFMA / HBM ridge: both fractions), 
 forward at 1024^2 (cond alone and the cond/uncond pair), the roofline of the dominant kernel
 and the oracle's CPU baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder|vae]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1024|1536|encoder|vae|pipeline]
 
 --workload encoder times the text encoder instead (its own JSON line): the Qwen3-4B-shaped
 decoder on two right-padded rows of 64 ids (45 and 10 valid) to hidden_states[-2].
 --workload vae times the fp32 VAE decode of one 1024x1024 image (latent 16 x 128 x 128).
+--workload pipeline times the whole chain for one 1024x1024 image: the text encoder on the prompt
+and the negative, the 8-step pass on its hidden states, the VAE decode, with the split per stage.
 --kernel-only NAME launches one kernel at its main-block shape a few times on operands that
 rotate through more memory than the 256 MB last-level cache holds (as in the pass), for
 rocprofv3 counter runs.
@@ -817,6 +819,84 @@ def vae_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+PIPE_METRIC = "images/s end to end at 1024x1024 (token ids -> text encoder -> 8-step negated-CFG sampler -> VAE decode)"
+
+
+def pipeline_bench(args):
+    """The whole chain for one 1024x1024 image: the text encoder on the prompt and the negative
+    (2 rows of 64 ids, 45 and 10 valid), the 8-step negated-CFG pass on its hidden states, the VAE
+    decode of the final latent; seeded random weights of every architecture, all resident.  HIP
+    events between the stages of every timed image give the split."""
+    import numpy as np
+    import torch
+    import synth
+    from diffusion_transformer_text_s3_amd import binding as Z
+    wl, ed, vd = synth.CFG5, synth.ENC_FULL, synth.VAE_FULL
+    dims = wl.dims
+    B, L, lens = 2, 64, list(wl.cap_len)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    cfg, cfg_e, cfg_v = Z.make_cfg(dims), Z.make_enc_cfg(ed), Z.make_vae_cfg(vd)
+    model = random_model_on_device(dims, args.seed)
+    enc = random_encoder_on_device(ed, ed.n_layers - 1, args.seed)
+    vae = Z.upload_vae(synth.vae_weights(vd, args.seed), vd)
+    ids = synth.token_ids(B, L, lens, ed.vocab, args.seed)
+    cap = torch.empty((B, L, ed.hidden), device="cuda")
+    ws_e = Z.workspace(Z.zdit_encoder_workspace(cfg_e, B, L))
+    x0 = torch.from_numpy(synth.latents((dims.latent_ch, wl.lat_h, wl.lat_w), wl.seed)).cuda()
+    x = x0.clone()
+    dec = torch.empty_like(x0)
+    ws_s = Z.workspace(Z.zdit_sample_workspace(cfg, wl.lat_h, wl.lat_w, L, wl.guidance))
+    img = torch.empty((1, vd.out_ch, 8 * wl.lat_h, 8 * wl.lat_w), device="cuda")
+    ws_v = Z.workspace(Z.zdit_vae_workspace(cfg_v, 1, wl.lat_h, wl.lat_w))
+
+    def image(ev=None):
+        if ev:
+            ev[0].record(stream)
+        Z.zdit_encoder_fwd(cfg_e, enc, B, L, ids, lens, cap, ws_e, stream)
+        if ev:
+            ev[1].record(stream)
+        x.copy_(x0)
+        Z.zdit_sample(cfg, model, wl.lat_h, wl.lat_w, x, cap, L, lens, wl.guidance, wl.num_steps, wl.shift, dec,
+                      ws_s, stream)
+        if ev:
+            ev[2].record(stream)
+        Z.zdit_vae_decode(cfg_v, vae, 1, wl.lat_h, wl.lat_w, x, img, ws_v, stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        image()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        image(evs[i])
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    per = {k: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, k in enumerate(("encoder", "sampler", "vae"))}
+    per["image"] = [e[0].elapsed_time(e[3]) for e in evs]
+    finite = bool(np.isfinite(img.cpu().numpy()).all())
+    n_cap = lambda n: -(-n // dims.seq_multiple) * dims.seq_multiple
+    fl = (pass_flops(dims, (wl.lat_h // 2) * (wl.lat_w // 2), lens, wl.num_steps, n_cap, reuse=True)
+          + vae_flops(vd, 1, wl.lat_h, wl.lat_w))
+    rec = {
+        "metric": PIPE_METRIC, "value": round(1.0 / dt, 4), "unit": "images/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 (encoder, DiT) + f32 (VAE)",
+        "data": "synthetic (seeded token ids and initial latent, random-init weights of every architecture)",
+        "config": {"workload": "one 1024x1024 image: encoder on 2 rows of 64 ids (45 and 10 valid), 8-step "
+                               "negated-CFG pass (guidance %.1f), VAE decode" % wl.guidance,
+                   "encoder_blocks": ed.n_layers - 1, "dit_blocks": [dims.n_noise_ref, dims.n_ctx_ref, dims.n_main],
+                   "vae_widths": list(vd.widths)},
+        "stages_ms": {k: stats(v) for k, v in per.items()},
+        "executed_tflop_per_image": round(fl / 1e12, 2),
+        "tflops": round(fl / dt / 1e12, 2),
+        "output_finite": finite,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def vae_cpu_baseline(vd, seed):
     """The decoder oracle (as it stands, fp32 NumPy) on a bounded sample: one decode of a
     32 x 32 latent (a 256 x 256 image), timed on this host's cores, in TFLOP/s."""
@@ -843,9 +923,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["1024", "1536", "encoder", "vae"], default="1024",
-                    help="the DiT pass at 1024^2 (default) or 1536x1024, the text encoder forward, or the VAE "
-                         "decode of a 1024x1024 image")
+    ap.add_argument("--workload", choices=["1024", "1536", "encoder", "vae", "pipeline"], default="1024",
+                    help="the DiT pass at 1024^2 (default) or 1536x1024, the text encoder forward, the VAE "
+                         "decode of a 1024x1024 image, or the whole chain for one 1024x1024 image")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--kernel-only", default=None,
@@ -873,6 +953,9 @@ def main():
         return
     if args.workload == "vae":
         vae_bench(args)
+        return
+    if args.workload == "pipeline":
+        pipeline_bench(args)
         return
 
     wl = synth.CFG5 if args.workload == "1024" else synth.CFG5_WIDE
