@@ -2,8 +2,12 @@
 // port", table "Architecture -> export mapping", row VAE: the decoder runs in fp32 and
 // upsamples by nearest neighbour).  Activations are NHWC fp32 so that a pixel's channels are
 // contiguous: the 3x3 convolutions run as implicit GEMMs on the fp32 MFMA (v_mfma_f32_16x16x4
-// _f32), reading each (pixel, tap) as a 64-byte channel slice, with the GroupNorm affine,
-// SiLU and the 2x nearest upsample applied while the input tile is staged in LDS.
+// _f32), reading each (pixel, tap) as a 64-byte channel slice and the 2x nearest upsample as
+// input addresses at half the coordinates.  Two forms: the direct one loads its tiles straight
+// into LDS and takes inputs that need no transform (the decoder writes SiLU(GroupNorm(x)) once
+// per convolution input, vact_kernel, and takes the GroupNorm statistics from the producing
+// convolution's epilogue); the staged one applies a GroupNorm affine and SiLU while it stages
+// the input tile through registers.  Both sum in the same order.
 #include <math.h>
 
 #include <algorithm>
