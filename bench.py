@@ -589,9 +589,12 @@ def encoder_bench(args):
     nb = ed.n_layers - 1
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    packed = args.enc_weights == "packed"
     m = random_encoder_on_device(ed, nb, args.seed)
+    if packed:
+        m = Z.pack_encoder(m)
     ids = synth.token_ids(B, L, lens, ed.vocab, args.seed)
-    cfg = Z.make_enc_cfg(ed)
+    cfg = Z.make_enc_cfg(ed, Z.ZDIT_ENC_PACKED_WEIGHTS if packed else 0)
     out = torch.empty((B, L, ed.hidden), device="cuda")
     ws = Z.workspace(Z.zdit_encoder_workspace(cfg, B, L))
     step = lambda: Z.zdit_encoder_fwd(cfg, m, B, L, ids, lens, out, ws, stream)
@@ -620,8 +623,14 @@ def encoder_bench(args):
     Wd = (torch.randn((D, I), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     X = torch.zeros((M, D), device="cuda")
     gws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, M, D, I))
-    g_ms = time_op(lambda: Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, M, D, I, A, Wd, None, None, X, gws, stream),
-                   20, stream)
+    if packed:
+        Wp = torch.empty_like(Wd)
+        Z.zdit_op_pack_weights(D, I, Wd, Wp, stream)
+        g_ms = time_op(lambda: Z.zdit_op_gemm_splitk_packed(Z.ZDIT_EPI_RESID, M, D, I, A, Wp, None, None, X, gws,
+                                                            stream), 20, stream)
+    else:
+        g_ms = time_op(lambda: Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, M, D, I, A, Wd, None, None, X, gws, stream),
+                       20, stream)
     g_bytes = 2 * D * I + 2 * M * I + 2 * 4 * M * D
     achieved = g_bytes / (g_ms * 1e-3) / 1e9
     blk_bytes = encoder_block_bytes(ed, M)
@@ -633,13 +642,14 @@ def encoder_bench(args):
         "data": "synthetic (seeded uniform token ids, random-init bf16 weights)",
         "config": {"workload": "text encoder, B=2 right-padded rows of 64 ids (45 and 10 valid), hidden 2560, "
                                "intermediate 9728, 32 / 8 heads, 35 blocks to hidden_states[-2]",
-                   "tokens": sum(lens), "weight_gb": round(nb * encoder_block_bytes(ed, 0) / 1e9, 3)},
+                   "tokens": sum(lens), "weight_gb": round(nb * encoder_block_bytes(ed, 0) / 1e9, 3),
+                   "weights": "packed (zdit_op_pack_weights)" if packed else "row-major"},
         "hbm_gbs_whole_forward": round(nb * blk_bytes / dt / 1e9, 1),
-        "roofline": {"kernel": f"gemm_splitk_kernel + splitk_reduce_kernel<EPI_RESID> (down projection), "
-                               f"M={M} N={D} K={I}",
+        "roofline": {"kernel": f"gemm_splitk_kernel + splitk_reduce_kernel<EPI_RESID> (down projection, "
+                               f"{'packed' if packed else 'row-major'} weights), M={M} N={D} K={I}",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "avg_launch_ms": round(g_ms, 4),
-                     "traffic": traffic_from_profiles("gemm_enc_down"),
+                     "traffic": traffic_from_profiles("gemm_enc_down") if packed else None,
                      "measured_peak": dev["copy_gbs_measured"],
                      "frac_of_measured": round(achieved / dev["copy_gbs_measured"], 4)},
         "device": dev,
@@ -678,7 +688,8 @@ def kernel_only(which):
     """Launches of one kernel at its main-block shape on rotating operand sets (KernelRunner):
     4 warm-up launches, then 12 more, for rocprofv3 counter runs; `copy` is a plain device
     copy of an [8320, 10240] bf16 tensor (170,393,600 bytes read and written), the counter
-    calibration; `enc_down` the encoder's split-K down projection (M=55, N=2560, K=9728)."""
+    calibration; `enc_down` the encoder's split-K down projection (M=55, N=2560, K=9728) on
+    weights in the packed layout, as the encoder bench runs it."""
     import torch
     import synth
     from diffusion_transformer_text_s3_amd import binding as Z
@@ -692,8 +703,10 @@ def kernel_only(which):
         Wd = (torch.randn((D, I), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
         X = torch.zeros((Me, D), device="cuda")
         ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(Z.ZDIT_EPI_RESID, Me, D, I))
+        Wp = torch.empty_like(Wd)
+        Z.zdit_op_pack_weights(D, I, Wd, Wp)
         for _ in range(3):
-            Z.zdit_op_gemm_splitk(Z.ZDIT_EPI_RESID, Me, D, I, A, Wd, None, None, X, ws)
+            Z.zdit_op_gemm_splitk_packed(Z.ZDIT_EPI_RESID, Me, D, I, A, Wp, None, None, X, ws)
     elif which in ("vae_conv", "vae_upconv", "vae_conv1024"):
         conv = (vae_conv_runner(False, stream, 1024, 128, True) if which == "vae_conv1024"
                 else vae_conv_runner(which == "vae_upconv", stream))
@@ -836,9 +849,13 @@ def pipeline_bench(args):
     B, L, lens = 2, 64, list(wl.cap_len)
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
-    cfg, cfg_e, cfg_v = Z.make_cfg(dims), Z.make_enc_cfg(ed), Z.make_vae_cfg(vd)
+    packed = args.enc_weights == "packed"
+    cfg, cfg_v = Z.make_cfg(dims), Z.make_vae_cfg(vd)
+    cfg_e = Z.make_enc_cfg(ed, Z.ZDIT_ENC_PACKED_WEIGHTS if packed else 0)
     model = random_model_on_device(dims, args.seed)
     enc = random_encoder_on_device(ed, ed.n_layers - 1, args.seed)
+    if packed:
+        enc = Z.pack_encoder(enc)
     vae = Z.upload_vae(synth.vae_weights(vd, args.seed), vd)
     ids = synth.token_ids(B, L, lens, ed.vocab, args.seed)
     cap = torch.empty((B, L, ed.hidden), device="cuda")
@@ -888,7 +905,8 @@ def pipeline_bench(args):
         "config": {"workload": "one 1024x1024 image: encoder on 2 rows of 64 ids (45 and 10 valid), 8-step "
                                "negated-CFG pass (guidance %.1f), VAE decode" % wl.guidance,
                    "encoder_blocks": ed.n_layers - 1, "dit_blocks": [dims.n_noise_ref, dims.n_ctx_ref, dims.n_main],
-                   "vae_widths": list(vd.widths)},
+                   "vae_widths": list(vd.widths),
+                   "encoder_weights": "packed (zdit_op_pack_weights)" if packed else "row-major"},
         "stages_ms": {k: stats(v) for k, v in per.items()},
         "executed_tflop_per_image": round(fl / 1e12, 2),
         "tflops": round(fl / dt / 1e12, 2),
@@ -928,6 +946,8 @@ def main():
                          "decode of a 1024x1024 image, or the whole chain for one 1024x1024 image")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--enc-weights", choices=["packed", "rowmajor"], default="packed",
+                    help="layout of the text encoder's projection weights (encoder and pipeline workloads)")
     ap.add_argument("--kernel-only", default=None,
                     choices=["qkv", "attn", "out", "swiglu", "w2", "rmsnorm", "adaln", "euler", "copy", "enc_down",
                              "vae_conv", "vae_upconv", "vae_conv1024"],

@@ -30,7 +30,8 @@ EXPORTS = [
     "zdit_op_patchify", "zdit_op_unpatchify", "zdit_op_cap_pad", "zdit_op_temb", "zdit_op_adaln",
     "zdit_encoder_workspace", "zdit_encoder_fwd", "zdit_op_embed_workspace", "zdit_op_embed",
     "zdit_op_qknorm_rope", "zdit_op_attn_gqa_workspace", "zdit_op_attn_gqa",
-    "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk", "zdit_op_mfma_peak",
+    "zdit_op_gemm_splitk_workspace", "zdit_op_gemm_splitk", "zdit_op_gemm_splitk_packed", "zdit_op_pack_weights",
+    "zdit_op_mfma_peak",
     "zdit_device_info",
     "zdit_vae_workspace", "zdit_vae_decode", "zdit_op_vae_groupnorm_workspace", "zdit_op_vae_groupnorm",
     "zdit_op_vae_conv", "zdit_op_vae_conv_out", "zdit_op_vae_attention_workspace", "zdit_op_vae_attention",
@@ -70,7 +71,7 @@ class zdit_model_w(C.Structure):
 class zdit_enc_cfg(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("inter", C.c_int32),
                 ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("vocab", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float)]
+                ("vocab", C.c_int32), ("rope_theta", C.c_float), ("norm_eps", C.c_float), ("flags", C.c_int32)]
 
 
 class zdit_enc_layer_w(C.Structure):
@@ -172,6 +173,8 @@ def lib():
             "zdit_op_attn_gqa": (i32, [i32, i32, i32, i32, i32, i32, pi32, vp, vp, vp, sz, vp]),
             "zdit_op_gemm_splitk_workspace": (sz, [i32, i32, i32, i32]),
             "zdit_op_gemm_splitk": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_op_gemm_splitk_packed": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "zdit_op_pack_weights": (i32, [i32, i32, vp, vp, vp]),
             "zdit_op_mfma_peak": (i32, [i32, i32, vp, vp]),
             "zdit_device_info": (i32, [i32, pi32, pi32, pi32]),
             "zdit_vae_workspace": (sz, [pv, i32, i32, i32]),
@@ -311,13 +314,17 @@ def upload_model(W: dict, precision=ZDIT_BF16, device="cuda") -> DeviceModel:
     return DeviceModel(t, nr, cr, mb)
 
 
-def make_enc_cfg(ed) -> zdit_enc_cfg:
+ZDIT_ENC_PACKED_WEIGHTS = 1
+
+
+def make_enc_cfg(ed, flags=0) -> zdit_enc_cfg:
     """zdit_enc_cfg from any object with the encoder shape attributes (n_layers, hidden,
     inter, n_heads, n_kv_heads, head_dim, vocab, rope_theta, norm_eps)."""
     c = zdit_enc_cfg()
     c.n_layers, c.hidden, c.inter = ed.n_layers, ed.hidden, ed.inter
     c.n_heads, c.n_kv_heads, c.head_dim, c.vocab = ed.n_heads, ed.n_kv_heads, ed.head_dim, ed.vocab
     c.rope_theta, c.norm_eps = ed.rope_theta, ed.norm_eps
+    c.flags = flags
     return c
 
 
@@ -337,6 +344,23 @@ class DeviceEncoder:
         self.w = zdit_enc_w()
         self.w.embed = embed.data_ptr()
         self.w.layers = C.cast(self.lw, C.POINTER(zdit_enc_layer_w))
+
+
+def pack_encoder(enc: DeviceEncoder, stream=None) -> DeviceEncoder:
+    """A copy of a device encoder whose projection matrices are in the layout of
+    zdit_op_pack_weights (for a zdit_enc_cfg with ZDIT_ENC_PACKED_WEIGHTS); gains and the
+    embedding table are shared."""
+    import torch
+    layers = []
+    for t in enc.layers:
+        p = dict(t)
+        for k in DeviceEncoder.MATS:
+            src = t[k]
+            dst = torch.empty_like(src)
+            zdit_op_pack_weights(src.shape[0], src.shape[1], src, dst, stream)
+            p[k] = dst
+        layers.append(p)
+    return DeviceEncoder(enc.embed, layers)
 
 
 def upload_encoder(W: dict, device="cuda") -> DeviceEncoder:
@@ -528,6 +552,15 @@ def zdit_op_gemm_splitk_workspace(epilogue, M, N, K) -> int:
 def zdit_op_gemm_splitk(epilogue, M, N, K, A, B, B2, vec, Cout, ws, stream=None):
     return check(lib().zdit_op_gemm_splitk(epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
                                            ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_gemm_splitk_packed(epilogue, M, N, K, A, B, B2, vec, Cout, ws, stream=None):
+    return check(lib().zdit_op_gemm_splitk_packed(epilogue, M, N, K, ptr(A), ptr(B), ptr(B2), ptr(vec), ptr(Cout),
+                                                  ptr(ws), ws.numel(), stream_handle(stream)))
+
+
+def zdit_op_pack_weights(N, K, src, dst, stream=None):
+    return check(lib().zdit_op_pack_weights(N, K, ptr(src), ptr(dst), stream_handle(stream)))
 
 
 def zdit_op_mfma_peak(workgroups, iters, out, stream=None):

@@ -97,6 +97,9 @@ struct SplitKArgs {
   int swiglu_direct;
   void* u_out;
   int64_t u_ld;
+  // B and B2 in the packed band layout of launch_pack_bfrag (ldb == K, N % 16 == 0): slab t of
+  // the 16-row band of a wavefront is 1 KB in a row, chunk lane at t * 1024 + 16 lane
+  int packed;
 };
 SplitKArgs splitk_plan(int epi, int M, int N, int K);
 size_t splitk_workspace(int epi, int M, int N, int K);
@@ -123,7 +126,12 @@ struct SplitKFuse {
   int s_pad = 0;
 };
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows = nullptr,
-                              int a_phys_rows = 0, const int* c_rows = nullptr, const SplitKFuse* fuse = nullptr);
+                              int a_phys_rows = 0, const int* c_rows = nullptr, const SplitKFuse* fuse = nullptr,
+                              bool b_packed = false);
+// bf16 [N][K] row-major -> bands of 16 rows, each a run of 32-column slabs of 64 16-byte chunks,
+// chunk l of slab t of band b = columns 32 t + 8 (l / 16) .. + 7 of row 16 b + l % 16 (the B
+// fragment of v_mfma_f32_16x16x32_bf16); N % 16 == 0, K % 32 == 0
+hipError_t launch_pack_bfrag(const void* src, void* dst, int N, int K, hipStream_t s);
 // The split-K reduction alone: sums a.splits partial planes [splits][M][Nv] of a.part in order
 // and applies the epilogue (EPI_STORE, EPI_RESID, EPI_SWIGLU) through g.out (a.c_rows NULL).
 hipError_t launch_splitk_reduce(int epi, const SplitKArgs& a, const GemmArgs& g, hipStream_t s);

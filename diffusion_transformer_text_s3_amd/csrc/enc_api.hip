@@ -26,6 +26,7 @@ zdit_status check_enc_cfg(const zdit_enc_cfg* c) {
   if (c->vocab < 1) return fail(ZDIT_EINVAL, "vocab %d", c->vocab);
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return fail(ZDIT_EINVAL, "rope_theta must be finite and > 0");
   if (!(c->norm_eps >= 0.f) || !isfinite(c->norm_eps)) return fail(ZDIT_EINVAL, "norm_eps must be finite and >= 0");
+  if (c->flags & ~ZDIT_ENC_PACKED_WEIGHTS) return fail(ZDIT_EINVAL, "unknown flags 0x%x", c->flags);
   return ZDIT_OK;
 }
 
@@ -41,6 +42,7 @@ constexpr int kSplitKMaxRows = 256;
 struct EncPlan {
   size_t ids, rows, cos, sin, h, qkv, vt, o, u, part, total;
   bool splitk;
+  bool packed;  // projection weights in the packed band layout (split-K path only)
 };
 
 size_t enc_part_bytes(const zdit_enc_cfg& c, int M) {
@@ -56,6 +58,7 @@ EncPlan plan_enc(const zdit_enc_cfg& c, int B, int L) {
   const size_t M = (size_t)B * L;
   EncPlan p;
   p.splitk = M <= (size_t)kSplitKMaxRows;
+  p.packed = (c.flags & ZDIT_ENC_PACKED_WEIGHTS) != 0;
   size_t off = 0;
   p.ids = off; off += al256(M * 4);
   p.rows = off; off += al256(M * 4);
@@ -91,7 +94,7 @@ hipError_t enc_gemm(int epi, GemmArgs g, bool a_gather, bool c_scatter, int B, i
   g.M = Mc;
   if (!c_scatter) g.out = compact_rows(Mc, g.out.ld);
   return launch_gemm_splitk(epi, g, (float*)(ws + pl.part), st, a_gather ? rows : nullptr, B * L,
-                            c_scatter ? rows : nullptr, fuse);
+                            c_scatter ? rows : nullptr, fuse, pl.packed);
 }
 
 zdit_status check_ids(int batch, int max_len, int vocab, const int32_t* ids, const int32_t* len) {
@@ -256,6 +259,9 @@ zdit_status zdit_encoder_fwd(const zdit_enc_cfg* cfg, const zdit_enc_w* w, int32
   if (zdit_status s = check_ids(batch, max_len, c.vocab, ids, len)) return s;
   if (!hidden_out || !aligned16(hidden_out)) return fail(ZDIT_EINVAL, "hidden_out NULL or not 16-byte aligned");
   const EncPlan pl = plan_enc(c, batch, max_len);
+  if (pl.packed && !pl.splitk)
+    return fail(ZDIT_EUNSUPPORTED, "packed weights need batch * max_len <= %d (got %d x %d)", kSplitKMaxRows, batch,
+                max_len);
   if (!ws || ws_bytes < pl.total + 256) return fail(ZDIT_EWORKSPACE, "workspace %zu < %zu", ws_bytes, pl.total + 256);
   char* base = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   const hipStream_t st = (hipStream_t)hip_stream;
@@ -289,15 +295,19 @@ size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int
   return splitk_workspace(epilogue, M, N, K) + 256;
 }
 
-zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
-                                const void* B2, const float* vec, void* C, void* ws, size_t ws_bytes,
-                                void* hip_stream) {
+}  // extern "C"
+
+namespace {
+zdit_status gemm_splitk_op(bool packed, int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
+                           const void* B, const void* B2, const float* vec, void* C, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
   if (epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU)
     return fail(ZDIT_EINVAL, "epilogue %d", epilogue);
   if (M < 1 || N < 1 || K < 1) return fail(ZDIT_EINVAL, "M %d N %d K %d", M, N, K);
   if (M > kSplitKMaxRows || N % 8 || K % 64 || (int64_t)N * K * 2 > INT32_MAX)
     return fail(ZDIT_EUNSUPPORTED, "M %d (<= %d), N %d (multiple of 8), K %d (multiple of 64)", M, kSplitKMaxRows,
                 N, K);
+  if (packed && N % 16) return fail(ZDIT_EUNSUPPORTED, "packed weights: N %d must be a multiple of 16", N);
   if (!A || !B || !C || (epilogue == ZDIT_EPI_SWIGLU && !B2)) return fail(ZDIT_EINVAL, "NULL operand");
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (B2 && !aligned16(B2)) || (vec && !aligned16(vec)))
     return fail(ZDIT_EINVAL, "operand not 16-byte aligned");
@@ -307,7 +317,32 @@ zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t 
   g.vec = epilogue == ZDIT_EPI_RESID ? vec : nullptr;
   g.out = compact_rows(M, N);
   float* part = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  HIP_TRY(launch_gemm_splitk(epilogue, g, part, (hipStream_t)hip_stream));
+  HIP_TRY(launch_gemm_splitk(epilogue, g, part, (hipStream_t)hip_stream, nullptr, 0, nullptr, nullptr, packed));
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, const void* B,
+                                const void* B2, const float* vec, void* C, void* ws, size_t ws_bytes,
+                                void* hip_stream) {
+  return gemm_splitk_op(false, epilogue, M, N, K, A, B, B2, vec, C, ws, ws_bytes, hip_stream);
+}
+
+zdit_status zdit_op_gemm_splitk_packed(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
+                                       const void* B, const void* B2, const float* vec, void* C, void* ws,
+                                       size_t ws_bytes, void* hip_stream) {
+  return gemm_splitk_op(true, epilogue, M, N, K, A, B, B2, vec, C, ws, ws_bytes, hip_stream);
+}
+
+zdit_status zdit_op_pack_weights(int32_t N, int32_t K, const void* src, void* dst, void* hip_stream) {
+  if (N < 16 || K < 32 || N % 16 || K % 32) return fail(ZDIT_EUNSUPPORTED, "N %d (multiple of 16), K %d (multiple of 32)", N, K);
+  if ((int64_t)N * K * 2 > INT32_MAX) return fail(ZDIT_EUNSUPPORTED, "matrix larger than 2 GiB");
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return fail(ZDIT_EINVAL, "NULL or misaligned pointer");
+  const uintptr_t a0 = (uintptr_t)src, b0 = (uintptr_t)dst, n = (uintptr_t)N * K * 2;
+  if (a0 < b0 + n && b0 < a0 + n) return fail(ZDIT_EINVAL, "src and dst overlap");
+  HIP_TRY(launch_pack_bfrag(src, dst, N, K, (hipStream_t)hip_stream));
   return ok();
 }
 

@@ -78,10 +78,13 @@ __global__ __launch_bounds__(512) void gemm_splitk_kernel(SplitKArgs a) {
   const bf16* bb = (const bf16*)(second ? a.B2 : a.B) + (int64_t)min(n0, a.N) * a.ldb;
   const __amdgpu_buffer_rsrc_t brs =
       __builtin_amdgcn_make_buffer_rsrc((void*)bb, 0, max(0, a.N - n0) * a.ldb * 2, kSBufFlags);
-  const unsigned bvo = (unsigned)(fr * a.ldb * 2 + fh * 16 + k0 * 2);
+  // row-major: lane l reads 16 bytes of row fr at column k0 + 32 t + 8 fh (16 rows of 64 bytes per
+  // slab); packed: slab k0 / 32 + t of the band is 1 KB in a row, the lane's chunk at 16 l
+  const unsigned bvo = a.packed ? (unsigned)(k0 * 32 + lane * 16) : (unsigned)(fr * a.ldb * 2 + fh * 16 + k0 * 2);
+  const unsigned bstep = a.packed ? 1024u : (unsigned)(KSL * 2);
   // slabs past the range reload the last one (branch-free); no MFMA uses them
   auto ldb = [&](int t) {
-    return __builtin_amdgcn_raw_buffer_load_b128(brs, (int)(bvo + (unsigned)min(t, nk - 1) * (KSL * 2)), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(brs, (int)(bvo + (unsigned)min(t, nk - 1) * bstep), 0, 0);
   };
 
   // A chunk loads: wave load j of this wave fills slots 64 (KCH_DMA wave + j) + lane, i.e. row
@@ -443,6 +446,32 @@ SplitKArgs splitk_plan(int epi, int M, int N, int K) {
   return a;
 }
 
+namespace {
+// one thread per 16-byte chunk of the packed matrix, in packed order (coalesced writes)
+__global__ __launch_bounds__(256) void pack_bfrag_kernel(const uint4* src, uint4* dst, int N, int K) {
+  const int64_t n = (int64_t)N * K / 8;
+  const int slabs = K / KSL;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int l = (int)(i & 63);
+    const int64_t bt = i >> 6;
+    const int t = (int)(bt % slabs);
+    const int64_t band = bt / slabs;
+    const int64_t row = band * 16 + (l & 15);
+    const int col = t * KSL + 8 * (l >> 4);
+    dst[i] = src[(row * K + col) >> 3];
+  }
+}
+}  // namespace
+
+hipError_t launch_pack_bfrag(const void* src, void* dst, int N, int K, hipStream_t s) {
+  if (N % 16 || K % KSL) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)N * K / 8;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(pack_bfrag_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)src, (uint4*)dst, N, K);
+  return hipGetLastError();
+}
+
 size_t splitk_workspace(int epi, int M, int N, int K) {
   const SplitKArgs a = splitk_plan(epi, M, N, K);
   return (size_t)a.splits * M * a.Nv * sizeof(float);
@@ -461,9 +490,11 @@ hipError_t launch_splitk_reduce(int epi, const SplitKArgs& a, const GemmArgs& g,
 }
 
 hipError_t launch_gemm_splitk(int epi, const GemmArgs& g, float* part, hipStream_t s, const int* a_rows,
-                              int a_phys_rows, const int* c_rows, const SplitKFuse* fuse) {
+                              int a_phys_rows, const int* c_rows, const SplitKFuse* fuse, bool b_packed) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (b_packed && (g.N % 16 || g.K % KSL || g.ldb != g.K)) return hipErrorInvalidValue;
   SplitKArgs a = splitk_plan(epi, g.M, g.N, g.K);
+  a.packed = b_packed ? 1 : 0;
   a.A = g.A; a.B = g.B; a.B2 = g.B2; a.part = part; a.lda = (int)g.lda; a.ldb = (int)g.ldb;
   a.a_rows = a_rows; a.a_phys_rows = a_phys_rows; a.c_rows = c_rows;
   const int vtiles = epi == EPI_SWIGLU ? 2 * a.col_tiles : a.col_tiles;

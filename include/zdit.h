@@ -385,7 +385,16 @@ typedef struct {
   int32_t vocab;       /* embedding rows */
   float rope_theta;    /* 1e6 */
   float norm_eps;      /* 1e-6 */
+  int32_t flags;       /* 0, or ZDIT_ENC_PACKED_WEIGHTS; any other bit: ZDIT_EINVAL */
 } zdit_enc_cfg;
+
+/* zdit_enc_cfg.flags.  ZDIT_ENC_PACKED_WEIGHTS: w_qkv, w_o, w_gate, w_up and w_down are in the
+ * layout of zdit_op_pack_weights (same bytes, reordered), which the projections stream as 1 KB
+ * runs instead of 64-byte pieces of 16 rows (the forward on two 64-id rows at the pinned widths:
+ * 2.8 against 3.2 ms).  Only
+ * the split-K path reads that layout: with the flag, batch * max_len must be <= 256
+ * (ZDIT_EUNSUPPORTED otherwise).  The result is bit-identical to the row-major weights'. */
+enum { ZDIT_ENC_PACKED_WEIGHTS = 1 };
 
 typedef struct {
   const float* in_norm;    /* fp32 [hidden] */
@@ -434,6 +443,19 @@ size_t zdit_op_gemm_splitk_workspace(int32_t epilogue, int32_t M, int32_t N, int
 zdit_status zdit_op_gemm_splitk(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
                                 const void* B, const void* B2, const float* vec, void* C,
                                 void* ws, size_t ws_bytes, void* hip_stream);
+/* The same with B (and B2) packed by zdit_op_pack_weights; N % 16 == 0 as well.  Only the
+ * weights' addresses differ: same sums in the same order, bit-identical results. */
+zdit_status zdit_op_gemm_splitk_packed(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,
+                                       const void* B, const void* B2, const float* vec, void* C,
+                                       void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Packs a bf16 weight matrix src [N, K] (row-major, device) into dst (device, N K 2 bytes, not
+ * overlapping src; both 16-byte aligned): bands of 16 rows, each a run of K / 32 slabs of 32
+ * columns, each slab 64 chunks of 16 bytes, chunk l of slab t of band b holding columns
+ * 32 t + 8 (l / 16) .. + 7 of row 16 b + l % 16 (the B operand of a 16 x 16 x 32 bf16 MFMA), so
+ * a wavefront reads a slab of its band as 1 KB in a row.  N % 16 == 0, K % 32 == 0, at most
+ * 2 GiB (else ZDIT_EUNSUPPORTED); enqueued on the stream. */
+zdit_status zdit_op_pack_weights(int32_t N, int32_t K, const void* src, void* dst, void* hip_stream);
 
 /* Embedding gather: out [batch, max_len, dim] fp32 = rows of table (bf16 [vocab, dim]) for
  * r < len[b], 0 after; ids / len host as in zdit_encoder_fwd; dim % 8 == 0; ws:

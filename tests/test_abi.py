@@ -295,6 +295,32 @@ def test_encoder_rejects_bad_arguments_before_launch():
     assert _enc_call(cfg5, w5, 2, 16, ids, [9, 4]) == Z.ZDIT_EUNSUPPORTED
 
 
+def test_encoder_packed_flag_checks_before_launch():
+    ed, cfg, w, _ = _enc_setup()
+    ids = synth.token_ids(2, 16, [9, 4], ed.vocab, 0)
+    cfg.flags = 2
+    assert _enc_call(cfg, w, 2, 16, ids, [9, 4]) == Z.ZDIT_EINVAL          # unknown flag
+    cfg.flags = Z.ZDIT_ENC_PACKED_WEIGHTS
+    wide = synth.token_ids(2, 200, [9, 4], ed.vocab, 0)
+    assert _enc_call(cfg, w, 2, 200, wide, [9, 4]) == Z.ZDIT_EUNSUPPORTED  # 400 rows: not the split-K path
+    assert "packed" in Z.last_error()
+
+
+def test_pack_and_packed_gemm_reject_bad_arguments_before_launch():
+    L = Z.lib()
+    a, b = C.c_void_p(1 << 20), C.c_void_p(1 << 24)
+    assert L.zdit_op_pack_weights(24, 64, a, b, None) == Z.ZDIT_EUNSUPPORTED            # N % 16
+    assert L.zdit_op_pack_weights(32, 48, a, b, None) == Z.ZDIT_EUNSUPPORTED            # K % 32
+    assert L.zdit_op_pack_weights(32, 64, None, b, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_pack_weights(32, 64, C.c_void_p((1 << 20) + 8), b, None) == Z.ZDIT_EINVAL
+    assert L.zdit_op_pack_weights(32, 64, a, C.c_void_p((1 << 20) + 1024), None) == Z.ZDIT_EINVAL  # overlap
+    args = (C.c_void_p(1 << 20), C.c_void_p(1 << 24), None, None, C.c_void_p(1 << 26), C.c_void_p(1 << 27), 1 << 20,
+            None)
+    assert L.zdit_op_gemm_splitk_packed(Z.ZDIT_EPI_STORE, 8, 24, 64, *args) == Z.ZDIT_EUNSUPPORTED  # N % 16
+    assert L.zdit_op_gemm_splitk(Z.ZDIT_EPI_STORE, 8, 24, 64, *args[:5], C.c_void_p(1 << 27), 16,
+                                 None) == Z.ZDIT_EWORKSPACE  # the row-major form takes N % 8
+
+
 def test_encoder_ops_reject_bad_arguments_before_launch():
     L = Z.lib()
     ids = np.zeros((1, 8), np.int32)

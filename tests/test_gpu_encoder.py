@@ -119,6 +119,52 @@ def test_gemm_splitk_partial_last_chunk_ignores_memory_after_a(epi, K):
         assert np.all(np.abs(got - (C0 + ref)) <= bound + 1e-6 * np.abs(C0) + 1e-6)
 
 
+def test_pack_weights_layout():
+    """zdit_op_pack_weights against its definition: chunk l of slab t of band b holds columns
+    32 t + 8 (l // 16) .. + 7 of row 16 b + l % 16."""
+    note("pack weights layout 48 x 96")
+    g = _rng(70)
+    N, K = 48, 96
+    W = bf16_values(g.standard_normal((N, K)).astype(np.float32))
+    src = dev(W, torch.bfloat16)
+    dst = torch.empty_like(src)
+    Z.zdit_op_pack_weights(N, K, src, dst)
+    got = host(dst).reshape(N // 16, K // 32, 64, 8)
+    b, t, l, e = np.meshgrid(np.arange(N // 16), np.arange(K // 32), np.arange(64), np.arange(8), indexing="ij")
+    want = W[16 * b + l % 16, 32 * t + 8 * (l // 16) + e]
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("epi,M,N,K", [(Z.ZDIT_EPI_STORE, 55, 6144, 2560), (Z.ZDIT_EPI_RESID, 55, 2560, 4096),
+                                       (Z.ZDIT_EPI_RESID, 55, 2560, 9728), (Z.ZDIT_EPI_SWIGLU, 55, 9728, 2560),
+                                       (Z.ZDIT_EPI_SWIGLU, 33, 208, 2560), (Z.ZDIT_EPI_STORE, 7, 64, 64)])
+def test_gemm_splitk_packed_bit_identical(epi, M, N, K):
+    """Weights packed by zdit_op_pack_weights give the row-major call's bits: same sums, same
+    order, only the weights' addresses differ (ranges of two and four resident chunks, the
+    double-buffered gate/up range, SwiGLU in the GEMM and through the reduction)."""
+    note(f"gemm split-K packed vs row-major epi={epi} M={M} N={N} K={K}")
+    A, B, B2 = _sk_inputs(M, N, K, 71)
+    Ad, Bd = dev(A, torch.bfloat16), dev(B, torch.bfloat16)
+    B2d = dev(B2, torch.bfloat16) if epi == Z.ZDIT_EPI_SWIGLU else None
+    vec = dev((1.0 + 0.1 * _rng(72).standard_normal(N)).astype(np.float32)) if epi == Z.ZDIT_EPI_RESID else None
+    if epi == Z.ZDIT_EPI_RESID:
+        c0 = dev(_rng(73).standard_normal((M, N)).astype(np.float32))
+        C1, C2 = c0.clone(), c0.clone()
+    else:
+        C1 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        C2 = C1.clone()
+    Bp = torch.empty_like(Bd)
+    Z.zdit_op_pack_weights(N, K, Bd, Bp)
+    B2p = None
+    if B2d is not None:
+        B2p = torch.empty_like(B2d)
+        Z.zdit_op_pack_weights(N, K, B2d, B2p)
+    ws = Z.workspace(Z.zdit_op_gemm_splitk_workspace(epi, M, N, K))
+    Z.zdit_op_gemm_splitk(epi, M, N, K, Ad, Bd, B2d, vec, C1, ws)
+    Z.zdit_op_gemm_splitk_packed(epi, M, N, K, Ad, Bp, B2p, vec, C2, ws)
+    assert torch.equal(C1, C2)
+
+
 def test_gemm_splitk_rows_do_not_depend_on_m():
     """The K ranges depend on N and K only: rows computed with 50 or 256 rows are identical."""
     N, K = 2560, 9728
@@ -386,3 +432,22 @@ def test_encoder_full_width_two_blocks_matches_oracle():
     ids = synth.token_ids(2, 64, lens, ed.vocab, 14)
     got = _encoder_run(ed, W, ids, lens)
     _check_vs_oracle(got, E.encoder_penultimate(ids, lens, W, ed), lens)
+
+
+def test_encoder_packed_weights_bit_identical():
+    """The forward with ZDIT_ENC_PACKED_WEIGHTS and zdit_op_pack_weights'd projections equals the
+    row-major forward bit for bit, at the pinned widths on the DiT's caption lengths."""
+    ed = synth.ENC_FULL.replace(n_layers=3, vocab=4096)
+    lens = [45, 10]
+    note("encoder packed vs row-major weights, full width, 2 blocks")
+    W = synth.encoder_weights(ed, 16, ed.n_layers - 1)
+    ids = synth.token_ids(2, 64, lens, ed.vocab, 17)
+    m = Z.upload_encoder(W)
+    mp = Z.pack_encoder(m)
+    outs = []
+    for cfg, mm in ((Z.make_enc_cfg(ed), m), (Z.make_enc_cfg(ed, Z.ZDIT_ENC_PACKED_WEIGHTS), mp)):
+        out = torch.full((2, 64, ed.hidden), 3.0, device="cuda")
+        ws = Z.workspace(Z.zdit_encoder_workspace(cfg, 2, 64))
+        Z.zdit_encoder_fwd(cfg, mm, 2, 64, ids, lens, out, ws)
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
