@@ -591,15 +591,17 @@ hipError_t launch_gemm_bf16(int epi, const GemmArgs& g, hipStream_t s) {
 }
 
 SplitPlan tile_split_plan(int epi, int N, int K) {
-  // About 160 workgroups per 256-row panel, at most 8 ranges and ranges of at least 16 slabs:
-  // more ranges spread a short branch's first (full) row panel over more CUs but write and read
-  // one more fp32 partial plane each (on the 256 px block, 256 workgroups per panel was slower
-  // than 128).  From N and K only, so a row's sums do not depend on M.
+  // At most 128 workgroups per 256-row panel, so that a branch of up to 512 rows (two panels)
+  // runs in one round on 256 CUs; at most 8 ranges and ranges of at least 16 slabs.  More ranges
+  // spread the work over more CUs but write and read one more fp32 partial plane each, and a
+  // second round of workgroups costs a whole tile time: on the 256 px block (two panels) two
+  // ranges instead of four for q/k/v and one instead of two for w1/w3 took the block from 0.366
+  // to 0.326 ms.  From N and K only, so a row's sums do not depend on M.
   SplitPlan p;
   const bool paired = epi == EPI_SWIGLU;
   const int n_tiles = (N + (paired ? BN / 2 : BN) - 1) / (paired ? BN / 2 : BN);
   const int max_splits = std::max(1, std::min(8, K / 512));
-  const int splits = std::min(max_splits, std::max(1, (160 + n_tiles / 2) / n_tiles));
+  const int splits = std::min(max_splits, std::max(1, 128 / n_tiles));
   p.k_split = ((K + splits - 1) / splits + BK - 1) / BK * BK;
   p.splits = (K + p.k_split - 1) / p.k_split;
   p.Nv = paired ? 2 * N : N;
@@ -608,13 +610,15 @@ SplitPlan tile_split_plan(int epi, int N, int K) {
 
 size_t tile_split_workspace(int epi, int M, int N, int K) {
   const SplitPlan p = tile_split_plan(epi, N, K);
-  return (size_t)p.splits * M * p.Nv * sizeof(float);
+  return p.splits == 1 ? 0 : (size_t)p.splits * M * p.Nv * sizeof(float);
 }
 
 hipError_t launch_gemm_bf16_split(int epi, const GemmArgs& g, float* part, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (epi != EPI_STORE && epi != EPI_RESID && epi != EPI_SWIGLU) return hipErrorInvalidValue;
   const SplitPlan p = tile_split_plan(epi, g.N, g.K);
+  // one range: the whole-K kernel with the epilogue itself (no partial plane, no reduction)
+  if (p.splits == 1) return launch_gemm_bf16(epi, g, s);
   GemmArgs pg = g;
   pg.C = part;
   pg.part = part;

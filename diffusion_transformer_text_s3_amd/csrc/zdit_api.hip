@@ -228,8 +228,10 @@ zdit_status block_forward(const zdit_dims& d, const zdit_block_w& w, int B, int 
   HIP_TRY(launch_rmsnorm_mod(P, na, st));
 
   {
+    // a one-range plan runs the whole-K GEMM, so the q/k/v projection then takes the fused form
+    const bool qkv_split = split && tile_split_plan(EPI_STORE, 3 * D, D).splits > 1;
     const zdit_status rc = qkv_attention(P, d.n_heads, B, s, seq_len, h, w.w_qkv, qkv, vt, o, cosT, sinT,
-                                         tab_bstride, st, part);
+                                         tab_bstride, st, qkv_split ? part : nullptr);
     if (rc != ZDIT_OK) return rc;
   }
 
@@ -810,7 +812,7 @@ size_t zdit_op_gemm_ksplit_workspace(int32_t epilogue, int32_t M, int32_t N, int
   if ((epilogue != ZDIT_EPI_STORE && epilogue != ZDIT_EPI_RESID && epilogue != ZDIT_EPI_SWIGLU) || M < 1 ||
       M > (1 << 24) || N < 8 || N % 8 || K < 64 || K % 64)
     return 0;
-  return al256(tile_split_workspace(epilogue, M, N, K));
+  return al256(tile_split_workspace(epilogue, M, N, K)) + 256;  // never 0 for an accepted shape
 }
 
 zdit_status zdit_op_gemm_ksplit(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A, const void* B,

@@ -131,8 +131,9 @@ zdit_status zdit_block_fwd(const zdit_dims* dims, const zdit_block_w* w, int32_t
  * the workspace replaced by a scratch array the library holds on each device (128 MiB, placed
  * when the library's code loads on that device and kept until the process ends).  Calls
  * zdit_block_fwd would accept whose zdit_block_workspace() exceeds 128 MiB return
- * ZDIT_EUNSUPPORTED (a 256 px branch and the 512 px pair fit; the 256 px pair, whose K-split
- * GEMMs keep ~105 MB of partial products, and the 1024^2 pair need a workspace).  All
+ * ZDIT_EUNSUPPORTED (a 256 px branch, the 256 px pair and the 512 px pair fit; a pair of
+ * 448-row branches, whose K-split GEMMs keep ~110 MB of partial products, and the 1024^2 pair
+ * need a workspace).  All
  * calls on one device share its scratch: calls that overlap on one device (other streams,
  * other threads) race and must be ordered by the caller.  No allocation, no free, no host
  * copy (except the ZDIT_CHECK_FINITE read-back). */
@@ -290,7 +291,8 @@ zdit_status zdit_op_gemm(int32_t precision, int32_t epilogue, int32_t M, int32_t
  * rows (bf16 only; epilogues ZDIT_EPI_STORE, ZDIT_EPI_RESID, ZDIT_EPI_SWIGLU): K is cut into
  * ranges chosen from N and K alone, the 256 x 256-tile kernel writes each range's fp32 partial
  * product to the workspace, and a second kernel sums the ranges in order and applies the
- * epilogue, so a row's result does not depend on M.  K % 64 == 0, N % 8 == 0; ws:
+ * epilogue, so a row's result does not depend on M (a plan of one range runs the whole-K
+ * kernel with the epilogue, as zdit_op_gemm).  K % 64 == 0, N % 8 == 0; ws:
  * zdit_op_gemm_ksplit_workspace() bytes (0 for a shape or epilogue this form rejects). */
 size_t zdit_op_gemm_ksplit_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t K);
 zdit_status zdit_op_gemm_ksplit(int32_t epilogue, int32_t M, int32_t N, int32_t K, const void* A,

@@ -128,8 +128,7 @@ def test_gemm_ksplit_swiglu(M, N, K):
 
 def test_gemm_ksplit_rows_do_not_depend_on_m():
     """The K ranges depend on N and K only: rows computed among 40 or 600 rows are identical,
-    and rows past the first 256-row panel (where the last panel's empty row groups skip their
-    MFMAs) too."""
+    rows past the first 256-row panel (whose last panel is mostly rows past M) too."""
     N, K = 3840, 10240
     note("gemm K-split rows independent of M")
     A, B, _ = _gemm_inputs(600, N, K, 33)
