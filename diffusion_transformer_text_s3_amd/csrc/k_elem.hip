@@ -75,30 +75,42 @@ __global__ __launch_bounds__(STAGED ? 64 * kNormWaves : 256) void rmsnorm_mod_ke
       continue;
     }
     const float4* x = (const float4*)(a.x + b * a.x_bstride + (int64_t)r * a.dim);
+    // Every load is issued before the first is used: the index is clamped into the row (a lane
+    // past its end reloads the last chunk) and the value zeroed by a select, so no branch
+    // separates the loads (guarded loads made the compiler wait for each one in turn).  Adding
+    // the zeros leaves the sum of squares unchanged, term for term.
     float4 v[kNormMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kNormMaxChunks; ++j) v[j] = x[min(lane + 64 * j, nchunk - 1)];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kNormMaxChunks; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nchunk) {
-        v[j] = x[c];
-        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-      }
+      if (lane + 64 * j >= nchunk) v[j] = float4{0.f, 0.f, 0.f, 0.f};
+      ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     }
     ss = wave_sum(ss);
     const float rinv = 1.0f / sqrtf(ss / (float)a.dim + a.eps);
+    // gain / shift / scale of four chunks at a time, loaded together (clamped like x)
 #pragma unroll
-    for (int j = 0; j < kNormMaxChunks; ++j) {
-      const int c = lane + 64 * j;
-      if (c < nchunk) {
-        const float4 gg = vg[c];
+    for (int j0 = 0; j0 < kNormMaxChunks; j0 += 4) {
+      float4 gg[4], s1[4], s2[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = min(lane + 64 * (j0 + q), nchunk - 1);
+        gg[q] = vg[c];
+        if (mod) { s1[q] = vsh[c]; s2[q] = vsc[c]; }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = lane + 64 * (j0 + q);
+        if (c >= nchunk) continue;
+        const float4 w = v[j0 + q];
         float4 o;
-        o.x = v[j].x * rinv * gg.x; o.y = v[j].y * rinv * gg.y;
-        o.z = v[j].z * rinv * gg.z; o.w = v[j].w * rinv * gg.w;
+        o.x = w.x * rinv * gg[q].x; o.y = w.y * rinv * gg[q].y;
+        o.z = w.z * rinv * gg[q].z; o.w = w.w * rinv * gg[q].w;
         if (mod) {
-          const float4 s1 = vsh[c], s2 = vsc[c];
-          o.x = o.x * (1.f + s2.x) + s1.x; o.y = o.y * (1.f + s2.y) + s1.y;
-          o.z = o.z * (1.f + s2.z) + s1.z; o.w = o.w * (1.f + s2.w) + s1.w;
+          o.x = o.x * (1.f + s2[q].x) + s1[q].x; o.y = o.y * (1.f + s2[q].y) + s1[q].y;
+          o.z = o.z * (1.f + s2[q].z) + s1[q].z; o.w = o.w * (1.f + s2[q].w) + s1[q].w;
         }
         if constexpr (sizeof(TO) == 2) {
           bf16x4 ob = {(bf16)o.x, (bf16)o.y, (bf16)o.z, (bf16)o.w};
