@@ -164,6 +164,24 @@ def test_ksplit_gemm_validates_before_launch():
     assert rc == Z.ZDIT_EWORKSPACE
 
 
+def test_ksplit_plan_fits_two_panels_in_one_round():
+    """The K-split plan for branches of at most 512 rows, read back through the workspace query
+    (ranges x M x Nv fp32 partials, 256 bytes of slack): at the block's four shapes a two-panel
+    branch (257..512 rows) takes at most 256 workgroups of 256 x 256 tiles, i.e. one round on 256
+    CUs, and a plan of one range needs no partial plane."""
+    D, H, M = 3840, 10240, 320
+    shapes = [(Z.ZDIT_EPI_STORE, 3 * D, D, 45, 2), (Z.ZDIT_EPI_RESID, D, D, 15, 7),
+              (Z.ZDIT_EPI_SWIGLU, H, D, 80, 1), (Z.ZDIT_EPI_RESID, D, H, 15, 8)]
+    for epi, N, K, n_tiles, want in shapes:
+        nv = 2 * N if epi == Z.ZDIT_EPI_SWIGLU else N
+        ws = Z.zdit_op_gemm_ksplit_workspace(epi, M, N, K) - 256
+        plane = M * nv * 4
+        splits = 1 if ws == 0 else ws // plane
+        assert ws in (0, -(-splits * plane // 256) * 256), (epi, N, K, ws)
+        assert splits == want, (epi, N, K, splits)
+        assert 2 * n_tiles * splits <= 256
+
+
 def test_fused_qkv_attn_validates_before_launch():
     L = Z.lib()
     p = _fake()

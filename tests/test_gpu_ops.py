@@ -126,6 +126,21 @@ def test_gemm_ksplit_swiglu(M, N, K):
     _check_swiglu(host(C), A.astype(np.float64), B.astype(np.float64), B2.astype(np.float64))
 
 
+def test_gemm_ksplit_one_range_is_the_whole_k_gemm():
+    """Where the K-split plan has one range (w1/w3 at 3840 wide) the K-split entry point runs the
+    whole-K kernel with its epilogue: bit-identical to zdit_op_gemm at the 256 px block's rows."""
+    M, N, K = 320, 10240, 3840
+    note(f"gemm K-split one range == whole-K M={M} N={N} K={K}")
+    assert Z.zdit_op_gemm_ksplit_workspace(Z.ZDIT_EPI_SWIGLU, M, N, K) == 256
+    A, B, B2 = _gemm_inputs(M, N, K, 34, two_b=True)
+    c1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    c2 = torch.empty_like(c1)
+    _ksplit(Z.ZDIT_EPI_SWIGLU, M, N, K, A, B, B2, None, c1)
+    Z.zdit_op_gemm(Z.ZDIT_BF16, Z.ZDIT_EPI_SWIGLU, M, N, K, dev(A, torch.bfloat16), dev(B, torch.bfloat16),
+                   dev(B2, torch.bfloat16), None, c2)
+    assert torch.equal(c1, c2)
+
+
 def test_gemm_ksplit_rows_do_not_depend_on_m():
     """The K ranges depend on N and K only: rows computed among 40 or 600 rows are identical,
     rows past the first 256-row panel (whose last panel is mostly rows past M) too."""
