@@ -27,19 +27,22 @@ template <> __device__ __forceinline__ float from_act<bf16>(bf16 v) { return (fl
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------------------------------
-// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift.  A workgroup of 8 wavefronts takes 8
+// RMSNorm (fp32 reduction) * gain * (1 + scale) + shift.  A workgroup of 4 wavefronts takes 4
 // rows of one branch; gain, shift and scale of that branch are staged in LDS once, then each
 // wavefront normalises one row, keeping it in registers (dim <= 4096: at most 16 float4 per
 // lane).  One row per wavefront keeps more rows in flight than a wavefront looping over rows
-// (55 against 61 us at 8320 x 3840 with 4 rows per wavefront, same box).
+// (55 against 61 us at 8320 x 3840 with 4 rows per wavefront, same box).  Four wavefronts per
+// workgroup rather than 8: with ~150 registers a CU holds 12 wavefronts and with 46 KB of
+// staged vectors 3 workgroups, so 4-wave workgroups fill it where 8-wave ones leave it at 8
+// (8320 x 3840: 47.5 -> 41.5 us; 16 waves 61.5 us).
 // ---------------------------------------------------------------------------------------
 constexpr int kNormMaxChunks = 16;
-constexpr int kNormRowsPerBlock = 8;
+constexpr int kNormRowsPerBlock = 4;
 
-// STAGED: 8 rows per workgroup with gain / shift / scale staged in LDS (many rows).  Else one
+// STAGED: 4 rows per workgroup with gain / shift / scale staged in LDS (many rows).  Else one
 // row per wavefront, 4 per workgroup, the vectors read from global memory where they stay in
 // L2 (few rows: more workgroups, no staging to amortise).
-constexpr int kNormWaves = 8;
+constexpr int kNormWaves = 4;
 
 template <typename TO, bool STAGED>
 __global__ __launch_bounds__(STAGED ? 64 * kNormWaves : 256) void rmsnorm_mod_kernel(NormArgs a) {
