@@ -79,3 +79,32 @@ def test_vae_decode_count():
     assert px == 1024 * 1024
     assert total == bench.vae_flops(vd, 1, 128, 128)
     assert round(total / 1e12, 3) == 10.472
+
+
+def test_encoder_down_projection_bytes():
+    """The encoder roofline's algorithmic bytes for the down projection on the 55 valid rows of
+    the 45- and 10-token captions: the bf16 weights once, the bf16 activations once, the fp32
+    residual rows read and written once (52.0 MB)."""
+    ed = synth.ENC_FULL
+    M, D, I = 45 + 10, ed.hidden, ed.inter
+    weights = D * I * 2
+    acts = M * I * 2
+    resid = M * D * 4 * 2
+    assert (D, I) == (2560, 9728)
+    assert round((weights + acts + resid) / 1e6, 1) == 52.0
+    # bench.py's formula for the same launch
+    assert 2 * D * I + 2 * M * I + 2 * 4 * M * D == weights + acts + resid
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits non-zero with a message, before any GPU
+    work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
