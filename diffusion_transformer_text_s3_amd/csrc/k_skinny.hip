@@ -18,6 +18,11 @@
 // padded batch.  The reduction can also carry the work that follows it (SplitKFuse): the
 // encoder's q/k RMSNorm + RoPE after the q/k/v projection, or the RMSNorm after a residual add.
 // Buffer resources make rows past M or N read as zero.
+//
+// The weights may also come packed (pack_bfrag_kernel): each band of 16 rows stored slab after
+// slab, a slab being the 64 lanes' 16-byte fragments in lane order, so a wavefront reads one
+// contiguous 1 KB run per slab instead of 16 pieces of 64 bytes K * 2 bytes apart.  Only the
+// weight addresses change: same fragments, same order, bit-identical results.
 #include "common.h"
 
 namespace zdit {
