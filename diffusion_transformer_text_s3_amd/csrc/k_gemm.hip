@@ -18,9 +18,10 @@
 // c ^ ((r >> 2) & 3), so the 16-byte fragment reads of 16 consecutive rows cover all 64 banks.
 //
 // Workgroups are numbered so that the ones dispatched to the same XCD (round-robin over 8)
-// get consecutive tiles, and tiles are walked in groups of 4 row-panels, so each XCD's L2
-// sees a compact set of A and B panels (the 32 tiles an XCD runs together span 4 row panels
-// and 8 column panels; groups of 8 rows were 0.6 % slower on the 1024^2 block, of 16 rows 3-4 %).
+// get consecutive tiles, and tiles are walked in groups of 5 row-panels, so each XCD's L2
+// sees a compact set of A and B panels (the 32 tiles an XCD runs together span 5 row panels
+// and 7 column panels).  On the 1024^2 pair stack, groups of 4, 6, 7 and 8 rows were 0.9, 0.3,
+// 0.5 and ~3 % slower, of 16 rows slower still.
 //
 // Epilogues work from the accumulators, staged through LDS into 16-byte row chunks: plain bf16
 // store (QKV), bias + fp32 store into a branch-strided buffer (embeds, final layer), fp32 gated
@@ -61,7 +62,7 @@ __device__ __forceinline__ void tile_coords(int pid, int nwg, int tiles_m, int t
   const int xcd = pid & 7, idx = pid >> 3;
   const int full = nwg >> 3, rem = nwg & 7;
   const int lid = (xcd < rem) ? xcd * (full + 1) + idx : rem * (full + 1) + (xcd - rem) * full + idx;
-  constexpr int G = 4;
+  constexpr int G = 5;
   const int per_group = G * tiles_n;
   const int group = lid / per_group;
   const int first_m = group * G;
